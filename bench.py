@@ -1,0 +1,239 @@
+"""Throughput of one tensor-parallel rank's Domino MLP block (forward + backward) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of the workload: the forward
+(GEMM1 with the activation epilogue, GEMM2 per chunk, each chunk's reduction of the 8
+shard partials on a second stream) and the backward (activation-gradient GEMM and
+input-gradient GEMM per chunk, each chunk's reduction of dX, then the two weight-gradient
+GEMMs). Peer ranks' partials are produced once before timing (they are other GPUs' work
+in a real tensor-parallel group). Inputs are resident in HBM when timing starts.
+
+Prints one JSON line: value = rank's fwd+bwd GEMM-chain TFLOP/s (algorithmic FLOPs:
+3 × 2·T·h·(n1 + f_s)), plus a roofline object for the dominant kernel (its average launch
+time measured with HIP events recorded on its own stream by the library) and the CPU
+oracle's throughput on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+METRIC = "TP-shard block fwd+bwd TFLOP/s (bf16) + % MFMA peak; shard_reduce GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt3_2p7b_mlp_tp8_row")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def mlp_flops(w):
+    fwd = 2.0 * w.tokens * w.hidden * w.n1 + 2.0 * w.tokens * w.ffn_shard * w.hidden
+    return fwd, 3.0 * fwd
+
+
+def kernel_flops(w, kind):
+    """Algorithmic FLOPs of one launch of each GEMM kind in the workload's schedule."""
+    T, h, f, n1 = w.tokens, w.hidden, w.ffn_shard, w.n1
+    Tc = T // w.row_chunks
+    hc_f = h // w.col_chunks
+    bwd_rows = w.row_chunks
+    bwd_cols = 1 if w.row_chunks > 1 else w.col_chunks
+    return {
+        "fwd_gemm1": 2.0 * Tc * h * n1,
+        "fwd_gemm2": 2.0 * Tc * f * hc_f,
+        "dgrad_b": 2.0 * (T // bwd_rows) * h * f,
+        "dgrad_a": 2.0 * (T // bwd_rows) * n1 * (h // bwd_cols),
+        "wgrad_b": 2.0 * T * f * h,
+        "wgrad_a": 2.0 * T * h * n1,
+    }[kind]
+
+
+KERNEL_NAMES = {
+    "fwd_gemm1": "gemm_bf16_kernel<BM,BN,true,false,Epi::kGelu|kSwiglu> (X·A_s + activation)",
+    "fwd_gemm2": "gemm_bf16_kernel<BM,BN,true,false,Epi::kStore> (H·B_s chunk)",
+    "dgrad_b": "gemm_bf16_kernel<BM,BN,true,true,Epi::kDGelu|kDSwiglu> (dY·B_sᵀ + activation gradient)",
+    "dgrad_a": "gemm_bf16_kernel<BM,BN,true,true,Epi::kStore> (dHpre·A_sᵀ chunk)",
+    "wgrad_b": "gemm_bf16_kernel<BM,BN,false,false,Epi::kF32> (Hᵀ·dY)",
+    "wgrad_a": "gemm_bf16_kernel<BM,BN,false,false,Epi::kF32> (Xᵀ·dHpre)",
+}
+
+
+def cpu_baseline(w, inp, reps):
+    """The oracle (numpy fp64) on this host: one rank's forward + backward of the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    A0, B0 = oracle.mlp_shard_weights(A, B, w.act, w.n_partials, 0)
+    A0, B0 = np.ascontiguousarray(A0), np.ascontiguousarray(B0)
+    _, total = mlp_flops(w)
+    best = None
+    for _ in range(max(1, reps)):
+        t0 = time.perf_counter()
+        oracle.mlp_shard_forward(X, A0, B0, w.act)
+        oracle.mlp_shard_backward(X, A0, B0, dY, w.act)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+        if time.perf_counter() - t0 > 30:
+            break
+    return {"value": total / best / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one rank's full forward+backward of {w.name} (T={w.tokens}, fp64 numpy), best of "
+                      f"{reps} reps, {best:.2f} s each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported in this build "
+              f"(the reduction of tensor-parallel partials runs on one GPU)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import tensor_transformer_block_domino_amd as D
+    from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
+
+    D.load()
+    w = synth.WORKLOADS[args.workload]
+    assert isinstance(w, synth.MlpWorkload) and w.dtype == "bf16"
+    dev = torch.device("cuda:0")
+    inp = synth.mlp_inputs(w)
+    g = MlpGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn_shard=w.ffn_shard, act=w.act, dtype=w.dtype,
+                 row_chunks=w.row_chunks, col_chunks=w.col_chunks, n_partials=w.n_partials, X=inp["X"], A=inp["A"],
+                 B=inp["B"], dY=inp["dY"], device=dev)
+    g.peer_forward()
+    g.forward()
+    g.peer_backward()
+    torch.cuda.synchronize()
+    compute = torch.cuda.Stream()
+    comm = torch.cuda.Stream()
+
+    def step_domino():
+        g.forward(compute, comm, no_join=1)
+        g.backward(compute, comm)
+
+    def step_serial():
+        g.forward(compute, None, row_chunks=1, col_chunks=1)
+        g.backward(compute, None, row_chunks=1, col_chunks=1)
+
+    def step_unsplit():
+        d_f = g.desc(rank_alone=True, row_chunks=1, col_chunks=1)
+        D.domino_block_fwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, compute, None)
+        D.domino_block_bwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.dY, g.dHpre[0], g.dX_own[0], None,
+                           None, g.dA, g.dB, 0, g.ws, g.ws_bytes, compute, None)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    # The timed region: Domino chunks, reductions on the second stream.
+    ms = timed(step_domino, args.steps, args.warmup)
+    print(f"[bench] domino step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms_serial = timed(step_serial, args.steps, 2)
+    ms_unsplit = timed(step_unsplit, args.steps, 2)
+    print(f"[bench] serial {ms_serial:.3f} ms, unsplit without reduce {ms_unsplit:.3f} ms", file=sys.stderr,
+          flush=True)
+
+    # Per-kernel durations: the same Domino steps with the library's event timing on.
+    D.domino_timing_enable(True)
+    for _ in range(args.steps):
+        step_domino()
+    torch.cuda.synchronize()
+    per = {}
+    for kind in ("reduce", "fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a"):
+        n, tot = D.domino_timing_read(kind)
+        per[kind] = (n, tot)
+    # shard_reduce alone: the whole [T, h] output, the 8 partials, on an idle GPU.
+    D.domino_timing_enable(True)
+    parts = [g.Y_own[r] for r in g.ranks]
+    for _ in range(args.steps):
+        D.shard_reduce(g.Y, w.hidden, parts, w.hidden, w.tokens, w.hidden, D.DOMINO_BF16, compute)
+    torch.cuda.synchronize()
+    n_sa, tot_sa = D.domino_timing_read("reduce")
+    D.domino_timing_enable(False)
+    red_sa_us = tot_sa / max(1, n_sa) * 1e3
+    red_sa_gbps = (w.n_partials + 1) * w.tokens * w.hidden * 2 / (red_sa_us * 1e-6) / 1e9
+
+    fwd_flops, total_flops = mlp_flops(w)
+    value = total_flops / (ms * 1e-3) / 1e12
+    gemm_kinds = ["fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a"]
+    dom = max(gemm_kinds, key=lambda k: per[k][1])
+    n_dom, tot_dom = per[dom]
+    avg_ms = tot_dom / max(1, n_dom)
+    achieved = kernel_flops(w, dom) / (avg_ms * 1e-3) / 1e12
+    n_red, tot_red = per["reduce"]
+    # Reduced bytes per step: Y and dX, each (P+1)·T·h·2 bytes.
+    red_bytes_step = 2 * (w.n_partials + 1) * w.tokens * w.hidden * 2
+    red_ms_step = tot_red / args.steps
+    red_gbps = red_bytes_step / (red_ms_step * 1e-3) / 1e9
+    gemm_ms_step = sum(per[k][1] for k in gemm_kinds) / args.steps
+    hidden_frac = 1.0 - (ms - ms_unsplit) / red_ms_step if red_ms_step > 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "ffn_shard": w.ffn_shard, "act": w.act, "tp_partials": w.n_partials,
+                   "split": f"rows x{w.row_chunks}, cols x{w.col_chunks}", "pass": "fwd+bwd"},
+        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gemm_chain_tflops": round(total_flops / (gemm_ms_step * 1e-3) / 1e12, 2),
+        "shard_reduce_GBps": round(red_sa_gbps, 1),
+        "shard_reduce_hbm_frac": round(red_sa_gbps / HBM_PEAK_GBPS, 4),
+        "shard_reduce_avg_us": round(red_sa_us, 2),
+        "shard_reduce_in_step_GBps": round(red_gbps, 1),
+        "t_domino_ms": round(ms, 4),
+        "t_serial_ms": round(ms_serial, 4),
+        "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
+        "t_reduce_ms": round(red_ms_step, 4),
+        "hidden_fraction": None if hidden_frac is None else round(hidden_frac, 3),
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
+        "roofline": {"bound": "mfma", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n_dom,
+                     "flops_per_launch": kernel_flops(w, dom)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

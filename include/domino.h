@@ -1,0 +1,210 @@
+/*
+ * domino.h — C ABI of the MI355X (gfx950) Domino tensor-parallel shard library.
+ *
+ * One tensor-parallel (TP) rank's share of a transformer layer, X·A·B = Y, computed in
+ * Domino's independent chunks, with the TP AllReduce's reduction done on one GPU by
+ * summing the rank's own partial with the other ranks' partials held in local HBM.
+ *
+ * Sources (web pages, by title and section):
+ *   "DeepSpeed-Domino 深度解析：通过通用张量切分与计算通信重叠实现单机与多节点统一的 LLM 张量并行训练"
+ *     — "TP 的数据依赖：通信为何难以隐藏": a TP layer is X·A·B = Y followed by AllReduce(Y);
+ *       for the MLP A and B are linear layers, for attention A is multi-head attention
+ *       and B the output projection.
+ *     — "按行切分输入 X" / "按列切分权重 B" / "2D 切分（同时切 X 与 B）": the three splits
+ *       (rows of X along batch; columns of B, its last dimension; both).
+ *     — "反向：扩展与权重梯度计算的重叠": each grad matmul is two independent products
+ *       (input gradient, weight gradient); the input-gradient reduce hides behind the
+ *       weight-gradient products.
+ *     — "异步 AllReduce 的发起" / "μ-batch 流水": the reduce is issued asynchronously per
+ *       chunk and waited before its consumer.
+ *     — "如何尝试 DeepSpeed-Domino": causal self-attention only; the config fields
+ *       hidden_size, num_attention_heads, ffn_hidden_size, params_dtype.
+ *   "从单卡到集群…" (parallel-training primer), §3.1 "TP的切分方式与计算模式": column-parallel
+ *     first FFN layer, row-parallel second layer, partial sums reduced.
+ *   "04 · TP/SP 的通信-计算 overlap 与工程优化", §1: grad_input = grad_output·Wᵀ needs the
+ *     reduce, grad_weight = grad_outputᵀ·input is local and accumulates in fp32.
+ *
+ * Conventions shared by every call
+ *   Layout     Row-major, explicit sizes. Tokens are T = batch·seq rows, token = b·seq + i,
+ *              so a batch chunk is a contiguous row range. Weights are [in, out] (the X·A
+ *              convention). SwiGLU's A_s is [hidden, 2·ffn_shard] = [gate | up].
+ *   Dtypes     DOMINO_BF16: bf16 storage, fp32 accumulation, fp32 weight gradients.
+ *              DOMINO_F32: fp32 everywhere (MLP calls and shard_reduce only).
+ *   Pointers   Device pointers from hipMalloc (or torch), 16-byte aligned. Leading
+ *              dimensions are in elements. bf16 matrix widths must be multiples of 8.
+ *   Ownership  The caller owns every buffer and both streams. The library keeps no
+ *              per-call state; it creates its hipEvent_t objects once per device, lazily.
+ *   Streams    Work is enqueued on `compute`; the reductions run on `comm` after an event
+ *              wait on the chunk they reduce. Before returning, `compute` is made to wait
+ *              on every reduction (the handle wait of the asynchronous AllReduce), unless
+ *              the descriptor's `no_join` is set, in which case the reduced output is
+ *              valid only in `comm` order. comm == NULL or comm == compute runs the
+ *              reductions inline on `compute` (plain, un-overlapped tensor parallelism).
+ *              Peer partials must be ready in `compute` order when the call is made.
+ *   Errors     Every argument is checked before anything is enqueued; on an error
+ *              nothing runs and the status says why. A failed HIP launch returns
+ *              DOMINO_ERR_HIP (work enqueued before it may have run).
+ *   Threads    Calls may come from any host thread; calls that share output buffers
+ *              must be ordered by the caller.
+ */
+#ifndef DOMINO_H
+#define DOMINO_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DOMINO_OK = 0,
+  DOMINO_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, n_partials out of range */
+  DOMINO_ERR_SHAPE = 2,        /* sizes inconsistent or not divisible as required */
+  DOMINO_ERR_ALIGN = 3,        /* pointer not 16-byte aligned or width / ld not a multiple of 8 */
+  DOMINO_ERR_UNSUPPORTED = 4,  /* a valid combination this build does not implement */
+  DOMINO_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} domino_status;
+
+typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
+typedef enum { DOMINO_ACT_GELU_TANH = 0, DOMINO_ACT_SWIGLU = 1 } domino_act;
+
+/* Maximum number of partials one reduction sums (own partial included). */
+#define DOMINO_MAX_PARTIALS 16
+
+/* MLP shard: Y_s = act(X·A_s)·B_s with A_s [hidden, n1], B_s [ffn_shard, hidden],
+ * n1 = ffn_shard (GeLU) or 2·ffn_shard (SwiGLU). Chunks: (row_chunks, col_chunks) =
+ * (1,1) unsplit, (r,1) rows of X split along batch into r chunks, (1,c) columns of B_s
+ * into c chunks, (r,c) the 2D split, chunk order r0c0, r0c1, r1c0, ... */
+typedef struct {
+  int64_t batch, seq, hidden, ffn_shard;
+  int32_t act;          /* domino_act */
+  int32_t dtype;        /* domino_dtype */
+  int32_t row_chunks;   /* >= 1, divides batch */
+  int32_t col_chunks;   /* >= 1, hidden % (8·col_chunks) == 0 */
+  int32_t n_partials;   /* P = TP degree: own partial + P-1 peer partials; 1..DOMINO_MAX_PARTIALS */
+  int32_t no_join;      /* 0: compute waits on the reductions before return; 1: it does not */
+} domino_mlp_desc;
+
+/* Attention shard: heads · head_dim columns each of Q, K, V; causal self-attention. */
+typedef struct {
+  int64_t batch, seq, hidden, heads, head_dim;
+  float scale;          /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t dtype;        /* DOMINO_BF16 only */
+  int32_t row_chunks;   /* >= 1, divides batch (a chunk holds whole sequences) */
+  int32_t n_partials;
+  int32_t no_join;
+} domino_attn_desc;
+
+/*
+ * shard_reduce — the AllReduce's reduction on one GPU ("TP 的数据依赖：通信为何难以隐藏":
+ * AllReduce(Y) sums the ranks' partials; primer §3.1: row-parallel outputs are partial
+ * sums). out[r, c] = Σ_{p=0}^{n_partials-1} partials[p][r·ld_in + c] for r < rows,
+ * c < cols, accumulated in fp32 in the order p = 0, 1, ..., rounded once to the dtype
+ * (round to nearest even for bf16).
+ *   out        device, [rows, ld_out]; may alias partials[p] only if ld_out == ld_in
+ *   partials   HOST array of n_partials device pointers, each [rows, ld_in]
+ *   cols       multiple of 8 (bf16) or 4 (fp32); ld_* >= cols and multiples of 8 / 4
+ * rows == 0 or cols == 0 enqueues nothing and returns DOMINO_OK.
+ */
+domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partials, int32_t n_partials,
+                           int64_t ld_in, int64_t rows, int64_t cols, int32_t dtype, hipStream_t stream);
+
+/*
+ * domino_block_fwd — MLP shard forward in Domino chunks ("按行切分输入 X", "按列切分权重 B",
+ * "2D 切分"; primer §3.1 for the column→row pairing).
+ * For each row chunk R_i: Hpre[R_i] = X[R_i]·A_s and H[R_i] = act(Hpre[R_i]) (GEMM with a
+ * fused activation epilogue); then for each column chunk C_j: Y_own[R_i, C_j] =
+ * H[R_i]·B_s[:, C_j], and the chunk's reduction Y[R_i, C_j] = Y_own + Σ peer_Y runs on
+ * `comm` while the next chunk's GEMMs run on `compute`.
+ *   X [T, hidden]; A_s [hidden, n1]; B_s [ffn_shard, hidden]            (inputs)
+ *   Hpre [T, n1], H [T, ffn_shard]     saved for the backward           (outputs)
+ *   Y_own [T, hidden]                  this rank's partial              (output)
+ *   peer_Y  HOST array of n_partials-1 device pointers [T, hidden]      (inputs; NULL if P==1)
+ *   Y [T, hidden]                      reduced output; NULL or Y_own reduces in place into
+ *                                      Y_own (with P == 1 that means no reduction runs)
+ */
+domino_status domino_block_fwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
+                               void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
+                               hipStream_t compute, hipStream_t comm);
+
+/* Bytes of `workspace` domino_block_bwd can use for split-K weight gradients (0 is
+ * always valid: the call then runs without split-K). */
+size_t domino_block_bwd_workspace_size(const domino_mlp_desc* desc);
+
+/*
+ * domino_block_bwd — MLP shard backward ("反向：扩展与权重梯度计算的重叠"; overlap page §1).
+ * Per dX chunk (row chunks; for a column-only split, column chunks of dX, the mirror of
+ * the forward's column split; the 2D split reduces dX by row chunks):
+ *   dHpre = act'(Hpre) ⊙ (dY·B_sᵀ)      (GEMM with a fused activation-gradient epilogue)
+ *   dX_own[chunk] = dHpre·A_s[chunk]ᵀ   (this rank's partial input gradient)
+ *   dX[chunk] = dX_own + Σ peer_dX      (reduction on `comm`)
+ * then the independent weight gradients, which hide the last reduction:
+ *   dB_s (+)= Hᵀ·dY,  dA_s (+)= Xᵀ·dHpre     (fp32; accumulate != 0 adds to their contents)
+ *   X, A_s, B_s, Hpre, H as in the forward; dY [T, hidden]                (inputs)
+ *   dHpre [T, n1]                       caller-provided scratch/output (bf16 or fp32)
+ *   dX_own, dX [T, hidden]; peer_dX HOST array of n_partials-1 device pointers; dX NULL or
+ *                                       dX_own reduces in place into dX_own
+ *   dA_s [hidden, n1], dB_s [ffn_shard, hidden]  fp32
+ *   workspace, workspace_bytes          optional device scratch (see _workspace_size)
+ * Weight gradients are deterministic; the reduction order is fixed.
+ */
+domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
+                               const void* Hpre, const void* H, const void* dY, void* dHpre,
+                               void* dX_own, const void* const* peer_dX, void* dX,
+                               float* dA_s, float* dB_s, int32_t accumulate,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t compute, hipStream_t comm);
+
+/*
+ * domino_attn_block_fwd — attention shard forward by row chunks (whole sequences)
+ * ("TP 的数据依赖…": A = multi-head attention on the rank's heads, B = output projection;
+ * "前向：多个计算片段轮转重叠 AllReduce": AllReduce(attn0) overlaps μ-batch 1's attention).
+ * Per chunk: QKV = X·A_qkv_s; O = causal softmax(Q·Kᵀ·scale)·V per (sequence, head);
+ * Y_own = O·B_o_s; Y = Y_own + Σ peer_Y on `comm`.
+ *   X [T, hidden]; A_qkv_s [hidden, 3·heads·head_dim] = [Q | K | V] blocks, head j at
+ *   columns j·head_dim within each block; B_o_s [heads·head_dim, hidden]   (inputs)
+ *   QKV [T, 3·heads·head_dim], O [T, heads·head_dim]   saved activations   (outputs)
+ *   Y_own, Y [T, hidden]; peer_Y HOST array of n_partials-1 device pointers
+ * head_dim must be 128; bf16 only.
+ */
+domino_status domino_attn_block_fwd(const domino_attn_desc* desc, const void* X, const void* A_qkv_s,
+                                    const void* B_o_s, void* QKV, void* O, void* Y_own,
+                                    const void* const* peer_Y, void* Y, hipStream_t compute, hipStream_t comm);
+
+/* Human-readable name of a status code (static storage). */
+const char* domino_status_string(domino_status status);
+
+/* Text of the most recent error on the calling thread (static thread-local storage). */
+const char* domino_last_error(void);
+
+/*
+ * Kernel timing for measurement: while enabled, every kernel the library launches is
+ * bracketed by a pair of hipEvents recorded on the stream it runs on. domino_timing_read
+ * waits for those events and returns, for kernel class `kind`, the number of launches
+ * and their summed duration in milliseconds since the last reset. Timing adds two event
+ * records per launch; keep it off outside measurement.
+ */
+typedef enum {
+  DOMINO_K_REDUCE = 0,
+  DOMINO_K_FWD_GEMM1 = 1,   /* X·A_s + activation epilogue */
+  DOMINO_K_FWD_GEMM2 = 2,   /* H·B_s[:, C_j] */
+  DOMINO_K_DGRAD_B = 3,     /* dY·B_sᵀ + activation-gradient epilogue */
+  DOMINO_K_DGRAD_A = 4,     /* dHpre·A_sᵀ */
+  DOMINO_K_WGRAD_B = 5,     /* Hᵀ·dY */
+  DOMINO_K_WGRAD_A = 6,     /* Xᵀ·dHpre */
+  DOMINO_K_QKV = 7,
+  DOMINO_K_ATTN = 8,
+  DOMINO_K_OUTPROJ = 9,
+  DOMINO_K_AUX = 10,        /* fills and split-K sums */
+  DOMINO_K_COUNT = 11
+} domino_kernel_kind;
+
+domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */
+domino_status domino_timing_read(int32_t kind, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DOMINO_H */

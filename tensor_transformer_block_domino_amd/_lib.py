@@ -1,0 +1,160 @@
+"""ctypes binding of libdomino_mi355x.so: the same calls as include/domino.h, argument
+marshalling only (tensors → device pointers, streams → hipStream_t handles, status →
+exception). Every step of the layer runs in the library's HIP kernels; there is no
+fallback path: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_NAME = "libdomino_mi355x.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+# Mirrors of the header's enums and descriptor structs.
+DOMINO_F32, DOMINO_BF16 = 0, 1
+DOMINO_ACT_GELU_TANH, DOMINO_ACT_SWIGLU = 0, 1
+DOMINO_MAX_PARTIALS = 16
+STATUS_NAMES = {0: "DOMINO_OK", 1: "DOMINO_ERR_INVALID_ARG", 2: "DOMINO_ERR_SHAPE", 3: "DOMINO_ERR_ALIGN",
+                4: "DOMINO_ERR_UNSUPPORTED", 5: "DOMINO_ERR_HIP"}
+KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgrad_a": 4, "wgrad_b": 5,
+                "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10}
+
+# Every symbol the header declares (checked by the CPU export test).
+EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_bwd", "domino_block_bwd_workspace_size",
+            "domino_attn_block_fwd", "domino_status_string", "domino_last_error", "domino_timing_enable",
+            "domino_timing_read")
+
+
+class MlpDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("ffn_shard", ctypes.c_int64), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("row_chunks", ctypes.c_int32), ("col_chunks", ctypes.c_int32), ("n_partials", ctypes.c_int32),
+                ("no_join", ctypes.c_int32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("row_chunks", ctypes.c_int32), ("n_partials", ctypes.c_int32),
+                ("no_join", ctypes.c_int32)]
+
+
+class DominoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with tensor_transformer_block_domino_amd.build.build()")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.shard_reduce.argtypes = [vp, i64, pp, i32, i64, i64, i64, i32, vp]
+    lib.shard_reduce.restype = i32
+    lib.domino_block_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, vp]
+    lib.domino_block_fwd.restype = i32
+    lib.domino_block_bwd_workspace_size.argtypes = [ctypes.POINTER(MlpDesc)]
+    lib.domino_block_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32,
+                                     vp, ctypes.c_size_t, vp, vp]
+    lib.domino_block_bwd.restype = i32
+    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, vp]
+    lib.domino_attn_block_fwd.restype = i32
+    lib.domino_status_string.argtypes = [i32]
+    lib.domino_status_string.restype = ctypes.c_char_p
+    lib.domino_last_error.argtypes = []
+    lib.domino_last_error.restype = ctypes.c_char_p
+    lib.domino_timing_enable.argtypes = [i32]
+    lib.domino_timing_enable.restype = i32
+    lib.domino_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    lib.domino_timing_read.restype = i32
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------------------
+# Marshalling.
+# ---------------------------------------------------------------------------------------
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _ptr_array(items: Optional[Sequence]):
+    if items is None:
+        return None
+    arr = (ctypes.c_void_p * max(1, len(items)))()
+    for i, t in enumerate(items):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _check(status: int):
+    if status != 0:
+        raise DominoError(status, load().domino_last_error().decode())
+
+
+def shard_reduce(out, ld_out: int, partials: Sequence, ld_in: int, rows: int, cols: int, dtype: int, stream=None):
+    _check(load().shard_reduce(_ptr(out), ld_out, _ptr_array(partials), len(partials), ld_in, rows, cols, dtype,
+                               _stream(stream)))
+
+
+def domino_block_fwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, Y_own, peer_Y, Y, compute=None, comm=None):
+    _check(load().domino_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H),
+                                   _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _stream(compute), _stream(comm)))
+
+
+def domino_block_bwd_workspace_size(desc: MlpDesc) -> int:
+    return int(load().domino_block_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def domino_block_bwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, peer_dX, dX, dA_s, dB_s,
+                     accumulate: int = 0, workspace=None, workspace_bytes: int = 0, compute=None, comm=None):
+    _check(load().domino_block_bwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H), _ptr(dY),
+                                   _ptr(dHpre), _ptr(dX_own), _ptr_array(peer_dX), _ptr(dX), _ptr(dA_s), _ptr(dB_s),
+                                   int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
+                                   _stream(comm)))
+
+
+def domino_attn_block_fwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, Y_own, peer_Y, Y, compute=None, comm=None):
+    _check(load().domino_attn_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
+                                        _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _stream(compute), _stream(comm)))
+
+
+def domino_status_string(status: int) -> str:
+    return load().domino_status_string(status).decode()
+
+
+def domino_timing_enable(enable: bool):
+    _check(load().domino_timing_enable(1 if enable else 0))
+
+
+def domino_timing_read(kind) -> tuple:
+    """(launches, total_ms) for a kernel class name or number since timing was enabled."""
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(load().domino_timing_read(k, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

@@ -1,0 +1,546 @@
+// C ABI of the Domino shard library: argument validation and the two-stream chunk
+// scheduler that turns one call into the chunked kernel sequence.
+//
+// The scheduler follows the pages' Domino schedule (page "DeepSpeed-Domino 深度解析"):
+//  * the layer's input rows are split along batch ("按行切分输入 X"), the second weight
+//    along its last dimension ("按列切分权重 B"), or both ("2D 切分"); each chunk's output is
+//    independent, so its reduction can start as soon as that chunk's products end;
+//  * the reductions are issued asynchronously on a second stream and waited only by the
+//    consumer ("异步 AllReduce 的发起", "μ-batch 流水"): here `compute` records an event after
+//    a chunk's last product, `comm` waits on it and reduces, and `compute` finally waits
+//    on `comm` (the handle wait);
+//  * in the backward, the input-gradient chunks and their reductions come first and the
+//    independent weight-gradient products follow, hiding the last reduction
+//    ("反向：扩展与权重梯度计算的重叠"; page "04 · TP/SP 的通信-计算 overlap 与工程优化", §1).
+// One hipEvent_t pair per chunk stands in for the pages' communication handles.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/domino.h"
+#include "kernels.hpp"
+
+using namespace domino;
+
+namespace {
+
+thread_local std::string t_last_error;
+
+domino_status fail(domino_status st, const std::string& msg) {
+  t_last_error = msg;
+  return st;
+}
+
+// ---------------------------------------------------------------------------------------
+// Events: a per-thread, per-device set, created once and reused by every call.
+// ---------------------------------------------------------------------------------------
+constexpr int kMaxChunks = 64;
+struct EventSet {
+  bool ready = false;
+  hipEvent_t done[kMaxChunks];  // compute: chunk's products finished
+  hipEvent_t reduced;           // comm: last reduction finished
+};
+constexpr int kMaxDevices = 64;
+thread_local EventSet t_events[kMaxDevices];
+
+hipError_t events_for_current_device(EventSet** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  EventSet& es = t_events[dev];
+  if (!es.ready) {
+    for (int i = 0; i < kMaxChunks; ++i) {
+      e = hipEventCreateWithFlags(&es.done[i], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    es.ready = true;
+  }
+  *out = &es;
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------------------
+// Kernel timing (measurement only).
+// ---------------------------------------------------------------------------------------
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_timing_mu;
+bool g_timing = false;
+std::vector<TimingRec> g_timing_recs;
+std::vector<hipEvent_t> g_timing_free;
+double g_timing_ms[DOMINO_K_COUNT];
+int64_t g_timing_n[DOMINO_K_COUNT];
+
+hipEvent_t timing_event() {
+  if (!g_timing_free.empty()) {
+    hipEvent_t e = g_timing_free.back();
+    g_timing_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& f) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    on = g_timing;
+  }
+  if (!on) return f();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    a = timing_event();
+    b = timing_event();
+  }
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = f();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing_recs.push_back({kind, a, b});
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------------------
+// Validation helpers.
+// ---------------------------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+domino_status check_ptr(const void* p, const char* name, bool needed) {
+  if (!needed) return DOMINO_OK;
+  if (!p) return fail(DOMINO_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(DOMINO_ERR_ALIGN, std::string(name) + " is not 16-byte aligned");
+  return DOMINO_OK;
+}
+
+domino_status check_peers(const void* const* peers, int n_partials, const char* name, bool needed) {
+  if (!needed || n_partials <= 1) return DOMINO_OK;
+  if (!peers) return fail(DOMINO_ERR_INVALID_ARG, std::string(name) + " is NULL but n_partials > 1");
+  for (int p = 0; p < n_partials - 1; ++p) {
+    const std::string nm = std::string(name) + "[" + std::to_string(p) + "]";
+    const domino_status st = check_ptr(peers[p], nm.c_str(), true);
+    if (st != DOMINO_OK) return st;
+  }
+  return DOMINO_OK;
+}
+
+hipError_t hip_ok(hipError_t e, std::string* msg, const char* what) {
+  if (e != hipSuccess) *msg = std::string(what) + ": " + hipGetErrorString(e);
+  return e;
+}
+
+size_t esize(int dtype) { return dtype == DOMINO_BF16 ? 2 : 4; }
+
+// Reduction of one chunk [rows × cols] at element offset `off` of [·, ld] buffers.
+hipError_t reduce_chunk(void* out, const void* own, const void* const* peers, int n_partials, int64_t ld, int64_t off,
+                        int64_t rows, int64_t cols, int dtype, hipStream_t s) {
+  ReduceArgs ra{};
+  const size_t es = esize(dtype);
+  ra.out = static_cast<char*>(out) + off * es;
+  ra.ld_out = ld;
+  ra.partials[0] = static_cast<const char*>(own) + off * es;
+  for (int p = 1; p < n_partials; ++p) ra.partials[p] = static_cast<const char*>(peers[p - 1]) + off * es;
+  ra.n_partials = n_partials;
+  ra.ld_in = ld;
+  ra.rows = rows;
+  ra.cols = cols;
+  ra.bf16 = dtype == DOMINO_BF16;
+  return timed(DOMINO_K_REDUCE, s, [&] { return launch_shard_reduce(ra, s); });
+}
+
+// The reduction step of the schedule: after the chunk's products on `cs`, reduce it on
+// `rs` (inline if rs == cs).
+struct Sched {
+  hipStream_t cs, rs;
+  bool overlap;
+  EventSet* ev;
+  int next_event = 0;
+  bool any_reduce = false;
+  hipError_t reduce(void* out, const void* own, const void* const* peers, int n_partials, int64_t ld, int64_t off,
+                    int64_t rows, int64_t cols, int dtype) {
+    hipError_t e = hipSuccess;
+    if (overlap) {
+      hipEvent_t done = ev->done[next_event++ % kMaxChunks];
+      e = hipEventRecord(done, cs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(rs, done, 0);
+    }
+    if (e == hipSuccess) e = reduce_chunk(out, own, peers, n_partials, ld, off, rows, cols, dtype, rs);
+    any_reduce = true;
+    return e;
+  }
+  hipError_t join() {
+    if (!overlap || !any_reduce) return hipSuccess;
+    hipError_t e = hipEventRecord(ev->reduced, rs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev->reduced, 0);
+    return e;
+  }
+};
+
+domino_status make_sched(hipStream_t compute, hipStream_t comm, Sched* s) {
+  s->cs = compute;
+  s->rs = (comm && comm != compute) ? comm : compute;
+  s->overlap = s->rs != s->cs;
+  s->ev = nullptr;
+  if (s->overlap) {
+    std::string msg;
+    if (hip_ok(events_for_current_device(&s->ev), &msg, "event setup") != hipSuccess)
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  return DOMINO_OK;
+}
+
+domino_status check_mlp_desc(const domino_mlp_desc* d) {
+  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
+  if (d->act != DOMINO_ACT_GELU_TANH && d->act != DOMINO_ACT_SWIGLU) return fail(DOMINO_ERR_INVALID_ARG, "bad act");
+  if (d->dtype != DOMINO_BF16 && d->dtype != DOMINO_F32) return fail(DOMINO_ERR_INVALID_ARG, "bad dtype");
+  if (d->batch < 0 || d->seq < 0 || d->hidden < 0 || d->ffn_shard < 0)
+    return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (d->row_chunks < 1 || d->col_chunks < 1) return fail(DOMINO_ERR_SHAPE, "row_chunks and col_chunks must be >= 1");
+  if (int64_t(d->row_chunks) * d->col_chunks > kMaxChunks) return fail(DOMINO_ERR_UNSUPPORTED, "too many chunks");
+  if (d->n_partials < 1 || d->n_partials > DOMINO_MAX_PARTIALS)
+    return fail(DOMINO_ERR_INVALID_ARG, "n_partials must be in 1..DOMINO_MAX_PARTIALS");
+  if (d->batch % d->row_chunks) return fail(DOMINO_ERR_SHAPE, "batch % row_chunks != 0");
+  const int64_t al = d->dtype == DOMINO_BF16 ? 8 : 4;
+  if (d->hidden % (al * d->col_chunks))
+    return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of col_chunks * (8 for bf16, 4 for fp32)");
+  if (d->ffn_shard % al) return fail(DOMINO_ERR_ALIGN, "ffn_shard must be a multiple of 8 (bf16) or 4 (fp32)");
+  const int64_t T = d->batch * d->seq;
+  if (T > (int64_t(1) << 31) || d->hidden > (int64_t(1) << 31) || d->ffn_shard > (int64_t(1) << 30))
+    return fail(DOMINO_ERR_UNSUPPORTED, "size beyond 32-bit tile indexing");
+  return DOMINO_OK;
+}
+
+bool needs_reduce(int n_partials, const void* own, const void* out) { return n_partials > 1 || (out && out != own); }
+
+}  // namespace
+
+extern "C" {
+
+const char* domino_status_string(domino_status st) {
+  switch (st) {
+    case DOMINO_OK: return "DOMINO_OK";
+    case DOMINO_ERR_INVALID_ARG: return "DOMINO_ERR_INVALID_ARG";
+    case DOMINO_ERR_SHAPE: return "DOMINO_ERR_SHAPE";
+    case DOMINO_ERR_ALIGN: return "DOMINO_ERR_ALIGN";
+    case DOMINO_ERR_UNSUPPORTED: return "DOMINO_ERR_UNSUPPORTED";
+    case DOMINO_ERR_HIP: return "DOMINO_ERR_HIP";
+  }
+  return "DOMINO_ERR_UNKNOWN";
+}
+
+const char* domino_last_error(void) { return t_last_error.c_str(); }
+
+domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partials, int32_t n_partials, int64_t ld_in,
+                           int64_t rows, int64_t cols, int32_t dtype, hipStream_t stream) {
+  t_last_error.clear();
+  if (dtype != DOMINO_BF16 && dtype != DOMINO_F32) return fail(DOMINO_ERR_INVALID_ARG, "bad dtype");
+  if (n_partials < 1 || n_partials > DOMINO_MAX_PARTIALS)
+    return fail(DOMINO_ERR_INVALID_ARG, "n_partials must be in 1..DOMINO_MAX_PARTIALS");
+  if (rows < 0 || cols < 0) return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (rows == 0 || cols == 0) return DOMINO_OK;
+  if (!partials) return fail(DOMINO_ERR_INVALID_ARG, "partials is NULL");
+  const int64_t al = dtype == DOMINO_BF16 ? 8 : 4;
+  if (cols % al || ld_in % al || ld_out % al)
+    return fail(DOMINO_ERR_ALIGN, "cols and leading dimensions must be multiples of 8 (bf16) / 4 (fp32)");
+  if (ld_in < cols || ld_out < cols) return fail(DOMINO_ERR_SHAPE, "leading dimension smaller than cols");
+  if (rows * (cols / al) > int64_t(0xffffffffu)) return fail(DOMINO_ERR_UNSUPPORTED, "region too large");
+  domino_status st = check_ptr(out, "out", true);
+  if (st != DOMINO_OK) return st;
+  for (int p = 0; p < n_partials; ++p) {
+    const std::string nm = "partials[" + std::to_string(p) + "]";
+    st = check_ptr(partials[p], nm.c_str(), true);
+    if (st != DOMINO_OK) return st;
+    if (partials[p] == out && ld_in != ld_out)
+      return fail(DOMINO_ERR_INVALID_ARG, "out aliases a partial with a different leading dimension");
+  }
+  ReduceArgs ra{};
+  ra.out = out;
+  ra.ld_out = ld_out;
+  for (int p = 0; p < n_partials; ++p) ra.partials[p] = partials[p];
+  ra.n_partials = n_partials;
+  ra.ld_in = ld_in;
+  ra.rows = rows;
+  ra.cols = cols;
+  ra.bf16 = dtype == DOMINO_BF16;
+  std::string msg;
+  if (hip_ok(timed(DOMINO_K_REDUCE, stream, [&] { return launch_shard_reduce(ra, stream); }), &msg, "shard_reduce") !=
+      hipSuccess)
+    return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s, void* Hpre,
+                               void* H, void* Y_own, const void* const* peer_Y, void* Y, hipStream_t compute,
+                               hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_mlp_desc(d);
+  if (st != DOMINO_OK) return st;
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
+  const bool sw = d->act == DOMINO_ACT_SWIGLU;
+  const int64_t n1 = sw ? 2 * f : f;
+  if (T == 0 || h == 0) return DOMINO_OK;
+  const bool red = needs_reduce(d->n_partials, Y_own, Y);
+  if ((st = check_ptr(X, "X", true)) || (st = check_ptr(A_s, "A_s", f > 0)) || (st = check_ptr(B_s, "B_s", f > 0)) ||
+      (st = check_ptr(Hpre, "Hpre", f > 0)) || (st = check_ptr(H, "H", f > 0)) || (st = check_ptr(Y_own, "Y_own", true)) ||
+      (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) || (st = check_ptr(Y ? Y : Y_own, "Y", red)))
+    return st;
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+
+  const bool bf = d->dtype == DOMINO_BF16;
+  const size_t es = esize(d->dtype);
+  const int64_t Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
+  std::string msg;
+  for (int i = 0; i < d->row_chunks; ++i) {
+    const int64_t r0 = i * Tc;
+    if (f > 0) {
+      GemmArgs g1{};
+      g1.M = Tc; g1.N = f; g1.K = h;
+      g1.A = static_cast<const char*>(X) + r0 * h * es; g1.lda = h; g1.a_kcontig = true;
+      g1.B = A_s; g1.ldb = n1; g1.b_kcontig = false;
+      g1.C = static_cast<char*>(Hpre) + r0 * n1 * es; g1.ldc = n1;
+      g1.C2 = static_cast<char*>(H) + r0 * f * es; g1.ldc2 = f;
+      g1.f_s = f;
+      g1.epi = sw ? Epi::kSwiglu : Epi::kGelu;
+      g1.bf16 = bf;
+      if (hip_ok(timed(DOMINO_K_FWD_GEMM1, sc.cs, [&] { return launch_gemm(g1, sc.cs, nullptr); }), &msg, "GEMM1"))
+        return fail(DOMINO_ERR_HIP, msg);
+    }
+    for (int j = 0; j < d->col_chunks; ++j) {
+      const int64_t c0 = j * hc;
+      GemmArgs g2{};
+      g2.M = Tc; g2.N = hc; g2.K = f;
+      g2.A = static_cast<const char*>(H) + r0 * f * es; g2.lda = f; g2.a_kcontig = true;
+      g2.B = static_cast<const char*>(B_s) + c0 * es; g2.ldb = h; g2.b_kcontig = false;
+      g2.C = static_cast<char*>(Y_own) + (r0 * h + c0) * es; g2.ldc = h;
+      g2.epi = Epi::kStore;
+      g2.bf16 = bf;
+      if (hip_ok(timed(DOMINO_K_FWD_GEMM2, sc.cs, [&] { return launch_gemm(g2, sc.cs, nullptr); }), &msg, "GEMM2"))
+        return fail(DOMINO_ERR_HIP, msg);
+      if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, r0 * h + c0, Tc, hc, d->dtype),
+                        &msg, "reduce Y"))
+        return fail(DOMINO_ERR_HIP, msg);
+    }
+  }
+  if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+size_t domino_block_bwd_workspace_size(const domino_mlp_desc* d) {
+  if (check_mlp_desc(d) != DOMINO_OK || d->dtype != DOMINO_BF16) return 0;
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
+  const int64_t n1 = d->act == DOMINO_ACT_SWIGLU ? 2 * f : f;
+  const int64_t a = gemm_splitk_ws_elems(f, h, T), b = gemm_splitk_ws_elems(h, n1, T);
+  return size_t(a > b ? a : b) * sizeof(float);
+}
+
+domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
+                               const void* Hpre, const void* H, const void* dY, void* dHpre, void* dX_own,
+                               const void* const* peer_dX, void* dX, float* dA_s, float* dB_s, int32_t accumulate,
+                               void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_mlp_desc(d);
+  if (st != DOMINO_OK) return st;
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
+  const bool sw = d->act == DOMINO_ACT_SWIGLU;
+  const int64_t n1 = sw ? 2 * f : f;
+  if (h == 0) return DOMINO_OK;
+  const bool red = T > 0 && needs_reduce(d->n_partials, dX_own, dX);
+  const bool tok = T > 0, ffn = f > 0;
+  if ((st = check_ptr(X, "X", tok && ffn)) || (st = check_ptr(A_s, "A_s", tok && ffn)) ||
+      (st = check_ptr(B_s, "B_s", tok && ffn)) || (st = check_ptr(Hpre, "Hpre", tok && ffn)) ||
+      (st = check_ptr(H, "H", tok && ffn)) || (st = check_ptr(dY, "dY", tok && ffn)) ||
+      (st = check_ptr(dHpre, "dHpre", tok && ffn)) || (st = check_ptr(dX_own, "dX_own", tok)) ||
+      (st = check_peers(peer_dX, d->n_partials, "peer_dX", red)) || (st = check_ptr(dX ? dX : dX_own, "dX", red)) ||
+      (st = check_ptr(dA_s, "dA_s", ffn)) || (st = check_ptr(dB_s, "dB_s", ffn)))
+    return st;
+  if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+
+  const bool bf = d->dtype == DOMINO_BF16;
+  const size_t es = esize(d->dtype);
+  // dX chunks: row chunks when rows are split (row or 2D split), else the column chunks.
+  const int rch = d->row_chunks, cch = d->row_chunks > 1 ? 1 : d->col_chunks;
+  const int64_t Tc = (d->batch / rch) * d->seq, hc = h / cch;
+  std::string msg;
+  for (int i = 0; i < rch && tok; ++i) {
+    const int64_t r0 = i * Tc;
+    if (ffn) {
+      GemmArgs gb{};
+      gb.M = Tc; gb.N = f; gb.K = h;
+      gb.A = static_cast<const char*>(dY) + r0 * h * es; gb.lda = h; gb.a_kcontig = true;
+      gb.B = B_s; gb.ldb = h; gb.b_kcontig = true;          // B(k, n) = B_s[n][k]
+      gb.C = static_cast<char*>(dHpre) + r0 * n1 * es; gb.ldc = n1;
+      gb.aux = static_cast<const char*>(Hpre) + r0 * n1 * es; gb.ldaux = n1;
+      gb.f_s = f;
+      gb.epi = sw ? Epi::kDSwiglu : Epi::kDGelu;
+      gb.bf16 = bf;
+      if (hip_ok(timed(DOMINO_K_DGRAD_B, sc.cs, [&] { return launch_gemm(gb, sc.cs, nullptr); }), &msg, "dgrad B"))
+        return fail(DOMINO_ERR_HIP, msg);
+    }
+    for (int j = 0; j < cch; ++j) {
+      const int64_t c0 = j * hc;
+      GemmArgs ga{};
+      ga.M = Tc; ga.N = hc; ga.K = n1;
+      ga.A = static_cast<const char*>(dHpre) + r0 * n1 * es; ga.lda = n1; ga.a_kcontig = true;
+      ga.B = static_cast<const char*>(A_s) + c0 * n1 * es; ga.ldb = n1; ga.b_kcontig = true;  // B(k,n) = A_s[n][k]
+      ga.C = static_cast<char*>(dX_own) + (r0 * h + c0) * es; ga.ldc = h;
+      ga.epi = Epi::kStore;
+      ga.bf16 = bf;
+      if (hip_ok(timed(DOMINO_K_DGRAD_A, sc.cs, [&] { return launch_gemm(ga, sc.cs, nullptr); }), &msg, "dgrad A"))
+        return fail(DOMINO_ERR_HIP, msg);
+      if (red && hip_ok(sc.reduce(dX ? dX : dX_own, dX_own, peer_dX, d->n_partials, h, r0 * h + c0, Tc, hc, d->dtype),
+                        &msg, "reduce dX"))
+        return fail(DOMINO_ERR_HIP, msg);
+    }
+  }
+  if (ffn) {
+    float* ws = static_cast<float*>(workspace);
+    const int64_t ws_elems = int64_t(workspace_bytes / sizeof(float));
+    GemmArgs wb{};
+    wb.M = f; wb.N = h; wb.K = T;
+    wb.A = H; wb.lda = f; wb.a_kcontig = false;       // A(m, k) = H[k][m]
+    wb.B = dY; wb.ldb = h; wb.b_kcontig = false;      // B(k, n) = dY[k][n]
+    wb.C = dB_s; wb.ldc = h;
+    wb.epi = Epi::kF32;
+    wb.accumulate = accumulate;
+    wb.ws = ws; wb.ws_elems = ws_elems;
+    wb.bf16 = bf;
+    if (hip_ok(timed(DOMINO_K_WGRAD_B, sc.cs, [&] { return launch_gemm(wb, sc.cs, nullptr); }), &msg, "wgrad B"))
+      return fail(DOMINO_ERR_HIP, msg);
+    GemmArgs wa{};
+    wa.M = h; wa.N = n1; wa.K = T;
+    wa.A = X; wa.lda = h; wa.a_kcontig = false;       // A(m, k) = X[k][m]
+    wa.B = dHpre; wa.ldb = n1; wa.b_kcontig = false;  // B(k, n) = dHpre[k][n]
+    wa.C = dA_s; wa.ldc = n1;
+    wa.epi = Epi::kF32;
+    wa.accumulate = accumulate;
+    wa.ws = ws; wa.ws_elems = ws_elems;
+    wa.bf16 = bf;
+    if (hip_ok(timed(DOMINO_K_WGRAD_A, sc.cs, [&] { return launch_gemm(wa, sc.cs, nullptr); }), &msg, "wgrad A"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
+                                    void* QKV, void* O, void* Y_own, const void* const* peer_Y, void* Y,
+                                    hipStream_t compute, hipStream_t comm) {
+  t_last_error.clear();
+  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != DOMINO_BF16) {
+    if (d->dtype == DOMINO_F32) return fail(DOMINO_ERR_UNSUPPORTED, "attention is bf16 only");
+    return fail(DOMINO_ERR_INVALID_ARG, "bad dtype");
+  }
+  if (d->batch < 0 || d->seq < 0 || d->hidden < 0 || d->heads < 0) return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (d->head_dim != 128) return fail(DOMINO_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->row_chunks < 1 || d->row_chunks > kMaxChunks) return fail(DOMINO_ERR_SHAPE, "bad row_chunks");
+  if (d->batch % d->row_chunks) return fail(DOMINO_ERR_SHAPE, "batch % row_chunks != 0");
+  if (d->n_partials < 1 || d->n_partials > DOMINO_MAX_PARTIALS)
+    return fail(DOMINO_ERR_INVALID_ARG, "n_partials must be in 1..DOMINO_MAX_PARTIALS");
+  if (d->hidden % 8) return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of 8");
+  if (!(d->scale >= 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "scale must be >= 0 (0 selects 1/sqrt(head_dim))");
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  if (T > (int64_t(1) << 31) || d->seq > (int64_t(1) << 30)) return fail(DOMINO_ERR_UNSUPPORTED, "too many tokens");
+  if (T == 0 || h == 0) return DOMINO_OK;
+  const bool red = needs_reduce(d->n_partials, Y_own, Y);
+  const bool heads = d->heads > 0;
+  domino_status st;
+  if ((st = check_ptr(X, "X", heads)) || (st = check_ptr(A_qkv_s, "A_qkv_s", heads)) ||
+      (st = check_ptr(B_o_s, "B_o_s", heads)) || (st = check_ptr(QKV, "QKV", heads)) || (st = check_ptr(O, "O", heads)) ||
+      (st = check_ptr(Y_own, "Y_own", true)) || (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) ||
+      (st = check_ptr(Y ? Y : Y_own, "Y", red)))
+    return st;
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+  const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
+  const int64_t bc = d->batch / d->row_chunks, Tc = bc * d->seq;
+  std::string msg;
+  for (int i = 0; i < d->row_chunks; ++i) {
+    const int64_t r0 = i * Tc;
+    char* qkv = static_cast<char*>(QKV) + r0 * 3 * hd * 2;
+    char* o = static_cast<char*>(O) + r0 * hd * 2;
+    GemmArgs gq{};
+    gq.M = Tc; gq.N = 3 * hd; gq.K = h;
+    gq.A = static_cast<const char*>(X) + r0 * h * 2; gq.lda = h; gq.a_kcontig = true;
+    gq.B = A_qkv_s; gq.ldb = 3 * hd; gq.b_kcontig = false;
+    gq.C = qkv; gq.ldc = 3 * hd;
+    gq.epi = Epi::kStore;
+    gq.bf16 = true;
+    GemmArgs go{};
+    go.M = Tc; go.N = h; go.K = hd;
+    go.A = o; go.lda = hd; go.a_kcontig = true;
+    go.B = B_o_s; go.ldb = h; go.b_kcontig = false;
+    go.C = static_cast<char*>(Y_own) + r0 * h * 2; go.ldc = h;
+    go.epi = Epi::kStore;
+    go.bf16 = true;
+    AttnArgs aa{};
+    aa.qkv = qkv; aa.ld_qkv = 3 * hd;
+    aa.o = o; aa.ld_o = hd;
+    aa.batch = bc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
+    aa.scale = scale;
+    if (heads) {
+      if (hip_ok(timed(DOMINO_K_QKV, sc.cs, [&] { return launch_gemm(gq, sc.cs, nullptr); }), &msg, "QKV GEMM") ||
+          hip_ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), &msg, "attention"))
+        return fail(DOMINO_ERR_HIP, msg);
+    }
+    if (hip_ok(timed(DOMINO_K_OUTPROJ, sc.cs, [&] { return launch_gemm(go, sc.cs, nullptr); }), &msg, "out-projection"))
+      return fail(DOMINO_ERR_HIP, msg);
+    if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, r0 * h, Tc, h, DOMINO_BF16), &msg,
+                      "reduce Y"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+domino_status domino_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& r : g_timing_recs) {
+    g_timing_free.push_back(r.a);
+    g_timing_free.push_back(r.b);
+  }
+  g_timing_recs.clear();
+  for (int k = 0; k < DOMINO_K_COUNT; ++k) {
+    g_timing_ms[k] = 0.0;
+    g_timing_n[k] = 0;
+  }
+  g_timing = enable != 0;
+  return DOMINO_OK;
+}
+
+domino_status domino_timing_read(int32_t kind, int64_t* launches, double* total_ms) {
+  t_last_error.clear();
+  if (kind < 0 || kind >= DOMINO_K_COUNT || !launches || !total_ms) return fail(DOMINO_ERR_INVALID_ARG, "bad argument");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& r : g_timing_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return fail(DOMINO_ERR_HIP, "timing event query failed");
+    g_timing_ms[r.kind] += ms;
+    g_timing_n[r.kind] += 1;
+    g_timing_free.push_back(r.a);
+    g_timing_free.push_back(r.b);
+  }
+  g_timing_recs.clear();
+  *launches = g_timing_n[kind];
+  *total_ms = g_timing_ms[kind];
+  return DOMINO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Host-side launchers of the library's HIP kernels (internal interface; no checks here —
+// the C ABI validates every argument before any launcher runs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace domino {
+
+constexpr int kMaxPartials = 16;
+
+struct ReduceArgs {
+  void* out;
+  int64_t ld_out;
+  const void* partials[kMaxPartials];
+  int n_partials;
+  int64_t ld_in;
+  int64_t rows, cols;
+  bool bf16;
+};
+hipError_t launch_shard_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_splitk_sum(float* out, int64_t ldc, const float* ws, int splits, int64_t rows, int64_t cols,
+                             int accumulate, hipStream_t s);
+hipError_t launch_fill_zero_f32(float* out, int64_t ld, int64_t rows, int64_t cols, hipStream_t s);
+
+// GEMM epilogues. C(m, n) = Σ_k A(m, k)·B(k, n), accumulated in fp32.
+enum class Epi : int {
+  kStore = 0,        // C[m, n] = acc                                  (C in the input dtype)
+  kGelu = 1,         // C[m, n] = acc (Hpre); C2[m, n] = gelu(acc) (H)
+  kSwiglu = 2,       // N = f_s pairs: C[m, j] = g, C[m, f_s + j] = u, C2[m, j] = silu(g)·u
+  kDGelu = 3,        // C[m, n] = acc · gelu'(aux[m, n])               (aux = Hpre)
+  kDSwiglu = 4,      // C[m, j] = acc·u·σ(g)(1 + g(1 − σ(g))), C[m, f_s + j] = acc·silu(g)
+  kF32 = 5,          // fp32 C: C = acc, or C += acc when accumulate; split-K writes slices
+};
+
+struct GemmArgs {
+  int64_t M, N, K;            // for kSwiglu N is f_s (each column yields a gate/up pair)
+  const void* A; int64_t lda; bool a_kcontig;   // A(m,k) = a_kcontig ? A[m·lda + k] : A[k·lda + m]
+  const void* B; int64_t ldb; bool b_kcontig;   // B(k,n) = b_kcontig ? B[n·ldb + k] : B[k·ldb + n]
+  void* C; int64_t ldc;
+  void* C2; int64_t ldc2;
+  const void* aux; int64_t ldaux;
+  int64_t f_s;                // gate/up offset for kSwiglu / kDSwiglu
+  Epi epi;
+  int accumulate;             // kF32
+  float* ws;                  // kF32 split-K slices [splits][M][N]; null disables split-K
+  int64_t ws_elems;           // capacity of ws in floats
+  bool bf16;                  // operand dtype: bf16 (MFMA path) or fp32 (vector-ALU path)
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* launches_out);
+// Number of float slots a split-K launch of this GEMM would use (0 = no split).
+int64_t gemm_splitk_ws_elems(int64_t M, int64_t N, int64_t K);
+
+struct AttnArgs {
+  const void* qkv; int64_t ld_qkv;   // [T, 3·H·d] = [Q | K | V]
+  void* o; int64_t ld_o;             // [T, H·d]
+  int64_t batch, seq, heads, head_dim;
+  float scale;
+};
+hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s);
+
+}  // namespace domino

@@ -1,0 +1,155 @@
+"""MLP shard forward / backward on the GPU against the fp64 oracle, at sizes that span
+several tiles with ragged tails, every Domino split, and the edge cases."""
+import pytest
+
+import synth
+from gpu_util import D, np, torch, dev, f64, check, poison, sync, oracle, BF16_TOL, F32_TOL
+from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = [(1, 1), (2, 1), (1, 2), (2, 2)]
+
+
+def small_workload(act, dtype="bf16", batch=2, seq=200, hidden=272, ffn_shard=136, P=3, split=(1, 1), seed=11):
+    return synth.MlpWorkload("small", batch=batch, seq=seq, hidden=hidden, ffn_shard=ffn_shard, act=act, dtype=dtype,
+                             row_chunks=split[0], col_chunks=split[1], n_partials=P, backward=True, seed=seed)
+
+
+def make_group(w, inputs):
+    return MlpGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn_shard=w.ffn_shard, act=w.act, dtype=w.dtype,
+                    row_chunks=w.row_chunks, col_chunks=w.col_chunks, n_partials=w.n_partials, X=inputs["X"],
+                    A=inputs["A"], B=inputs["B"], dY=inputs["dY"], device=dev())
+
+
+def run_fwd_bwd(w, streams=True, inputs=None):
+    inputs = inputs or synth.mlp_inputs(w)
+    g = make_group(w, inputs)
+    poison(g.Y, *g.Hpre.values(), *g.H.values(), *g.Y_own.values())
+    g.peer_forward()
+    comm = torch.cuda.Stream() if streams else None
+    g.forward(comm=comm)
+    g.peer_backward()
+    poison(g.dX, *g.dHpre.values(), *g.dX_own.values(), g.dA, g.dB)
+    g.backward(comm=comm)
+    sync()
+    return g, inputs
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+@pytest.mark.parametrize("split", SPLITS)
+def test_mlp_forward_backward_small(act, split):
+    w = small_workload(act, split=split)
+    print(f"mlp small act={act} split={split} T={w.tokens} h={w.hidden} f_s={w.ffn_shard} P={w.n_partials}",
+          flush=True)
+    g, inp = run_fwd_bwd(w)
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    P = w.n_partials
+    # Reduced forward output against the chunked oracle (= the unsharded layer).
+    Y_ref = oracle.domino_mlp_forward(X, A, B, act, P, w.batch, w.seq, *split)
+    check("Y", f64(g.Y), Y_ref, BF16_TOL)
+    A0, B0 = oracle.mlp_shard_weights(A, B, act, P, 0)
+    Hpre_ref, H_ref, Y0_ref = oracle.mlp_shard_forward(X, A0, B0, act)
+    check("Hpre", f64(g.Hpre[0]), Hpre_ref, BF16_TOL)
+    check("H", f64(g.H[0]), H_ref, BF16_TOL)
+    check("Y_own", f64(g.Y_own[0]), Y0_ref, BF16_TOL)
+    dX_ref, dA_ref, dB_ref = oracle.domino_mlp_backward(X, A, B, dY, act, P, 0, w.batch, w.seq, *split)
+    dHpre_ref = oracle.mlp_shard_backward(X, A0, B0, dY, act)[0]
+    check("dHpre", f64(g.dHpre[0]), dHpre_ref, BF16_TOL)
+    check("dX", f64(g.dX), dX_ref, BF16_TOL)
+    check("dA_s", f64(g.dA), dA_ref, BF16_TOL)
+    check("dB_s", f64(g.dB), dB_ref, BF16_TOL)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_chunked_results_bitwise_equal_unsplit(act):
+    """Domino chunks change no dot product, so every output is bit-identical to the
+    unsplit call (row, column and 2D splits; with and without the second stream)."""
+    base = None
+    inputs = synth.mlp_inputs(small_workload(act))
+    for split in SPLITS:
+        for streams in (False, True):
+            g, _ = run_fwd_bwd(small_workload(act, split=split), streams=streams, inputs=inputs)
+            outs = [g.Y, g.Hpre[0], g.H[0], g.dX, g.dHpre[0], g.dA, g.dB]
+            outs = [o.detach().clone() for o in outs]
+            if base is None:
+                base = outs
+            else:
+                for name, a, b in zip(["Y", "Hpre", "H", "dX", "dHpre", "dA", "dB"], outs, base):
+                    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                        (split, streams, name)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_fp32_layer_small(act):
+    w = small_workload(act, dtype="f32", batch=2, seq=40, hidden=68, ffn_shard=36, P=2, split=(2, 1))
+    g, inp = run_fwd_bwd(w)
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    check("Y", f64(g.Y), oracle.domino_mlp_forward(X, A, B, act, 2, w.batch, w.seq, 2, 1), F32_TOL)
+    dX_ref, dA_ref, dB_ref = oracle.domino_mlp_backward(X, A, B, dY, act, 2, 0, w.batch, w.seq, 2, 1)
+    check("dX", f64(g.dX), dX_ref, F32_TOL)
+    check("dA_s", f64(g.dA), dA_ref, F32_TOL)
+    check("dB_s", f64(g.dB), dB_ref, F32_TOL)
+
+
+def test_tiny_fp32_workload_full():
+    """The tiny fp32 layer (X [2×16, 64], A [64, 256], B [256, 64], tanh-GeLU, TP = 2,
+    row split ×2, forward), compared in full."""
+    w = synth.WORKLOADS["tiny_fp32_mlp_tp2_row"]
+    inp = synth.mlp_inputs(w)
+    g = MlpGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn_shard=w.ffn_shard, act=w.act, dtype=w.dtype,
+                 row_chunks=w.row_chunks, col_chunks=w.col_chunks, n_partials=w.n_partials, X=inp["X"], A=inp["A"],
+                 B=inp["B"], device=dev())
+    poison(g.Y, *g.Y_own.values())
+    g.peer_forward()
+    g.forward(comm=torch.cuda.Stream())
+    sync()
+    X, A, B = (oracle.to_f64(inp[k]) for k in ("X", "A", "B"))
+    ref = oracle.domino_mlp_forward(X, A, B, w.act, w.n_partials, w.batch, w.seq, w.row_chunks, w.col_chunks)
+    check("Y", f64(g.Y), ref, F32_TOL)
+    check("Y (unsharded)", f64(g.Y), oracle.mlp_forward_unsharded(X, A, B, w.act), F32_TOL)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_accumulate_adds_to_weight_gradients(act):
+    w = small_workload(act, P=1)
+    inp = synth.mlp_inputs(w)
+    g = make_group(w, inp)
+    g.forward()
+    g.backward()
+    dA1, dB1 = g.dA.clone(), g.dB.clone()
+    g.backward(accumulate=1)
+    sync()
+    check("dA accumulated", f64(g.dA), 2 * f64(dA1), 1e-6)
+    check("dB accumulated", f64(g.dB), 2 * f64(dB1), 1e-6)
+
+
+def test_edge_single_token_rows_and_minimal_widths():
+    # One sequence of one token, hidden and f_s at their minimum (8): everything ragged.
+    w = small_workload("swiglu", batch=1, seq=1, hidden=8, ffn_shard=8, P=2)
+    g, inp = run_fwd_bwd(w)
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    check("Y", f64(g.Y), oracle.mlp_forward_unsharded(X, A, B, "swiglu"), BF16_TOL)
+    check("dX", f64(g.dX), oracle.mlp_backward_unsharded(X, A, B, dY, "swiglu"), BF16_TOL)
+
+
+def test_edge_empty_batch_is_noop():
+    d = dev()
+    desc = D.MlpDesc(batch=0, seq=128, hidden=64, ffn_shard=64, act=0, dtype=1, row_chunks=1, col_chunks=1,
+                     n_partials=2, no_join=0)
+    D.domino_block_fwd(desc, None, None, None, None, None, None, None, None, None, torch.cuda.Stream())
+    sync()
+
+
+def test_edge_n_partials_one_in_place():
+    # P = 1 and Y = NULL: Y_own is the layer's output; no reduction runs.
+    w = small_workload("gelu_tanh", P=1)
+    inp = synth.mlp_inputs(w)
+    g = make_group(w, inp)
+    d = g.desc()
+    D.domino_block_fwd(d, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, None,
+                       torch.cuda.Stream())
+    sync()
+    X, A, B = (oracle.to_f64(inp[k]) for k in ("X", "A", "B"))
+    check("Y_own", f64(g.Y_own[0]), oracle.mlp_forward_unsharded(X, A, B, "gelu_tanh"), BF16_TOL)
