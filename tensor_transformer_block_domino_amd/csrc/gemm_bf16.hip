@@ -65,21 +65,40 @@ __device__ __forceinline__ int64_t map_row(const RowMap& m, int r) {
   }
 }
 
+// Global loads go through buffer instructions: a lane whose element is outside the
+// matrix gets byte offset kOOB, which the buffer range check turns into zeros without a
+// branch. Each k-step rebuilds the resource from a base pointer so offsets stay small.
+constexpr int32_t kOOB = int32_t(0x80000000u);
+constexpr int32_t kRangeBytes = 0x7fffffff;
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, kRangeBytes, kRsrcWord3);
+}
+
 // Operand contiguous along k: element (row, k) at p[row·ld + k].
 template <int R, bool kSw>
 struct TileKContig {
   static constexpr int kPer = R / 32;  // 16-byte chunks per thread
   u32x4_t v[kPer];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t ld, const RowMap& rm, int64_t k0,
-                                       int64_t K, int tid) {
-    const int c = tid & 7;
-    const int64_t kk = k0 + c * 8;
+  const uint16_t* base;
+  int32_t off[kPer];
+  int c8;
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, const RowMap& rm, int tid) {
+    static_assert(!kSw, "the SwiGLU column map applies to the m/n-contiguous forward operand only");
+    c8 = (tid & 7) * 8;
+    base = p + rm.base * ld;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int r = (tid >> 3) + 32 * j;
-      const int64_t g = map_row<kSw, R>(rm, r);
-      v[j] = (g >= 0 && kk < K) ? *reinterpret_cast<const u32x4_t*>(p + g * ld + kk) : u32x4_t{0u, 0u, 0u, 0u};
+      off[j] = map_row<false, R>(rm, r) >= 0 ? int32_t((r * ld + c8) * 2) : kOOB;
     }
+  }
+  __device__ __forceinline__ void load(int64_t k0, int64_t K) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
+    const bool kok = k0 + c8 < K;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, kok ? off[j] : kOOB, 0, 0);
   }
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
     const int c = tid & 7;
@@ -89,6 +108,8 @@ struct TileKContig {
       *reinterpret_cast<u32x4_t*>(lds + lds_off(r, c)) = v[j];
     }
   }
+  static constexpr int kStores = kPer;
+  static constexpr int kLoads = kPer;
 };
 
 // Operand contiguous along m/n: element (row, k) at p[k·ld + row]. Thread t reads
@@ -97,26 +118,34 @@ template <int R, bool kSw>
 struct TileMNContig {
   static constexpr int kW = R / 32;  // tile rows per thread: 8 (R = 256) or 4 (R = 128)
   uint32_t v[8][kW / 2];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t ld, const RowMap& rm, int64_t k0,
-                                       int64_t K, int tid) {
-    const int b = tid & 31, kb = tid >> 5;
-    const int64_t g = map_row<kSw, R>(rm, b * kW);
+  const uint16_t* base;
+  int64_t ld;
+  int32_t moff;
+  int kb;
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld_, const RowMap& rm, int tid) {
+    ld = ld_;
+    kb = tid >> 5;
+    base = p + rm.base;
+    const int64_t g = map_row<kSw, R>(rm, (tid & 31) * kW);
+    moff = g >= 0 ? int32_t((g - rm.base) * 2) : kOOB;
+  }
+  __device__ __forceinline__ void load(int64_t k0, int64_t K) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const int64_t krow = k0 + kb * 8 + kk;
-      const bool ok = g >= 0 && krow < K;
-      const uint16_t* src = p + krow * ld + g;
+      const int kr = kb * 8 + kk;
+      const int32_t o = (moff != kOOB && k0 + kr < K) ? moff + int32_t(kr * ld * 2) : kOOB;
       if constexpr (kW == 8) {
-        const u32x4_t t = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
         v[kk][0] = t.x; v[kk][1] = t.y; v[kk][2] = t.z; v[kk][3] = t.w;
       } else {
-        const u32x2_t t = ok ? *reinterpret_cast<const u32x2_t*>(src) : u32x2_t{0u, 0u};
+        const u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
         v[kk][0] = t.x; v[kk][1] = t.y;
       }
     }
   }
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int b = tid & 31, kb = tid >> 5;
+    const int b = tid & 31;
 #pragma unroll
     for (int e = 0; e < kW; ++e) {
       uint32_t d[4];
@@ -129,6 +158,8 @@ struct TileMNContig {
       *reinterpret_cast<u32x4_t*>(lds + lds_off(r, kb)) = u32x4_t{d[0], d[1], d[2], d[3]};
     }
   }
+  static constexpr int kStores = kW;
+  static constexpr int kLoads = 8;
 };
 
 template <int R, bool kKContig, bool kSw>
@@ -148,6 +179,17 @@ struct KParams {
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
   *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// Interleave hints for the scheduler: `n` groups of {one instruction of class `mask`,
+// then `mfma` MFMAs}. Masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write.
+template <int kMask, int kN, int kMfma>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMask, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  }
 }
 
 template <int BM, int BN, bool kAK, bool kBKc, Epi kEpi>
@@ -190,49 +232,75 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(KParams p) {
 
   Tile<BM, kAK, false> ta;
   Tile<BN, kBKc, kSw> tb;
+  ta.init(p.A, p.lda, rmA, tid);
+  tb.init(p.B, p.ldb, rmB, tid);
+
+  // MFMA fragments of one 32-wide k sub-step, double-buffered in registers: the LDS
+  // reads of sub-step s+1 are in flight while sub-step s feeds the matrix cores.
+  struct Frag {
+    u32x4_t a[TM], b[TN];
+  };
+  Frag f0, f1;
+  const int frow_a = wm * WM + (lane & 15), frow_b = wn * WN + (lane & 15);
+  auto read_frags = [&](Frag& f, const uint16_t* sA, const uint16_t* sB, int s) {
+    const int chunk = s * 4 + (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4_t*>(sB + lds_off(frow_b + j * 16, chunk));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4_t*>(sA + lds_off(frow_a + i * 16, chunk));
+  };
+  auto mma = [&](const Frag& f, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                           __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
+  };
+
   uint16_t* const sA0 = smem;
   uint16_t* const sB0 = smem + BM * kKStep;
   uint16_t* const sA1 = smem + (BM + BN) * kKStep;
   uint16_t* const sB1 = sA1 + BM * kKStep;
 
   if (kt_begin < kt_end) {
-    ta.load(p.A, p.lda, rmA, int64_t(kt_begin) * kKStep, p.K, tid);
-    tb.load(p.B, p.ldb, rmB, int64_t(kt_begin) * kKStep, p.K, tid);
+    ta.load(int64_t(kt_begin) * kKStep, p.K);
+    tb.load(int64_t(kt_begin) * kKStep, p.K);
     ta.store(sA0, tid);
     tb.store(sB0, tid);
     __syncthreads();
+    ta.load(int64_t(kt_begin + 1) * kKStep, p.K);
+    tb.load(int64_t(kt_begin + 1) * kKStep, p.K);
+    read_frags(f0, sA0, sB0, 0);
   }
+  // One k-step per iteration, a single basic block: loads past the end of the k range
+  // read zeros (or another split's data) and their LDS stores are never read.
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const bool odd = (kt - kt_begin) & 1;
-    const uint16_t* sA = odd ? sA1 : sA0;
-    const uint16_t* sB = odd ? sB1 : sB0;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) {
-      ta.load(p.A, p.lda, rmA, int64_t(kt + 1) * kKStep, p.K, tid);
-      tb.load(p.B, p.ldb, rmB, int64_t(kt + 1) * kKStep, p.K, tid);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int chunk = s * 4 + (lane >> 4);
-      u32x4_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(sA + lds_off(wm * WM + i * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4_t*>(sB + lds_off(wn * WN + j * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[j]),
-                                                             __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
-    }
-    if (has_next) {
-      ta.store(odd ? sA0 : sA1, tid);
-      tb.store(odd ? sB0 : sB1, tid);
-    }
+    const uint16_t* cA = odd ? sA1 : sA0;
+    const uint16_t* cB = odd ? sB1 : sB0;
+    uint16_t* nA = odd ? sA0 : sA1;
+    uint16_t* nB = odd ? sB0 : sB1;
+    // Sub-step 0 on the matrix cores; sub-step 1's fragments come in from LDS.
+    read_frags(f1, cA, cB, 1);
+    mma(f0, 0, TM);
+    interleave<0x100, TM + TN, (TM * TN) / (TM + TN)>();
+    __builtin_amdgcn_sched_barrier(0);
+    // First half of sub-step 1; the next k-step's tile goes from registers to LDS.
+    ta.store(nA, tid);
+    tb.store(nB, tid);
+    mma(f1, 0, TM / 2);
+    interleave<0x200, decltype(ta)::kStores + decltype(tb)::kStores,
+               (TM / 2 * TN) / (decltype(ta)::kStores + decltype(tb)::kStores)>();
     __syncthreads();
+    // Second half of sub-step 1; the k-step after next is requested from memory and the
+    // next k-step's first fragments are read.
+    ta.load(int64_t(kt + 2) * kKStep, p.K);
+    tb.load(int64_t(kt + 2) * kKStep, p.K);
+    read_frags(f0, nA, nB, 0);
+    mma(f1, TM / 2, TM);
+    interleave<0x100, TM + TN, (TM / 2 * TN) / (TM + TN) ? (TM / 2 * TN) / (TM + TN) : 1>();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue: lane holds C[m][n .. n+3] of each sub-tile.
@@ -304,9 +372,7 @@ struct TileCfg {
 
 template <bool kAK, bool kBKc, Epi kEpi>
 hipError_t dispatch_tile(const TileCfg& tc, const KParams& kp, int blocks, hipStream_t s) {
-  if (tc.bm == 256 && tc.bn == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
-  else if (tc.bm == 256 && tc.bn == 128)
+  if (tc.bm == 256 && tc.bn == 128)
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
   else if (tc.bm == 128 && tc.bn == 256)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 256, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
@@ -318,11 +384,11 @@ hipError_t dispatch_tile(const TileCfg& tc, const KParams& kp, int blocks, hipSt
 // Choose the tile that minimises (waves of workgroups) × (work per workgroup ÷ its
 // relative efficiency) on 256 CUs, one workgroup per CU.
 TileCfg choose_tile(int64_t M, int64_t Neff, bool swiglu) {
-  const TileCfg cands[4] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
-  const double eff[4] = {1.0, 0.88, 0.88, 0.72};
+  const TileCfg cands[3] = {{256, 128}, {128, 256}, {128, 128}};
+  const double eff[3] = {1.0, 1.0, 0.8};
   double best = 1e300;
   TileCfg bt = cands[0];
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < 3; ++c) {
     const int64_t bn_cols = swiglu ? cands[c].bn / 2 : cands[c].bn;
     const int64_t tiles = ((M + cands[c].bm - 1) / cands[c].bm) * ((Neff + bn_cols - 1) / bn_cols);
     const int64_t waves = (tiles + 255) / 256;

@@ -29,8 +29,8 @@ def run_fwd_bwd(w, streams=True, inputs=None):
     g.peer_forward()
     comm = torch.cuda.Stream() if streams else None
     g.forward(comm=comm)
-    g.peer_backward()
     poison(g.dX, *g.dHpre.values(), *g.dX_own.values(), g.dA, g.dB)
+    g.peer_backward()
     g.backward(comm=comm)
     sync()
     return g, inputs
