@@ -225,6 +225,14 @@ domino_status check_mlp_desc(const domino_mlp_desc* d) {
 
 bool needs_reduce(int n_partials, const void* own, const void* out) { return n_partials > 1 || (out && out != own); }
 
+// The fixed-order sum of a split-K product's fp32 slices into its output.
+hipError_t splitk_finish(const GemmArgs& g, int splits, hipStream_t s) {
+  if (splits <= 1) return hipSuccess;
+  return timed(DOMINO_K_AUX, s, [&] {
+    return launch_splitk_sum(static_cast<float*>(g.C), g.ldc, g.ws, splits, g.M, g.N, g.accumulate, s);
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,7 +428,9 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
     wb.accumulate = accumulate;
     wb.ws = ws; wb.ws_elems = ws_elems;
     wb.bf16 = bf;
-    if (hip_ok(timed(DOMINO_K_WGRAD_B, sc.cs, [&] { return launch_gemm(wb, sc.cs, nullptr); }), &msg, "wgrad B"))
+    int splits = 1;
+    if (hip_ok(timed(DOMINO_K_WGRAD_B, sc.cs, [&] { return launch_gemm(wb, sc.cs, &splits); }), &msg, "wgrad B") ||
+        hip_ok(splitk_finish(wb, splits, sc.cs), &msg, "wgrad B split-K sum"))
       return fail(DOMINO_ERR_HIP, msg);
     GemmArgs wa{};
     wa.M = h; wa.N = n1; wa.K = T;
@@ -431,7 +441,8 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
     wa.accumulate = accumulate;
     wa.ws = ws; wa.ws_elems = ws_elems;
     wa.bf16 = bf;
-    if (hip_ok(timed(DOMINO_K_WGRAD_A, sc.cs, [&] { return launch_gemm(wa, sc.cs, nullptr); }), &msg, "wgrad A"))
+    if (hip_ok(timed(DOMINO_K_WGRAD_A, sc.cs, [&] { return launch_gemm(wa, sc.cs, &splits); }), &msg, "wgrad A") ||
+        hip_ok(splitk_finish(wa, splits, sc.cs), &msg, "wgrad A split-K sum"))
       return fail(DOMINO_ERR_HIP, msg);
   }
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);

@@ -7,7 +7,7 @@
 
 namespace domino {
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* launches_out);
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* splits_out);
 
 namespace {
 
@@ -181,11 +181,10 @@ hipError_t launch_fill_zero_f32(float* out, int64_t ld, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* launches_out) {
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* splits_out) {
+  if (splits_out) *splits_out = 1;
   int launches = 0;
-  const hipError_t e = g.bf16 ? launch_gemm_bf16(g, s, &launches) : launch_gemm_f32_path(g, s, &launches);
-  if (launches_out) *launches_out = launches;
-  return e;
+  return g.bf16 ? launch_gemm_bf16(g, s, splits_out) : launch_gemm_f32_path(g, s, &launches);
 }
 
 }  // namespace domino

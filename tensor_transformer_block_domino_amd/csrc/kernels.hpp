@@ -47,7 +47,10 @@ struct GemmArgs {
   int64_t ws_elems;           // capacity of ws in floats
   bool bf16;                  // operand dtype: bf16 (MFMA path) or fp32 (vector-ALU path)
 };
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* launches_out);
+// Launches the product. With split-K (weight gradients with a workspace), the kernel
+// writes fp32 slices to g.ws and *splits_out > 1: the caller then launches
+// launch_splitk_sum(g.C, g.ldc, g.ws, *splits_out, g.M, g.N, g.accumulate).
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* splits_out);
 // Number of float slots a split-K launch of this GEMM would use (0 = no split).
 int64_t gemm_splitk_ws_elems(int64_t M, int64_t N, int64_t K);
 
