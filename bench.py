@@ -36,7 +36,29 @@ def parse():
     ap.add_argument("--workload", default="gpt3_2p7b_mlp_tp8_row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (for HBM counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wgrad_gemm_gpt3_2p7b_mlp.txt")
+GEMM_SOURCE = os.path.join(ROOT, "tensor_transformer_block_domino_amd", "csrc", "gemm_bf16.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the weight-gradient GEMM from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None if the kernel
+    source changed since the counters were taken."""
+    import hashlib
+
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256", "").strip() != src:
+            return None
+        return float(kv["calibrated_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def mlp_flops(w):
@@ -114,6 +136,13 @@ def main():
     from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
 
     D.load()
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     assert isinstance(w, synth.MlpWorkload) and w.dtype == "bf16"
     dev = torch.device("cuda:0")
@@ -228,7 +257,8 @@ def main():
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic() if args.workload == "gpt3_2p7b_mlp_tp8_row" else None,
                      "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n_dom,
                      "flops_per_launch": flops_dom / max(1, n_dom)},
     }

@@ -114,10 +114,10 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
 /*
  * domino_block_fwd — MLP shard forward in Domino chunks ("按行切分输入 X", "按列切分权重 B",
  * "2D 切分"; primer §3.1 for the column→row pairing).
- * For each row chunk R_i: Hpre[R_i] = X[R_i]·A_s and H[R_i] = act(Hpre[R_i]) (GEMM with a
- * fused activation epilogue); then for each column chunk C_j: Y_own[R_i, C_j] =
+ * Hpre = X·A_s and H = act(Hpre) (one GEMM over all rows with a fused activation
+ * epilogue; it feeds no reduction); then for each chunk (R_i, C_j): Y_own[R_i, C_j] =
  * H[R_i]·B_s[:, C_j], and the chunk's reduction Y[R_i, C_j] = Y_own + Σ peer_Y runs on
- * `comm` while the next chunk's GEMMs run on `compute`.
+ * `comm` while the next chunk's GEMM runs on `compute`.
  *   X [T, hidden]; A_s [hidden, n1]; B_s [ffn_shard, hidden]            (inputs)
  *   Hpre [T, n1], H [T, ffn_shard]     saved for the backward           (outputs)
  *   Y_own [T, hidden]                  this rank's partial              (output)
@@ -135,9 +135,9 @@ size_t domino_block_bwd_workspace_size(const domino_mlp_desc* desc);
 
 /*
  * domino_block_bwd — MLP shard backward ("反向：扩展与权重梯度计算的重叠"; overlap page §1).
- * Per dX chunk (row chunks; for a column-only split, column chunks of dX, the mirror of
- * the forward's column split; the 2D split reduces dX by row chunks):
- *   dHpre = act'(Hpre) ⊙ (dY·B_sᵀ)      (GEMM with a fused activation-gradient epilogue)
+ *   dHpre = act'(Hpre) ⊙ (dY·B_sᵀ)      (one GEMM over all rows, activation gradient fused)
+ * then per dX chunk (row chunks; for a column-only split, column chunks of dX, the mirror
+ * of the forward's column split; the 2D split reduces dX by row chunks):
  *   dX_own[chunk] = dHpre·A_s[chunk]ᵀ   (this rank's partial input gradient)
  *   dX[chunk] = dX_own + Σ peer_dX      (reduction on `comm`)
  * then the independent weight gradients, which hide the last reduction:
@@ -161,8 +161,8 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
  * domino_attn_block_fwd — attention shard forward by row chunks (whole sequences)
  * ("TP 的数据依赖…": A = multi-head attention on the rank's heads, B = output projection;
  * "前向：多个计算片段轮转重叠 AllReduce": AllReduce(attn0) overlaps μ-batch 1's attention).
- * Per chunk: QKV = X·A_qkv_s; O = causal softmax(Q·Kᵀ·scale)·V per (sequence, head);
- * Y_own = O·B_o_s; Y = Y_own + Σ peer_Y on `comm`.
+ * QKV = X·A_qkv_s and O = causal softmax(Q·Kᵀ·scale)·V per (sequence, head), each one
+ * launch over all sequences; then per chunk: Y_own = O·B_o_s; Y = Y_own + Σ peer_Y on `comm`.
  *   X [T, hidden]; A_qkv_s [hidden, 3·heads·head_dim] = [Q | K | V] blocks, head j at
  *   columns j·head_dim within each block; B_o_s [heads·head_dim, hidden]   (inputs)
  *   QKV [T, 3·heads·head_dim], O [T, heads·head_dim]   saved activations   (outputs)

@@ -5,6 +5,10 @@
 //  * the layer's input rows are split along batch ("按行切分输入 X"), the second weight
 //    along its last dimension ("按列切分权重 B"), or both ("2D 切分"); each chunk's output is
 //    independent, so its reduction can start as soon as that chunk's products end;
+//  * the layer's first product (and, for attention, the attention itself) feeds no
+//    reduction, so it is launched once over all rows; only the product whose output is
+//    reduced is launched per chunk. Row-splitting makes tensors narrower and hurts kernel
+//    efficiency ("按行切分输入 X"), and here that cost buys nothing;
 //  * the reductions are issued asynchronously on a second stream and waited only by the
 //    consumer ("异步 AllReduce 的发起", "μ-batch 流水"): here `compute` records an event after
 //    a chunk's last product, `comm` waits on it and reduces, and `compute` finally waits
@@ -52,11 +56,14 @@ hipError_t events_for_current_device(EventSet** out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   EventSet& es = t_events[dev];
   if (!es.ready) {
+    // Both streams run on this device, so a device-scope release orders the chunk's
+    // products before its reduction; the default system-scope fence costs several
+    // microseconds of idle compute stream at every chunk boundary.
     for (int i = 0; i < kMaxChunks; ++i) {
-      e = hipEventCreateWithFlags(&es.done[i], hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&es.done[i], hipEventDisableTiming | hipEventReleaseToDevice);
       if (e != hipSuccess) return e;
     }
-    e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming | hipEventReleaseToDevice);
     if (e != hipSuccess) return e;
     es.ready = true;
   }
@@ -85,7 +92,7 @@ hipEvent_t timing_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventReleaseToDevice) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -312,21 +319,24 @@ domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const vo
   const size_t es = esize(d->dtype);
   const int64_t Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
   std::string msg;
+  // The first product (column-parallel, activation fused) feeds no reduction, so it runs
+  // once over all rows: chunking it would only narrow the GEMM. The second product is
+  // launched per Domino chunk, and each chunk's reduction starts as soon as it ends.
+  if (f > 0) {
+    GemmArgs g1{};
+    g1.M = T; g1.N = f; g1.K = h;
+    g1.A = X; g1.lda = h; g1.a_kcontig = true;
+    g1.B = A_s; g1.ldb = n1; g1.b_kcontig = false;
+    g1.C = Hpre; g1.ldc = n1;
+    g1.C2 = H; g1.ldc2 = f;
+    g1.f_s = f;
+    g1.epi = sw ? Epi::kSwiglu : Epi::kGelu;
+    g1.bf16 = bf;
+    if (hip_ok(timed(DOMINO_K_FWD_GEMM1, sc.cs, [&] { return launch_gemm(g1, sc.cs, nullptr); }), &msg, "GEMM1"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
   for (int i = 0; i < d->row_chunks; ++i) {
     const int64_t r0 = i * Tc;
-    if (f > 0) {
-      GemmArgs g1{};
-      g1.M = Tc; g1.N = f; g1.K = h;
-      g1.A = static_cast<const char*>(X) + r0 * h * es; g1.lda = h; g1.a_kcontig = true;
-      g1.B = A_s; g1.ldb = n1; g1.b_kcontig = false;
-      g1.C = static_cast<char*>(Hpre) + r0 * n1 * es; g1.ldc = n1;
-      g1.C2 = static_cast<char*>(H) + r0 * f * es; g1.ldc2 = f;
-      g1.f_s = f;
-      g1.epi = sw ? Epi::kSwiglu : Epi::kGelu;
-      g1.bf16 = bf;
-      if (hip_ok(timed(DOMINO_K_FWD_GEMM1, sc.cs, [&] { return launch_gemm(g1, sc.cs, nullptr); }), &msg, "GEMM1"))
-        return fail(DOMINO_ERR_HIP, msg);
-    }
     for (int j = 0; j < d->col_chunks; ++j) {
       const int64_t c0 = j * hc;
       GemmArgs g2{};
@@ -385,21 +395,24 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
   const int rch = d->row_chunks, cch = d->row_chunks > 1 ? 1 : d->col_chunks;
   const int64_t Tc = (d->batch / rch) * d->seq, hc = h / cch;
   std::string msg;
+  // dgrad of the second layer (activation gradient fused) feeds no reduction: one launch
+  // over all rows. dgrad of the first layer is launched per dX chunk, each followed by
+  // its reduction.
+  if (tok && ffn) {
+    GemmArgs gb{};
+    gb.M = T; gb.N = f; gb.K = h;
+    gb.A = dY; gb.lda = h; gb.a_kcontig = true;
+    gb.B = B_s; gb.ldb = h; gb.b_kcontig = true;          // B(k, n) = B_s[n][k]
+    gb.C = dHpre; gb.ldc = n1;
+    gb.aux = Hpre; gb.ldaux = n1;
+    gb.f_s = f;
+    gb.epi = sw ? Epi::kDSwiglu : Epi::kDGelu;
+    gb.bf16 = bf;
+    if (hip_ok(timed(DOMINO_K_DGRAD_B, sc.cs, [&] { return launch_gemm(gb, sc.cs, nullptr); }), &msg, "dgrad B"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
   for (int i = 0; i < rch && tok; ++i) {
     const int64_t r0 = i * Tc;
-    if (ffn) {
-      GemmArgs gb{};
-      gb.M = Tc; gb.N = f; gb.K = h;
-      gb.A = static_cast<const char*>(dY) + r0 * h * es; gb.lda = h; gb.a_kcontig = true;
-      gb.B = B_s; gb.ldb = h; gb.b_kcontig = true;          // B(k, n) = B_s[n][k]
-      gb.C = static_cast<char*>(dHpre) + r0 * n1 * es; gb.ldc = n1;
-      gb.aux = static_cast<const char*>(Hpre) + r0 * n1 * es; gb.ldaux = n1;
-      gb.f_s = f;
-      gb.epi = sw ? Epi::kDSwiglu : Epi::kDGelu;
-      gb.bf16 = bf;
-      if (hip_ok(timed(DOMINO_K_DGRAD_B, sc.cs, [&] { return launch_gemm(gb, sc.cs, nullptr); }), &msg, "dgrad B"))
-        return fail(DOMINO_ERR_HIP, msg);
-    }
     for (int j = 0; j < cch; ++j) {
       const int64_t c0 = j * hc;
       GemmArgs ga{};
@@ -482,34 +495,35 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
   const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
   const int64_t bc = d->batch / d->row_chunks, Tc = bc * d->seq;
   std::string msg;
-  for (int i = 0; i < d->row_chunks; ++i) {
-    const int64_t r0 = i * Tc;
-    char* qkv = static_cast<char*>(QKV) + r0 * 3 * hd * 2;
-    char* o = static_cast<char*>(O) + r0 * hd * 2;
+  // QKV projection and attention feed no reduction: one launch each over all sequences.
+  // The output projection runs per chunk (whole sequences) and each chunk's reduction
+  // starts as soon as it ends.
+  if (heads) {
     GemmArgs gq{};
-    gq.M = Tc; gq.N = 3 * hd; gq.K = h;
-    gq.A = static_cast<const char*>(X) + r0 * h * 2; gq.lda = h; gq.a_kcontig = true;
+    gq.M = T; gq.N = 3 * hd; gq.K = h;
+    gq.A = X; gq.lda = h; gq.a_kcontig = true;
     gq.B = A_qkv_s; gq.ldb = 3 * hd; gq.b_kcontig = false;
-    gq.C = qkv; gq.ldc = 3 * hd;
+    gq.C = QKV; gq.ldc = 3 * hd;
     gq.epi = Epi::kStore;
     gq.bf16 = true;
+    AttnArgs aa{};
+    aa.qkv = QKV; aa.ld_qkv = 3 * hd;
+    aa.o = O; aa.ld_o = hd;
+    aa.batch = d->batch; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
+    aa.scale = scale;
+    if (hip_ok(timed(DOMINO_K_QKV, sc.cs, [&] { return launch_gemm(gq, sc.cs, nullptr); }), &msg, "QKV GEMM") ||
+        hip_ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), &msg, "attention"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  for (int i = 0; i < d->row_chunks; ++i) {
+    const int64_t r0 = i * Tc;
     GemmArgs go{};
     go.M = Tc; go.N = h; go.K = hd;
-    go.A = o; go.lda = hd; go.a_kcontig = true;
+    go.A = static_cast<const char*>(O) + r0 * hd * 2; go.lda = hd; go.a_kcontig = true;
     go.B = B_o_s; go.ldb = h; go.b_kcontig = false;
     go.C = static_cast<char*>(Y_own) + r0 * h * 2; go.ldc = h;
     go.epi = Epi::kStore;
     go.bf16 = true;
-    AttnArgs aa{};
-    aa.qkv = qkv; aa.ld_qkv = 3 * hd;
-    aa.o = o; aa.ld_o = hd;
-    aa.batch = bc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
-    aa.scale = scale;
-    if (heads) {
-      if (hip_ok(timed(DOMINO_K_QKV, sc.cs, [&] { return launch_gemm(gq, sc.cs, nullptr); }), &msg, "QKV GEMM") ||
-          hip_ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), &msg, "attention"))
-        return fail(DOMINO_ERR_HIP, msg);
-    }
     if (hip_ok(timed(DOMINO_K_OUTPROJ, sc.cs, [&] { return launch_gemm(go, sc.cs, nullptr); }), &msg, "out-projection"))
       return fail(DOMINO_ERR_HIP, msg);
     if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, r0 * h, Tc, h, DOMINO_BF16), &msg,
