@@ -15,7 +15,8 @@
 //    buffer loads that write LDS directly (no staging registers), NS−1 stages ahead of
 //    the one being consumed; one barrier per stage.
 //  * Within a stage, k advances 16 at a time; the fragments of sub-step s+1 are read
-//    from LDS while sub-step s runs on the matrix cores.
+//    from LDS while sub-step s runs on the matrix cores, one read between consecutive
+//    MFMAs (MFMA issue blocks the wave, so the reads must not form a run).
 //  * An operand contiguous along k is staged [row][k] with an XOR chunk swizzle, and
 //    each MFMA fragment (8 consecutive k of one row) is one 16-byte LDS read. An
 //    operand contiguous along m (or n) — the [in, out] weights of the forward and both
@@ -344,10 +345,24 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           slot = slot + 1 == NS ? 0 : slot + 1;
           read_frags(nxt, slot, 0);
         }
-        // Keep the reads of the next sub-step ahead of this sub-step's MFMAs (the
-        // scheduler would otherwise sink them next to their first use).
-        __builtin_amdgcn_sched_barrier(0);
+        // One LDS read (and, on a stage's last sub-step, one global→LDS issue) between
+        // consecutive MFMAs: MFMA issue blocks the wave, so a run of other instructions
+        // would leave the matrix pipe idle.
         mma(cur);
+        if (s + 1 < NSUB) {
+#pragma unroll
+          for (int q = 0; q < TM * TN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < TM * TN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -392,41 +407,57 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 struct TileCfg {
   int bm, bn, bk, ns, occ;
 };
-// Measured on the MLP and attention shapes: two or three workgroups per CU hide the
-// global-memory latency of each stage far better than one large tile per CU, which
-// outweighs the extra operand traffic of the smaller tile.
+// Three configurations, chosen by shape (measured on the MLP and attention products):
+// the 256×256 tile has the least LDS and L2 traffic per FLOP and wins when there are at
+// least two rounds of such tiles and a long k loop; smaller grids fill the GPU better
+// with 128×128 tiles at two or three workgroups per CU, whose resident workgroups also
+// hide each other's memory latency.
 constexpr TileCfg kTiles[] = {
-    {128, 128, 64, 2, 2},  // 64 KB LDS, 2 workgroups per CU: forward and input-gradient products
-    {128, 128, 32, 3, 3},  // 48 KB LDS, 3 per CU: weight gradients (both operands transposed)
+    {128, 128, 64, 2, 2},  // 64 KB LDS, 2 workgroups per CU
+    {128, 128, 32, 3, 3},  // 48 KB LDS, 3 per CU
+    {256, 256, 64, 2, 1},  // 128 KB LDS, 1 per CU
 };
 
 template <bool kAK, bool kBKc, Epi kEpi>
 hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
   if (ti == 0)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 2, 2, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
-  else
+  else if (ti == 1)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 32, 3, 3, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 64, 2, 1, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
   return hipGetLastError();
 }
 
-int choose_tile(bool a_kcontig, bool b_kcontig) { return (!a_kcontig && !b_kcontig) ? 1 : 0; }
+// Neff: output columns (FFN column pairs for the SwiGLU forward, whose 256-wide tile holds
+// 128 pairs).
+int choose_tile(int64_t M, int64_t Neff, int64_t K, bool a_kcontig, bool b_kcontig, bool swiglu) {
+  const int64_t bn = swiglu ? 128 : 256;
+  const int64_t big_tiles = ((M + 255) / 256) * ((Neff + bn - 1) / bn);
+  if (big_tiles >= 2 * 256 && K >= 1024) return 2;
+  if (a_kcontig && b_kcontig) return 0;  // input gradients (both operands k-contiguous)
+  return 1;
+}
 
 }  // namespace
 
 int64_t gemm_splitk_ws_elems(int64_t M, int64_t N, int64_t K) {
-  // Split-K applies to the weight gradients (both operands transposed).
-  const TileCfg& tc = kTiles[choose_tile(false, false)];
+  // Split-K applies to the weight gradients (both operands transposed) whose output grid
+  // fills less than 3/4 of one round of workgroups: the largest split that still fits in
+  // one round (each split keeping at least 1024 of k).
+  const TileCfg& tc = kTiles[choose_tile(M, N, K, false, false, false)];
   const int64_t slots = 256 * tc.occ;
   const int64_t tiles = ((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
-  if (tiles * 4 >= slots * 3 || K < 2048) return 0;
+  if (tiles * 4 >= slots * 3) return 0;
   int64_t splits = 1;
-  while (tiles * splits * 2 <= slots * 5 / 4 && K / (splits * 2) >= 1024) splits *= 2;
+  for (int64_t sp = 2; sp <= 8; ++sp)
+    if (tiles * sp <= slots && K / sp >= 1024) splits = sp;
   return splits > 1 ? splits * M * N : 0;
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* splits_out) {
   const bool sw = g.epi == Epi::kSwiglu;
-  const int ti = choose_tile(g.a_kcontig, g.b_kcontig);
+  const int ti = choose_tile(g.M, g.N, g.K, g.a_kcontig, g.b_kcontig, sw);
   const TileCfg& tc = kTiles[ti];
   KParams kp{};
   kp.A = static_cast<const uint16_t*>(g.A); kp.lda = g.lda;
