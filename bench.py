@@ -41,24 +41,26 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wgrad_gemm_gpt3_2p7b_mlp.txt")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "traffic_*_gpt3_2p7b_mlp.txt")
 GEMM_SOURCE = os.path.join(ROOT, "tensor_transformer_block_domino_amd", "csrc", "gemm_bf16.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the weight-gradient GEMM from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None if the kernel
-    source changed since the counters were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated against a plain copy), or None if the summary covers another
+    kernel or the kernel source changed since the counters were taken."""
+    import glob
     import hashlib
 
-    try:
-        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
-        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-        if kv.get("kernel_source_sha256", "").strip() != src:
-            return None
-        return float(kv["calibrated_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        try:
+            kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
+            if kv.get("kernel_source_sha256", "").strip() == src and kv.get("kernel", "").strip() == kernel:
+                return float(kv["calibrated_bytes_per_launch"])
+        except (OSError, KeyError, ValueError):
+            continue
+    return None
 
 
 def mlp_flops(w):
@@ -81,16 +83,6 @@ def kernel_flops(w, kind):
         "wgrad_b": 2.0 * T * f * h,
         "wgrad_a": 2.0 * T * h * n1,
     }[kind]
-
-
-# Kernel symbols (one template instantiation each) and the schedule roles that launch them.
-KERNELS = {
-    "gemm_bf16_kernel<128,128,64,2,2,true,false,Epi::kGelu|kSwiglu> (X·A_s + activation)": ["fwd_gemm1"],
-    "gemm_bf16_kernel<128,128,64,2,2,true,false,Epi::kStore> (H·B_s chunk)": ["fwd_gemm2"],
-    "gemm_bf16_kernel<128,128,64,2,2,true,true,Epi::kDGelu|kDSwiglu> (dY·B_sᵀ + activation gradient)": ["dgrad_b"],
-    "gemm_bf16_kernel<128,128,64,2,2,true,true,Epi::kStore> (dHpre·A_sᵀ chunk)": ["dgrad_a"],
-    "gemm_bf16_kernel<128,128,32,3,3,false,false,Epi::kF32> (weight gradients Hᵀ·dY, Xᵀ·dHpre)": ["wgrad_b", "wgrad_a"],
-}
 
 
 def cpu_baseline(w, inp, reps):
@@ -194,10 +186,11 @@ def main():
     for _ in range(args.steps):
         step_domino()
     torch.cuda.synchronize()
-    per = {}
+    per, kernel_of = {}, {}
     for kind in ("reduce", "fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a", "aux"):
         n, tot = D.domino_timing_read(kind)
         per[kind] = (n, tot)
+        kernel_of[kind] = D.domino_timing_kernel(kind)
     # shard_reduce alone: the whole [T, h] output, the 8 partials, on an idle GPU.
     D.domino_timing_enable(True)
     parts = [g.Y_own[r] for r in g.ranks]
@@ -212,11 +205,15 @@ def main():
     fwd_flops, total_flops = mlp_flops(w)
     value = total_flops / (ms * 1e-3) / 1e12
     gemm_kinds = ["fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a"]
-    # Dominant kernel: the symbol with the most time per step.
-    dom = max(KERNELS, key=lambda k: sum(per[r][1] for r in KERNELS[k]))
-    n_dom = sum(per[r][0] for r in KERNELS[dom])
-    tot_dom = sum(per[r][1] for r in KERNELS[dom])
-    flops_dom = sum(per[r][0] * kernel_flops(w, r) for r in KERNELS[dom])
+    # Dominant kernel: the GEMM kernel (one template instantiation, as the profiler names
+    # it) with the most time per step, over every schedule role that launched it.
+    by_kernel = {}
+    for r in gemm_kinds:
+        by_kernel.setdefault(kernel_of[r], []).append(r)
+    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
+    n_dom = sum(per[r][0] for r in by_kernel[dom])
+    tot_dom = sum(per[r][1] for r in by_kernel[dom])
+    flops_dom = sum(per[r][0] * kernel_flops(w, r) for r in by_kernel[dom])
     avg_ms = tot_dom / max(1, n_dom)
     achieved = flops_dom / (tot_dom * 1e-3) / 1e12
     n_red, tot_red = per["reduce"]
@@ -255,10 +252,11 @@ def main():
         "t_reduce_ms": round(red_ms_step, 4),
         "hidden_fraction": None if hidden_frac is None else round(hidden_frac, 3),
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+        "kernel_of_role": kernel_of,
+        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if args.workload == "gpt3_2p7b_mlp_tp8_row" else None,
+                     "traffic": measured_traffic(dom) if args.workload == "gpt3_2p7b_mlp_tp8_row" else None,
                      "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n_dom,
                      "flops_per_launch": flops_dom / max(1, n_dom)},
     }

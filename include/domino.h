@@ -203,6 +203,15 @@ typedef enum {
 
 domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */
 domino_status domino_timing_read(int32_t kind, int64_t* launches, double* total_ms);
+/*
+ * Writes into `name` (capacity bytes, NUL-terminated) the kernel that the most recent
+ * timed launch of class `kind` ran: its symbol and template arguments as a profiler
+ * prints them, e.g. "gemm_bf16_kernel<128, 128, 32, 3, 3, false, false, (domino::Epi)5>", or
+ * "" if none was timed since the last reset. Launches of one class with the same shapes
+ * run the same kernel, so classes can be grouped by it. DOMINO_ERR_INVALID_ARG for a bad
+ * kind, a NULL name or a buffer too small for the text.
+ */
+domino_status domino_timing_kernel(int32_t kind, char* name, size_t capacity);
 
 #ifdef __cplusplus
 }

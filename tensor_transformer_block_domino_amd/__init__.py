@@ -7,5 +7,5 @@ from ._lib import (  # noqa: F401
     DOMINO_ACT_GELU_TANH, DOMINO_ACT_SWIGLU, DOMINO_BF16, DOMINO_F32, DOMINO_MAX_PARTIALS, EXPORTED, KERNEL_KINDS,
     LIB_PATH, AttnDesc, DominoError, MlpDesc, domino_attn_block_fwd, domino_block_bwd,
     domino_block_bwd_workspace_size, domino_block_fwd, domino_status_string, domino_timing_enable,
-    domino_timing_read, load, shard_reduce,
+    domino_timing_kernel, domino_timing_read, load, shard_reduce,
 )

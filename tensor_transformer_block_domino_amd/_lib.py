@@ -24,7 +24,7 @@ KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgra
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_bwd", "domino_block_bwd_workspace_size",
             "domino_attn_block_fwd", "domino_status_string", "domino_last_error", "domino_timing_enable",
-            "domino_timing_read")
+            "domino_timing_read", "domino_timing_kernel")
 
 
 class MlpDesc(ctypes.Structure):
@@ -80,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.domino_timing_enable.restype = i32
     lib.domino_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
     lib.domino_timing_read.restype = i32
+    lib.domino_timing_kernel.argtypes = [i32, ctypes.c_char_p, ctypes.c_size_t]
+    lib.domino_timing_kernel.restype = i32
     _lib = lib
     return lib
 
@@ -158,3 +160,11 @@ def domino_timing_read(kind) -> tuple:
     n, ms = ctypes.c_int64(), ctypes.c_double()
     _check(load().domino_timing_read(k, ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def domino_timing_kernel(kind) -> str:
+    """The kernel the most recent timed launch of a kernel class ran ("" if none)."""
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    buf = ctypes.create_string_buffer(256)
+    _check(load().domino_timing_kernel(k, buf, len(buf)))
+    return buf.value.decode()

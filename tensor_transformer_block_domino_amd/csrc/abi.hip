@@ -19,6 +19,7 @@
 // One hipEvent_t pair per chunk stands in for the pages' communication handles.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -77,6 +78,7 @@ hipError_t events_for_current_device(EventSet** out) {
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
+  std::string kernel;
 };
 std::mutex g_timing_mu;
 bool g_timing = false;
@@ -84,6 +86,8 @@ std::vector<TimingRec> g_timing_recs;
 std::vector<hipEvent_t> g_timing_free;
 double g_timing_ms[DOMINO_K_COUNT];
 int64_t g_timing_n[DOMINO_K_COUNT];
+std::string g_timing_kernel[DOMINO_K_COUNT];
+thread_local std::string t_kernel;  // the kernel the calling thread's launcher last noted
 
 hipEvent_t timing_event() {
   if (!g_timing_free.empty()) {
@@ -111,12 +115,13 @@ hipError_t timed(int kind, hipStream_t s, F&& f) {
     b = timing_event();
   }
   if (!a || !b) return hipErrorOutOfMemory;
+  t_kernel.clear();
   hipError_t e = hipEventRecord(a, s);
   if (e == hipSuccess) e = f();
   if (e == hipSuccess) e = hipEventRecord(b, s);
   if (e == hipSuccess) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_timing_recs.push_back({kind, a, b});
+    g_timing_recs.push_back({kind, a, b, t_kernel});
   }
   return e;
 }
@@ -240,7 +245,25 @@ hipError_t splitk_finish(const GemmArgs& g, int splits, hipStream_t s) {
   });
 }
 
+// Folds the pending event pairs into the per-kind sums (caller holds g_timing_mu).
+domino_status timing_collect() {
+  for (auto& r : g_timing_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return fail(DOMINO_ERR_HIP, "timing event query failed");
+    g_timing_ms[r.kind] += ms;
+    g_timing_n[r.kind] += 1;
+    if (!r.kernel.empty()) g_timing_kernel[r.kind] = r.kernel;
+    g_timing_free.push_back(r.a);
+    g_timing_free.push_back(r.b);
+  }
+  g_timing_recs.clear();
+  return DOMINO_OK;
+}
+
 }  // namespace
+
+void domino::note_kernel(const char* name) { t_kernel = name; }
 
 extern "C" {
 
@@ -544,6 +567,7 @@ domino_status domino_timing_enable(int32_t enable) {
   for (int k = 0; k < DOMINO_K_COUNT; ++k) {
     g_timing_ms[k] = 0.0;
     g_timing_n[k] = 0;
+    g_timing_kernel[k].clear();
   }
   g_timing = enable != 0;
   return DOMINO_OK;
@@ -553,18 +577,22 @@ domino_status domino_timing_read(int32_t kind, int64_t* launches, double* total_
   t_last_error.clear();
   if (kind < 0 || kind >= DOMINO_K_COUNT || !launches || !total_ms) return fail(DOMINO_ERR_INVALID_ARG, "bad argument");
   std::lock_guard<std::mutex> lk(g_timing_mu);
-  for (auto& r : g_timing_recs) {
-    float ms = 0.f;
-    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
-      return fail(DOMINO_ERR_HIP, "timing event query failed");
-    g_timing_ms[r.kind] += ms;
-    g_timing_n[r.kind] += 1;
-    g_timing_free.push_back(r.a);
-    g_timing_free.push_back(r.b);
-  }
-  g_timing_recs.clear();
+  domino_status st = timing_collect();
+  if (st != DOMINO_OK) return st;
   *launches = g_timing_n[kind];
   *total_ms = g_timing_ms[kind];
+  return DOMINO_OK;
+}
+
+domino_status domino_timing_kernel(int32_t kind, char* name, size_t capacity) {
+  t_last_error.clear();
+  if (kind < 0 || kind >= DOMINO_K_COUNT || !name || capacity == 0) return fail(DOMINO_ERR_INVALID_ARG, "bad argument");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  domino_status st = timing_collect();
+  if (st != DOMINO_OK) return st;
+  const std::string& k = g_timing_kernel[kind];
+  if (k.size() + 1 > capacity) return fail(DOMINO_ERR_INVALID_ARG, "name buffer too small");
+  std::copy(k.c_str(), k.c_str() + k.size() + 1, name);
   return DOMINO_OK;
 }
 

@@ -13,20 +13,17 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 <-> fp32. A bf16 value is the top half of an fp32; conversion to bf16 rounds to
-// nearest, ties to even (NaN stays NaN).
+// nearest, ties to even (v_cvt_pk_bf16_f32, two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Element type traits for the generic (fp32 / bf16) paths.
 template <typename T> struct Elem;
@@ -39,22 +36,25 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = uint16_t(f32_to_bf16_bits(v)); }
 };
 
-// Activations, written from their definitions. σ(x) = 1 / (1 + e^(−x)); the tanh-form
-// GeLU uses 0.5·(1 + tanh(u)) = σ(2u) with u = √(2/π)·(x + 0.044715·x³).
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-
-__device__ __forceinline__ float gelu_tanh_f(float x) {
-  const float k0 = 0.7978845608028654f;  // √(2/π)
-  const float u = k0 * (x + 0.044715f * x * x * x);
-  return x * sigmoidf_(2.0f * u);
+// Activations, written from their definitions. σ(x) = 1 / (1 + e^(−x)), evaluated as
+// rcp(1 + 2^(−x·log2 e)) (v_exp_f32, v_rcp_f32: about 1 ulp each). The tanh-form GeLU
+// uses 0.5·(1 + tanh(u)) = σ(2u) with u = √(2/π)·(x + 0.044715·x³), so
+// gelu(x) = x·σ(2u) and, with s = σ(2u) and 1 − tanh²(u) = 4·s·(1 − s),
+// gelu'(x) = s + x·s·(1 − s)·2√(2/π)·(1 + 3·0.044715·x²).
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
+constexpr float kGeluA = 2.0f * 0.7978845608028654f;  // 2·√(2/π): 2u = x·(A + B·x²)
+constexpr float kGeluB = kGeluA * 0.044715f;
+constexpr float kGeluC = kGeluA * 3.0f * 0.044715f;   // d(2u)/dx = A + C·x²
+
+__device__ __forceinline__ float gelu_tanh_f(float x) { return x * sigmoidf_(x * fmaf(kGeluB, x * x, kGeluA)); }
+
 __device__ __forceinline__ float gelu_tanh_grad_f(float x) {
-  const float k0 = 0.7978845608028654f;
-  const float u = k0 * (x + 0.044715f * x * x * x);
-  const float t = 2.0f * sigmoidf_(2.0f * u) - 1.0f;  // tanh(u)
-  const float du = k0 * (1.0f + 3.0f * 0.044715f * x * x);
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * du;
+  const float x2 = x * x;
+  const float s = sigmoidf_(x * fmaf(kGeluB, x2, kGeluA));
+  return fmaf(s, x * (1.0f - s) * fmaf(kGeluC, x2, kGeluA), s);
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoidf_(x); }

@@ -28,6 +28,7 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile index is remapped
 //    so each XCD gets a contiguous, M-grouped range of tiles that share operand rows in
 //    its L2.
+#include <cstdio>
 #include <type_traits>
 
 #include "common.hpp"
@@ -196,22 +197,38 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
   *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
+// The saved activation input the backward epilogues read for outputs (m, n..n+3): Hpre
+// (tanh-GeLU), or its gate and up columns (SwiGLU). Loaded for a whole row block before
+// any is used, so the loads overlap.
+struct AuxQuad {
+  u32x2_t g, u;
+};
+template <Epi kEpi>
+__device__ __forceinline__ AuxQuad load_aux4(const KParams& p, int64_t m, int64_t n) {
+  AuxQuad a{};
+  if constexpr (kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu)
+    a.g = *reinterpret_cast<const u32x2_t*>(p.aux + m * p.ldaux + n);
+  if constexpr (kEpi == Epi::kDSwiglu)
+    a.u = *reinterpret_cast<const u32x2_t*>(p.aux + m * p.ldaux + p.f_s + n);
+  return a;
+}
+
 // Epilogue for 4 consecutive output columns n..n+3 of row m (n < N, all four in range).
 template <Epi kEpi>
-__device__ __forceinline__ void epilogue4(const KParams& p, int split, int64_t m, int64_t n, f32x4_t v) {
+__device__ __forceinline__ void epilogue4(const KParams& p, int split, int64_t m, int64_t n, f32x4_t v,
+                                          const AuxQuad& ax) {
   if constexpr (kEpi == Epi::kStore) {
     store_bf16x4(static_cast<uint16_t*>(p.C) + m * p.ldc + n, v.x, v.y, v.z, v.w);
   } else if constexpr (kEpi == Epi::kGelu) {
     store_bf16x4(static_cast<uint16_t*>(p.C) + m * p.ldc + n, v.x, v.y, v.z, v.w);
     store_bf16x4(p.C2 + m * p.ldc2 + n, gelu_tanh_f(v.x), gelu_tanh_f(v.y), gelu_tanh_f(v.z), gelu_tanh_f(v.w));
   } else if constexpr (kEpi == Epi::kDGelu) {
-    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p.aux + m * p.ldaux + n);
+    const u32x2_t x = ax.g;
     store_bf16x4(static_cast<uint16_t*>(p.C) + m * p.ldc + n, v.x * gelu_tanh_grad_f(bf16_lo(x.x)),
                  v.y * gelu_tanh_grad_f(bf16_hi(x.x)), v.z * gelu_tanh_grad_f(bf16_lo(x.y)),
                  v.w * gelu_tanh_grad_f(bf16_hi(x.y)));
   } else if constexpr (kEpi == Epi::kDSwiglu) {
-    const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(p.aux + m * p.ldaux + n);
-    const u32x2_t uw = *reinterpret_cast<const u32x2_t*>(p.aux + m * p.ldaux + p.f_s + n);
+    const u32x2_t gw = ax.g, uw = ax.u;
     const float g[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
     const float u[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
     const float dh[4] = {v.x, v.y, v.z, v.w};
@@ -389,6 +406,14 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           epilogue_swiglu4(p, m, jj, g, u);
         }
     } else {
+      AuxQuad ax[TN][4];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = n0 + wn * WN + j * 32 + q * 8 + 4 * (lane >> 5);
+          ax[j][q] = n < p.N ? load_aux4<kEpi>(p, m, n) : AuxQuad{};
+        }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -396,7 +421,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           const int64_t n = n0 + wn * WN + j * 32 + q * 8 + 4 * (lane >> 5);
           if (n >= p.N) continue;
           const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epilogue4<kEpi>(p, split, m, n, v);
+          epilogue4<kEpi>(p, split, m, n, v, ax[j][q]);
         }
     }
   }
@@ -420,6 +445,11 @@ constexpr TileCfg kTiles[] = {
 
 template <bool kAK, bool kBKc, Epi kEpi>
 hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
+  const TileCfg& tc = kTiles[ti];
+  char name[96];
+  snprintf(name, sizeof name, "gemm_bf16_kernel<%d, %d, %d, %d, %d, %s, %s, (domino::Epi)%d>", tc.bm, tc.bn, tc.bk,
+           tc.ns, tc.occ, kAK ? "true" : "false", kBKc ? "true" : "false", int(kEpi));
+  note_kernel(name);
   if (ti == 0)
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 2, 2, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
   else if (ti == 1)

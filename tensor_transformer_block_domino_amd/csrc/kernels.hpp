@@ -9,6 +9,10 @@ namespace domino {
 
 constexpr int kMaxPartials = 16;
 
+// Records the kernel (symbol and template arguments) a launcher is about to launch on the
+// calling thread; the timing facility attaches it to the launch it brackets.
+void note_kernel(const char* name);
+
 struct ReduceArgs {
   void* out;
   int64_t ld_out;

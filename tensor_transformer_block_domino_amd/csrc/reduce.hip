@@ -8,6 +8,8 @@
 // (P+1)·rows·cols·elem bytes. Each thread owns 16-byte column groups of a row; all P
 // loads of a group are issued before the fp32 accumulation in the fixed order p = 0..P−1,
 // so a wave keeps 2·P 16-byte loads in flight. No LDS, no MFMA.
+#include <cstdio>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -87,6 +89,9 @@ static hipError_t launch_reduce_p(const ReduceArgs& a, hipStream_t s) {
   // Enough waves to cover HBM latency: up to 8 workgroups of 256 threads per CU.
   const uint32_t want = (total + 2 * 256 - 1) / (2 * 256);
   const uint32_t blocks = want < 256u * 8u ? (want ? want : 1u) : 256u * 8u;
+  char name[64];
+  snprintf(name, sizeof name, "shard_reduce_kernel<%s, %d>", sizeof(T) == 2 ? "bf16" : "f32", P);
+  note_kernel(name);
   hipLaunchKernelGGL((shard_reduce_kernel<T, P>), dim3(blocks), dim3(256), 0, s, a.out, a.ld_out, parts,
                      a.ld_in, uint32_t(a.rows), groups_per_row, total);
   return hipGetLastError();
@@ -145,6 +150,7 @@ hipError_t launch_splitk_sum(float* out, int64_t ldc, const float* ws, int split
   if (!total) return hipSuccess;
   const uint32_t want = (total + 255) / 256;
   const uint32_t blocks = want < 2048u ? want : 2048u;
+  note_kernel("splitk_sum_kernel");
   hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, out, ldc, ws, rows * cols, splits,
                      uint32_t(rows), cols4, accumulate);
   return hipGetLastError();

@@ -147,6 +147,9 @@ def test_timing_read_rejects_bad_kind(lib):
         D.domino_timing_read(99)
     D.domino_timing_enable(False)
     assert D.domino_timing_read("reduce") == (0, 0.0)
+    assert D.domino_timing_kernel("reduce") == ""
+    with pytest.raises(D.DominoError):
+        D.domino_timing_kernel(-1)
 
 
 def test_workspace_size_is_zero_for_fp32_and_sized_for_bf16(lib):
