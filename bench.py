@@ -159,7 +159,8 @@ def main():
 
     def step_unsplit():
         d_f = g.desc(rank_alone=True, row_chunks=1, col_chunks=1)
-        D.domino_block_fwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, compute, None)
+        D.domino_block_fwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, g.ws, g.ws_bytes,
+                           compute, None)
         D.domino_block_bwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.dY, g.dHpre[0], g.dX_own[0], None,
                            None, g.dA, g.dB, 0, g.ws, g.ws_bytes, compute, None)
 

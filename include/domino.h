@@ -41,6 +41,14 @@
  *              valid only in `comm` order. comm == NULL or comm == compute runs the
  *              reductions inline on `compute` (plain, un-overlapped tensor parallelism).
  *              Peer partials must be ready in `compute` order when the call is made.
+ *   Workspace  The block calls take an optional device workspace (`workspace`,
+ *              `workspace_bytes`; its size from the matching *_workspace_size query).
+ *              With it, a product whose last round of tiles would leave most of the GPU
+ *              idle splits those tiles along k into fp32 slices and finishes them with a
+ *              fixed-order sum (results do not depend on timing); without it (NULL, or
+ *              too small) every tile is computed whole. Its contents need no
+ *              initialisation and are scratch between calls; calls sharing one workspace
+ *              must be ordered by the caller.
  *   Errors     Every argument is checked before anything is enqueued; on an error
  *              nothing runs and the status says why. A failed HIP launch returns
  *              DOMINO_ERR_HIP (work enqueued before it may have run).
@@ -124,13 +132,16 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
  *   peer_Y  HOST array of n_partials-1 device pointers [T, hidden]      (inputs; NULL if P==1)
  *   Y [T, hidden]                      reduced output; NULL or Y_own reduces in place into
  *                                      Y_own (with P == 1 that means no reduction runs)
+ *   workspace, workspace_bytes         optional device scratch (see Workspace above)
  */
 domino_status domino_block_fwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
                                void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
+                               void* workspace, size_t workspace_bytes,
                                hipStream_t compute, hipStream_t comm);
 
-/* Bytes of `workspace` domino_block_bwd can use for split-K weight gradients (0 is
- * always valid: the call then runs without split-K). */
+/* Bytes of workspace the block calls with this descriptor can use (0 for an invalid
+ * descriptor or when no product splits; any size, including 0, is valid to pass). */
+size_t domino_block_fwd_workspace_size(const domino_mlp_desc* desc);
 size_t domino_block_bwd_workspace_size(const domino_mlp_desc* desc);
 
 /*
@@ -147,7 +158,7 @@ size_t domino_block_bwd_workspace_size(const domino_mlp_desc* desc);
  *   dX_own, dX [T, hidden]; peer_dX HOST array of n_partials-1 device pointers; dX NULL or
  *                                       dX_own reduces in place into dX_own
  *   dA_s [hidden, n1], dB_s [ffn_shard, hidden]  fp32
- *   workspace, workspace_bytes          optional device scratch (see _workspace_size)
+ *   workspace, workspace_bytes          optional device scratch (see Workspace above)
  * Weight gradients are deterministic; the reduction order is fixed.
  */
 domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
@@ -167,11 +178,14 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
  *   columns j·head_dim within each block; B_o_s [heads·head_dim, hidden]   (inputs)
  *   QKV [T, 3·heads·head_dim], O [T, heads·head_dim]   saved activations   (outputs)
  *   Y_own, Y [T, hidden]; peer_Y HOST array of n_partials-1 device pointers
+ *   workspace, workspace_bytes          optional device scratch (see Workspace above)
  * head_dim must be 128; bf16 only.
  */
 domino_status domino_attn_block_fwd(const domino_attn_desc* desc, const void* X, const void* A_qkv_s,
                                     const void* B_o_s, void* QKV, void* O, void* Y_own,
-                                    const void* const* peer_Y, void* Y, hipStream_t compute, hipStream_t comm);
+                                    const void* const* peer_Y, void* Y, void* workspace, size_t workspace_bytes,
+                                    hipStream_t compute, hipStream_t comm);
+size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* desc);
 
 /* Human-readable name of a status code (static storage). */
 const char* domino_status_string(domino_status status);
@@ -197,7 +211,7 @@ typedef enum {
   DOMINO_K_QKV = 7,
   DOMINO_K_ATTN = 8,
   DOMINO_K_OUTPROJ = 9,
-  DOMINO_K_AUX = 10,        /* fills and split-K sums */
+  DOMINO_K_AUX = 10,        /* k-split tiles' fixed-order slice sums with their epilogues */
   DOMINO_K_COUNT = 11
 } domino_kernel_kind;
 

@@ -22,8 +22,9 @@ KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgra
                 "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10}
 
 # Every symbol the header declares (checked by the CPU export test).
-EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_bwd", "domino_block_bwd_workspace_size",
-            "domino_attn_block_fwd", "domino_status_string", "domino_last_error", "domino_timing_enable",
+EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
+            "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
+            "domino_status_string", "domino_last_error", "domino_timing_enable",
             "domino_timing_read", "domino_timing_kernel")
 
 
@@ -63,14 +64,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     pp = ctypes.POINTER(ctypes.c_void_p)
     lib.shard_reduce.argtypes = [vp, i64, pp, i32, i64, i64, i64, i32, vp]
     lib.shard_reduce.restype = i32
-    lib.domino_block_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, vp]
+    lib.domino_block_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, ctypes.c_size_t,
+                                     vp, vp]
     lib.domino_block_fwd.restype = i32
-    lib.domino_block_bwd_workspace_size.argtypes = [ctypes.POINTER(MlpDesc)]
-    lib.domino_block_bwd_workspace_size.restype = ctypes.c_size_t
+    for name, desc in (("domino_block_fwd_workspace_size", MlpDesc), ("domino_block_bwd_workspace_size", MlpDesc),
+                       ("domino_attn_block_fwd_workspace_size", AttnDesc)):
+        getattr(lib, name).argtypes = [ctypes.POINTER(desc)]
+        getattr(lib, name).restype = ctypes.c_size_t
     lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32,
                                      vp, ctypes.c_size_t, vp, vp]
     lib.domino_block_bwd.restype = i32
-    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, vp]
+    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp,
+                                          ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_fwd.restype = i32
     lib.domino_status_string.argtypes = [i32]
     lib.domino_status_string.restype = ctypes.c_char_p
@@ -124,13 +129,23 @@ def shard_reduce(out, ld_out: int, partials: Sequence, ld_in: int, rows: int, co
                                _stream(stream)))
 
 
-def domino_block_fwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, Y_own, peer_Y, Y, compute=None, comm=None):
+def domino_block_fwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, Y_own, peer_Y, Y, workspace=None, workspace_bytes: int = 0,
+                     compute=None, comm=None):
     _check(load().domino_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H),
-                                   _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _stream(compute), _stream(comm)))
+                                   _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace), int(workspace_bytes),
+                                   _stream(compute), _stream(comm)))
+
+
+def domino_block_fwd_workspace_size(desc: MlpDesc) -> int:
+    return int(load().domino_block_fwd_workspace_size(ctypes.byref(desc)))
 
 
 def domino_block_bwd_workspace_size(desc: MlpDesc) -> int:
     return int(load().domino_block_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def domino_attn_block_fwd_workspace_size(desc: AttnDesc) -> int:
+    return int(load().domino_attn_block_fwd_workspace_size(ctypes.byref(desc)))
 
 
 def domino_block_bwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, peer_dX, dX, dA_s, dB_s,
@@ -141,9 +156,11 @@ def domino_block_bwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, pee
                                    _stream(comm)))
 
 
-def domino_attn_block_fwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, Y_own, peer_Y, Y, compute=None, comm=None):
+def domino_attn_block_fwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, Y_own, peer_Y, Y, workspace=None,
+                          workspace_bytes: int = 0, compute=None, comm=None):
     _check(load().domino_attn_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
-                                        _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _stream(compute), _stream(comm)))
+                                        _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace),
+                                        int(workspace_bytes), _stream(compute), _stream(comm)))
 
 
 def domino_status_string(status: int) -> str:

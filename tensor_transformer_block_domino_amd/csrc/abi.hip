@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -235,14 +236,151 @@ domino_status check_mlp_desc(const domino_mlp_desc* d) {
   return DOMINO_OK;
 }
 
+domino_status check_attn_desc(const domino_attn_desc* d) {
+  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != DOMINO_BF16) {
+    if (d->dtype == DOMINO_F32) return fail(DOMINO_ERR_UNSUPPORTED, "attention is bf16 only");
+    return fail(DOMINO_ERR_INVALID_ARG, "bad dtype");
+  }
+  if (d->batch < 0 || d->seq < 0 || d->hidden < 0 || d->heads < 0) return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (d->head_dim != 128) return fail(DOMINO_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->row_chunks < 1 || d->row_chunks > kMaxChunks) return fail(DOMINO_ERR_SHAPE, "bad row_chunks");
+  if (d->batch % d->row_chunks) return fail(DOMINO_ERR_SHAPE, "batch % row_chunks != 0");
+  if (d->n_partials < 1 || d->n_partials > DOMINO_MAX_PARTIALS)
+    return fail(DOMINO_ERR_INVALID_ARG, "n_partials must be in 1..DOMINO_MAX_PARTIALS");
+  if (d->hidden % 8) return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of 8");
+  if (!(d->scale >= 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "scale must be >= 0 (0 selects 1/sqrt(head_dim))");
+  const int64_t T = d->batch * d->seq;
+  if (T > (int64_t(1) << 31) || d->seq > (int64_t(1) << 30)) return fail(DOMINO_ERR_UNSUPPORTED, "too many tokens");
+  return DOMINO_OK;
+}
+
 bool needs_reduce(int n_partials, const void* own, const void* out) { return n_partials > 1 || (out && out != own); }
 
-// The fixed-order sum of a split-K product's fp32 slices into its output.
-hipError_t splitk_finish(const GemmArgs& g, int splits, hipStream_t s) {
-  if (splits <= 1) return hipSuccess;
-  return timed(DOMINO_K_AUX, s, [&] {
-    return launch_splitk_sum(static_cast<float*>(g.C), g.ldc, g.ws, splits, g.M, g.N, g.accumulate, s);
-  });
+// The products of each call, built from the descriptor and the caller's buffers (null
+// buffers give the shapes alone, as the workspace-size queries need). Row-major buffers;
+// B(k, n) of a product reads an [in, out] weight as stored, or its transpose.
+GemmArgs gemm_base(int64_t M, int64_t N, int64_t K, bool bf16) {
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.bf16 = bf16;
+  return g;
+}
+int64_t mlp_n1(const domino_mlp_desc* d) { return d->act == DOMINO_ACT_SWIGLU ? 2 * d->ffn_shard : d->ffn_shard; }
+const char* at(const void* p, int64_t elems, size_t es) { return p ? static_cast<const char*>(p) + elems * es : nullptr; }
+char* at(void* p, int64_t elems, size_t es) { return p ? static_cast<char*>(p) + elems * es : nullptr; }
+
+// Hpre = X·A_s with the activation epilogue (H = act(Hpre)), over all T rows.
+GemmArgs mlp_gemm1(const domino_mlp_desc* d, const void* X, const void* A_s, void* Hpre, void* H) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard, n1 = mlp_n1(d);
+  GemmArgs g = gemm_base(T, f, h, d->dtype == DOMINO_BF16);
+  g.A = X; g.lda = h; g.a_kcontig = true;
+  g.B = A_s; g.ldb = n1; g.b_kcontig = false;
+  g.C = Hpre; g.ldc = n1;
+  g.C2 = H; g.ldc2 = f;
+  g.f_s = f;
+  g.epi = d->act == DOMINO_ACT_SWIGLU ? Epi::kSwiglu : Epi::kGelu;
+  return g;
+}
+// Y_own chunk (i, j) = H[rows_i]·B_s[:, cols_j].
+GemmArgs mlp_gemm2(const domino_mlp_desc* d, const void* H, const void* B_s, void* Y_own, int i, int j) {
+  const int64_t h = d->hidden, f = d->ffn_shard, Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
+  const size_t es = esize(d->dtype);
+  GemmArgs g = gemm_base(Tc, hc, f, d->dtype == DOMINO_BF16);
+  g.A = at(H, i * Tc * f, es); g.lda = f; g.a_kcontig = true;
+  g.B = at(B_s, j * hc, es); g.ldb = h; g.b_kcontig = false;
+  g.C = at(Y_own, i * Tc * h + j * hc, es); g.ldc = h;
+  g.epi = Epi::kStore;
+  return g;
+}
+// dX chunks: row chunks when rows are split (row or 2D split), else the column chunks.
+void mlp_dx_chunks(const domino_mlp_desc* d, int* rch, int* cch) {
+  *rch = d->row_chunks;
+  *cch = d->row_chunks > 1 ? 1 : d->col_chunks;
+}
+// dHpre = (dY·B_sᵀ) ⊙ act'(Hpre), over all T rows.
+GemmArgs mlp_dgrad_b(const domino_mlp_desc* d, const void* dY, const void* B_s, void* dHpre, const void* Hpre) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard, n1 = mlp_n1(d);
+  GemmArgs g = gemm_base(T, f, h, d->dtype == DOMINO_BF16);
+  g.A = dY; g.lda = h; g.a_kcontig = true;
+  g.B = B_s; g.ldb = h; g.b_kcontig = true;  // B(k, n) = B_s[n][k]
+  g.C = dHpre; g.ldc = n1;
+  g.aux = Hpre; g.ldaux = n1;
+  g.f_s = f;
+  g.epi = d->act == DOMINO_ACT_SWIGLU ? Epi::kDSwiglu : Epi::kDGelu;
+  return g;
+}
+// dX_own chunk (i, j) = dHpre[rows_i]·A_s[cols_j, :]ᵀ.
+GemmArgs mlp_dgrad_a(const domino_mlp_desc* d, const void* dHpre, const void* A_s, void* dX_own, int i, int j) {
+  int rch, cch;
+  mlp_dx_chunks(d, &rch, &cch);
+  const int64_t h = d->hidden, n1 = mlp_n1(d), Tc = (d->batch / rch) * d->seq, hc = h / cch;
+  const size_t es = esize(d->dtype);
+  GemmArgs g = gemm_base(Tc, hc, n1, d->dtype == DOMINO_BF16);
+  g.A = at(dHpre, i * Tc * n1, es); g.lda = n1; g.a_kcontig = true;
+  g.B = at(A_s, j * hc * n1, es); g.ldb = n1; g.b_kcontig = true;  // B(k, n) = A_s[n][k]
+  g.C = at(dX_own, i * Tc * h + j * hc, es); g.ldc = h;
+  g.epi = Epi::kStore;
+  return g;
+}
+// dB_s (+)= Hᵀ·dY in fp32.
+GemmArgs mlp_wgrad_b(const domino_mlp_desc* d, const void* H, const void* dY, float* dB_s, int accumulate) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
+  GemmArgs g = gemm_base(f, h, T, d->dtype == DOMINO_BF16);
+  g.A = H; g.lda = f; g.a_kcontig = false;   // A(m, k) = H[k][m]
+  g.B = dY; g.ldb = h; g.b_kcontig = false;  // B(k, n) = dY[k][n]
+  g.C = dB_s; g.ldc = h;
+  g.epi = Epi::kF32;
+  g.accumulate = accumulate;
+  return g;
+}
+// dA_s (+)= Xᵀ·dHpre in fp32.
+GemmArgs mlp_wgrad_a(const domino_mlp_desc* d, const void* X, const void* dHpre, float* dA_s, int accumulate) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, n1 = mlp_n1(d);
+  GemmArgs g = gemm_base(h, n1, T, d->dtype == DOMINO_BF16);
+  g.A = X; g.lda = h; g.a_kcontig = false;      // A(m, k) = X[k][m]
+  g.B = dHpre; g.ldb = n1; g.b_kcontig = false;  // B(k, n) = dHpre[k][n]
+  g.C = dA_s; g.ldc = n1;
+  g.epi = Epi::kF32;
+  g.accumulate = accumulate;
+  return g;
+}
+// QKV = X·A_qkv_s over all T rows.
+GemmArgs attn_qkv(const domino_attn_desc* d, const void* X, const void* A_qkv_s, void* QKV) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  GemmArgs g = gemm_base(T, 3 * hd, h, true);
+  g.A = X; g.lda = h; g.a_kcontig = true;
+  g.B = A_qkv_s; g.ldb = 3 * hd; g.b_kcontig = false;
+  g.C = QKV; g.ldc = 3 * hd;
+  g.epi = Epi::kStore;
+  return g;
+}
+// Y_own chunk i = O[rows_i]·B_o_s.
+GemmArgs attn_out(const domino_attn_desc* d, const void* O, const void* B_o_s, void* Y_own, int i) {
+  const int64_t h = d->hidden, hd = d->heads * d->head_dim, Tc = (d->batch / d->row_chunks) * d->seq;
+  GemmArgs g = gemm_base(Tc, h, hd, true);
+  g.A = at(O, i * Tc * hd, 2); g.lda = hd; g.a_kcontig = true;
+  g.B = B_o_s; g.ldb = h; g.b_kcontig = false;
+  g.C = at(Y_own, i * Tc * h, 2); g.ldc = h;
+  g.epi = Epi::kStore;
+  return g;
+}
+
+// One product on stream s: the GEMM (timed as `kind`), then, if it split tiles along k,
+// the fixed-order sum of their slices with the epilogue (timed as auxiliary work).
+hipError_t run_gemm(int kind, GemmArgs g, void* ws, size_t ws_bytes, hipStream_t s) {
+  g.ws = static_cast<float*>(ws);
+  g.ws_elems = ws ? int64_t(ws_bytes / sizeof(float)) : 0;
+  GemmSplit sp;
+  hipError_t e = timed(kind, s, [&] { return launch_gemm(g, s, &sp); });
+  if (e == hipSuccess && sp.pending) e = timed(DOMINO_K_AUX, s, [&] { return launch_gemm_fixup(g, sp, s); });
+  return e;
+}
+
+size_t ws_bytes_of(std::initializer_list<GemmArgs> gs) {
+  int64_t n = 0;
+  for (const GemmArgs& g : gs) n = std::max(n, gemm_ws_elems(g));
+  return size_t(n) * sizeof(float);
 }
 
 // Folds the pending event pairs into the per-kind sums (caller holds g_timing_mu).
@@ -320,58 +458,42 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
   return DOMINO_OK;
 }
 
+size_t domino_block_fwd_workspace_size(const domino_mlp_desc* d) {
+  if (check_mlp_desc(d) != DOMINO_OK) return 0;
+  return ws_bytes_of({mlp_gemm1(d, nullptr, nullptr, nullptr, nullptr), mlp_gemm2(d, nullptr, nullptr, nullptr, 0, 0)});
+}
+
 domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s, void* Hpre,
-                               void* H, void* Y_own, const void* const* peer_Y, void* Y, hipStream_t compute,
-                               hipStream_t comm) {
+                               void* H, void* Y_own, const void* const* peer_Y, void* Y, void* workspace,
+                               size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_mlp_desc(d);
   if (st != DOMINO_OK) return st;
   const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
-  const bool sw = d->act == DOMINO_ACT_SWIGLU;
-  const int64_t n1 = sw ? 2 * f : f;
   if (T == 0 || h == 0) return DOMINO_OK;
   const bool red = needs_reduce(d->n_partials, Y_own, Y);
   if ((st = check_ptr(X, "X", true)) || (st = check_ptr(A_s, "A_s", f > 0)) || (st = check_ptr(B_s, "B_s", f > 0)) ||
       (st = check_ptr(Hpre, "Hpre", f > 0)) || (st = check_ptr(H, "H", f > 0)) || (st = check_ptr(Y_own, "Y_own", true)) ||
       (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) || (st = check_ptr(Y ? Y : Y_own, "Y", red)))
     return st;
+  if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
   Sched sc;
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
 
-  const bool bf = d->dtype == DOMINO_BF16;
-  const size_t es = esize(d->dtype);
   const int64_t Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
   std::string msg;
   // The first product (column-parallel, activation fused) feeds no reduction, so it runs
   // once over all rows: chunking it would only narrow the GEMM. The second product is
   // launched per Domino chunk, and each chunk's reduction starts as soon as it ends.
-  if (f > 0) {
-    GemmArgs g1{};
-    g1.M = T; g1.N = f; g1.K = h;
-    g1.A = X; g1.lda = h; g1.a_kcontig = true;
-    g1.B = A_s; g1.ldb = n1; g1.b_kcontig = false;
-    g1.C = Hpre; g1.ldc = n1;
-    g1.C2 = H; g1.ldc2 = f;
-    g1.f_s = f;
-    g1.epi = sw ? Epi::kSwiglu : Epi::kGelu;
-    g1.bf16 = bf;
-    if (hip_ok(timed(DOMINO_K_FWD_GEMM1, sc.cs, [&] { return launch_gemm(g1, sc.cs, nullptr); }), &msg, "GEMM1"))
-      return fail(DOMINO_ERR_HIP, msg);
-  }
+  if (f > 0 && hip_ok(run_gemm(DOMINO_K_FWD_GEMM1, mlp_gemm1(d, X, A_s, Hpre, H), workspace, workspace_bytes, sc.cs),
+                      &msg, "GEMM1"))
+    return fail(DOMINO_ERR_HIP, msg);
   for (int i = 0; i < d->row_chunks; ++i) {
-    const int64_t r0 = i * Tc;
     for (int j = 0; j < d->col_chunks; ++j) {
-      const int64_t c0 = j * hc;
-      GemmArgs g2{};
-      g2.M = Tc; g2.N = hc; g2.K = f;
-      g2.A = static_cast<const char*>(H) + r0 * f * es; g2.lda = f; g2.a_kcontig = true;
-      g2.B = static_cast<const char*>(B_s) + c0 * es; g2.ldb = h; g2.b_kcontig = false;
-      g2.C = static_cast<char*>(Y_own) + (r0 * h + c0) * es; g2.ldc = h;
-      g2.epi = Epi::kStore;
-      g2.bf16 = bf;
-      if (hip_ok(timed(DOMINO_K_FWD_GEMM2, sc.cs, [&] { return launch_gemm(g2, sc.cs, nullptr); }), &msg, "GEMM2"))
+      if (hip_ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(d, H, B_s, Y_own, i, j), workspace, workspace_bytes, sc.cs),
+                 &msg, "GEMM2"))
         return fail(DOMINO_ERR_HIP, msg);
-      if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, r0 * h + c0, Tc, hc, d->dtype),
+      if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, i * Tc * h + j * hc, Tc, hc, d->dtype),
                         &msg, "reduce Y"))
         return fail(DOMINO_ERR_HIP, msg);
     }
@@ -381,11 +503,9 @@ domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const vo
 }
 
 size_t domino_block_bwd_workspace_size(const domino_mlp_desc* d) {
-  if (check_mlp_desc(d) != DOMINO_OK || d->dtype != DOMINO_BF16) return 0;
-  const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
-  const int64_t n1 = d->act == DOMINO_ACT_SWIGLU ? 2 * f : f;
-  const int64_t a = gemm_splitk_ws_elems(f, h, T), b = gemm_splitk_ws_elems(h, n1, T);
-  return size_t(a > b ? a : b) * sizeof(float);
+  if (check_mlp_desc(d) != DOMINO_OK) return 0;
+  return ws_bytes_of({mlp_dgrad_b(d, nullptr, nullptr, nullptr, nullptr), mlp_dgrad_a(d, nullptr, nullptr, nullptr, 0, 0),
+                      mlp_wgrad_b(d, nullptr, nullptr, nullptr, 0), mlp_wgrad_a(d, nullptr, nullptr, nullptr, 0)});
 }
 
 domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
@@ -396,8 +516,6 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
   domino_status st = check_mlp_desc(d);
   if (st != DOMINO_OK) return st;
   const int64_t T = d->batch * d->seq, h = d->hidden, f = d->ffn_shard;
-  const bool sw = d->act == DOMINO_ACT_SWIGLU;
-  const int64_t n1 = sw ? 2 * f : f;
   if (h == 0) return DOMINO_OK;
   const bool red = T > 0 && needs_reduce(d->n_partials, dX_own, dX);
   const bool tok = T > 0, ffn = f > 0;
@@ -412,144 +530,84 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
   Sched sc;
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
 
-  const bool bf = d->dtype == DOMINO_BF16;
-  const size_t es = esize(d->dtype);
-  // dX chunks: row chunks when rows are split (row or 2D split), else the column chunks.
-  const int rch = d->row_chunks, cch = d->row_chunks > 1 ? 1 : d->col_chunks;
+  int rch, cch;
+  mlp_dx_chunks(d, &rch, &cch);
   const int64_t Tc = (d->batch / rch) * d->seq, hc = h / cch;
   std::string msg;
   // dgrad of the second layer (activation gradient fused) feeds no reduction: one launch
   // over all rows. dgrad of the first layer is launched per dX chunk, each followed by
-  // its reduction.
-  if (tok && ffn) {
-    GemmArgs gb{};
-    gb.M = T; gb.N = f; gb.K = h;
-    gb.A = dY; gb.lda = h; gb.a_kcontig = true;
-    gb.B = B_s; gb.ldb = h; gb.b_kcontig = true;          // B(k, n) = B_s[n][k]
-    gb.C = dHpre; gb.ldc = n1;
-    gb.aux = Hpre; gb.ldaux = n1;
-    gb.f_s = f;
-    gb.epi = sw ? Epi::kDSwiglu : Epi::kDGelu;
-    gb.bf16 = bf;
-    if (hip_ok(timed(DOMINO_K_DGRAD_B, sc.cs, [&] { return launch_gemm(gb, sc.cs, nullptr); }), &msg, "dgrad B"))
-      return fail(DOMINO_ERR_HIP, msg);
-  }
+  // its reduction; the weight gradients follow, behind the last reduction.
+  if (tok && ffn &&
+      hip_ok(run_gemm(DOMINO_K_DGRAD_B, mlp_dgrad_b(d, dY, B_s, dHpre, Hpre), workspace, workspace_bytes, sc.cs), &msg,
+             "dgrad B"))
+    return fail(DOMINO_ERR_HIP, msg);
   for (int i = 0; i < rch && tok; ++i) {
-    const int64_t r0 = i * Tc;
     for (int j = 0; j < cch; ++j) {
-      const int64_t c0 = j * hc;
-      GemmArgs ga{};
-      ga.M = Tc; ga.N = hc; ga.K = n1;
-      ga.A = static_cast<const char*>(dHpre) + r0 * n1 * es; ga.lda = n1; ga.a_kcontig = true;
-      ga.B = static_cast<const char*>(A_s) + c0 * n1 * es; ga.ldb = n1; ga.b_kcontig = true;  // B(k,n) = A_s[n][k]
-      ga.C = static_cast<char*>(dX_own) + (r0 * h + c0) * es; ga.ldc = h;
-      ga.epi = Epi::kStore;
-      ga.bf16 = bf;
-      if (hip_ok(timed(DOMINO_K_DGRAD_A, sc.cs, [&] { return launch_gemm(ga, sc.cs, nullptr); }), &msg, "dgrad A"))
+      if (hip_ok(run_gemm(DOMINO_K_DGRAD_A, mlp_dgrad_a(d, dHpre, A_s, dX_own, i, j), workspace, workspace_bytes, sc.cs),
+                 &msg, "dgrad A"))
         return fail(DOMINO_ERR_HIP, msg);
-      if (red && hip_ok(sc.reduce(dX ? dX : dX_own, dX_own, peer_dX, d->n_partials, h, r0 * h + c0, Tc, hc, d->dtype),
+      if (red && hip_ok(sc.reduce(dX ? dX : dX_own, dX_own, peer_dX, d->n_partials, h, i * Tc * h + j * hc, Tc, hc,
+                                  d->dtype),
                         &msg, "reduce dX"))
         return fail(DOMINO_ERR_HIP, msg);
     }
   }
   if (ffn) {
-    float* ws = static_cast<float*>(workspace);
-    const int64_t ws_elems = int64_t(workspace_bytes / sizeof(float));
-    GemmArgs wb{};
-    wb.M = f; wb.N = h; wb.K = T;
-    wb.A = H; wb.lda = f; wb.a_kcontig = false;       // A(m, k) = H[k][m]
-    wb.B = dY; wb.ldb = h; wb.b_kcontig = false;      // B(k, n) = dY[k][n]
-    wb.C = dB_s; wb.ldc = h;
-    wb.epi = Epi::kF32;
-    wb.accumulate = accumulate;
-    wb.ws = ws; wb.ws_elems = ws_elems;
-    wb.bf16 = bf;
-    int splits = 1;
-    if (hip_ok(timed(DOMINO_K_WGRAD_B, sc.cs, [&] { return launch_gemm(wb, sc.cs, &splits); }), &msg, "wgrad B") ||
-        hip_ok(splitk_finish(wb, splits, sc.cs), &msg, "wgrad B split-K sum"))
-      return fail(DOMINO_ERR_HIP, msg);
-    GemmArgs wa{};
-    wa.M = h; wa.N = n1; wa.K = T;
-    wa.A = X; wa.lda = h; wa.a_kcontig = false;       // A(m, k) = X[k][m]
-    wa.B = dHpre; wa.ldb = n1; wa.b_kcontig = false;  // B(k, n) = dHpre[k][n]
-    wa.C = dA_s; wa.ldc = n1;
-    wa.epi = Epi::kF32;
-    wa.accumulate = accumulate;
-    wa.ws = ws; wa.ws_elems = ws_elems;
-    wa.bf16 = bf;
-    if (hip_ok(timed(DOMINO_K_WGRAD_A, sc.cs, [&] { return launch_gemm(wa, sc.cs, &splits); }), &msg, "wgrad A") ||
-        hip_ok(splitk_finish(wa, splits, sc.cs), &msg, "wgrad A split-K sum"))
+    if (hip_ok(run_gemm(DOMINO_K_WGRAD_B, mlp_wgrad_b(d, H, dY, dB_s, accumulate), workspace, workspace_bytes, sc.cs),
+               &msg, "wgrad B") ||
+        hip_ok(run_gemm(DOMINO_K_WGRAD_A, mlp_wgrad_a(d, X, dHpre, dA_s, accumulate), workspace, workspace_bytes, sc.cs),
+               &msg, "wgrad A"))
       return fail(DOMINO_ERR_HIP, msg);
   }
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
 }
 
+size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* d) {
+  if (check_attn_desc(d) != DOMINO_OK) return 0;
+  return ws_bytes_of({attn_qkv(d, nullptr, nullptr, nullptr), attn_out(d, nullptr, nullptr, nullptr, 0)});
+}
+
 domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
                                     void* QKV, void* O, void* Y_own, const void* const* peer_Y, void* Y,
-                                    hipStream_t compute, hipStream_t comm) {
+                                    void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
-  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
-  if (d->dtype != DOMINO_BF16) {
-    if (d->dtype == DOMINO_F32) return fail(DOMINO_ERR_UNSUPPORTED, "attention is bf16 only");
-    return fail(DOMINO_ERR_INVALID_ARG, "bad dtype");
-  }
-  if (d->batch < 0 || d->seq < 0 || d->hidden < 0 || d->heads < 0) return fail(DOMINO_ERR_SHAPE, "negative size");
-  if (d->head_dim != 128) return fail(DOMINO_ERR_UNSUPPORTED, "head_dim must be 128");
-  if (d->row_chunks < 1 || d->row_chunks > kMaxChunks) return fail(DOMINO_ERR_SHAPE, "bad row_chunks");
-  if (d->batch % d->row_chunks) return fail(DOMINO_ERR_SHAPE, "batch % row_chunks != 0");
-  if (d->n_partials < 1 || d->n_partials > DOMINO_MAX_PARTIALS)
-    return fail(DOMINO_ERR_INVALID_ARG, "n_partials must be in 1..DOMINO_MAX_PARTIALS");
-  if (d->hidden % 8) return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of 8");
-  if (!(d->scale >= 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "scale must be >= 0 (0 selects 1/sqrt(head_dim))");
+  domino_status st = check_attn_desc(d);
+  if (st != DOMINO_OK) return st;
   const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
-  if (T > (int64_t(1) << 31) || d->seq > (int64_t(1) << 30)) return fail(DOMINO_ERR_UNSUPPORTED, "too many tokens");
   if (T == 0 || h == 0) return DOMINO_OK;
   const bool red = needs_reduce(d->n_partials, Y_own, Y);
   const bool heads = d->heads > 0;
-  domino_status st;
   if ((st = check_ptr(X, "X", heads)) || (st = check_ptr(A_qkv_s, "A_qkv_s", heads)) ||
       (st = check_ptr(B_o_s, "B_o_s", heads)) || (st = check_ptr(QKV, "QKV", heads)) || (st = check_ptr(O, "O", heads)) ||
       (st = check_ptr(Y_own, "Y_own", true)) || (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) ||
       (st = check_ptr(Y ? Y : Y_own, "Y", red)))
     return st;
+  if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
   Sched sc;
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
   const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
-  const int64_t bc = d->batch / d->row_chunks, Tc = bc * d->seq;
+  const int64_t Tc = (d->batch / d->row_chunks) * d->seq;
   std::string msg;
   // QKV projection and attention feed no reduction: one launch each over all sequences.
   // The output projection runs per chunk (whole sequences) and each chunk's reduction
   // starts as soon as it ends.
   if (heads) {
-    GemmArgs gq{};
-    gq.M = T; gq.N = 3 * hd; gq.K = h;
-    gq.A = X; gq.lda = h; gq.a_kcontig = true;
-    gq.B = A_qkv_s; gq.ldb = 3 * hd; gq.b_kcontig = false;
-    gq.C = QKV; gq.ldc = 3 * hd;
-    gq.epi = Epi::kStore;
-    gq.bf16 = true;
     AttnArgs aa{};
     aa.qkv = QKV; aa.ld_qkv = 3 * hd;
     aa.o = O; aa.ld_o = hd;
     aa.batch = d->batch; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
     aa.scale = scale;
-    if (hip_ok(timed(DOMINO_K_QKV, sc.cs, [&] { return launch_gemm(gq, sc.cs, nullptr); }), &msg, "QKV GEMM") ||
+    if (hip_ok(run_gemm(DOMINO_K_QKV, attn_qkv(d, X, A_qkv_s, QKV), workspace, workspace_bytes, sc.cs), &msg,
+               "QKV GEMM") ||
         hip_ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), &msg, "attention"))
       return fail(DOMINO_ERR_HIP, msg);
   }
   for (int i = 0; i < d->row_chunks; ++i) {
-    const int64_t r0 = i * Tc;
-    GemmArgs go{};
-    go.M = Tc; go.N = h; go.K = hd;
-    go.A = static_cast<const char*>(O) + r0 * hd * 2; go.lda = hd; go.a_kcontig = true;
-    go.B = B_o_s; go.ldb = h; go.b_kcontig = false;
-    go.C = static_cast<char*>(Y_own) + r0 * h * 2; go.ldc = h;
-    go.epi = Epi::kStore;
-    go.bf16 = true;
-    if (hip_ok(timed(DOMINO_K_OUTPROJ, sc.cs, [&] { return launch_gemm(go, sc.cs, nullptr); }), &msg, "out-projection"))
+    if (hip_ok(run_gemm(DOMINO_K_OUTPROJ, attn_out(d, O, B_o_s, Y_own, i), workspace, workspace_bytes, sc.cs), &msg,
+               "out-projection"))
       return fail(DOMINO_ERR_HIP, msg);
-    if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, r0 * h, Tc, h, DOMINO_BF16), &msg,
+    if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, i * Tc * h, Tc, h, DOMINO_BF16), &msg,
                       "reduce Y"))
       return fail(DOMINO_ERR_HIP, msg);
   }

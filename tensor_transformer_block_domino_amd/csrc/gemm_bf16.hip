@@ -28,6 +28,7 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile index is remapped
 //    so each XCD gets a contiguous, M-grouped range of tiles that share operand rows in
 //    its L2.
+#include <algorithm>
 #include <cstdio>
 #include <type_traits>
 
@@ -187,11 +188,25 @@ struct KParams {
   void* C; int64_t ldc;
   uint16_t* C2; int64_t ldc2;
   const uint16_t* aux; int64_t ldaux;
-  float* ws;
+  float* ws;             // k-split tiles' fp32 slices: [tile − dp_tiles][split][BM][BN]
   int64_t M, N, K, f_s;
-  int tiles_m, tiles_n, splits, kt_per_split;
+  int tiles_m, tiles_n;
+  int dp_tiles;          // tiles 0 .. dp_tiles−1 run whole, with the fused epilogue
+  int splits;            // k-slices of each remaining tile
+  int kt_per_split;      // k-steps (of BK) per slice
   int accumulate;
 };
+
+// Tile t → (tile row, tile column): groups of 8 tile rows, column-major inside a group, so
+// consecutive tiles share rows of A.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kGroup = 8;
+  const int per_group = kGroup * tiles_n;
+  const int first_m = (t / per_group) * kGroup;
+  const int gsize = min(tiles_m - first_m, kGroup);
+  tm = first_m + (t % per_group) % gsize;
+  tn = (t % per_group) / gsize;
+}
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
   *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
@@ -215,7 +230,7 @@ __device__ __forceinline__ AuxQuad load_aux4(const KParams& p, int64_t m, int64_
 
 // Epilogue for 4 consecutive output columns n..n+3 of row m (n < N, all four in range).
 template <Epi kEpi>
-__device__ __forceinline__ void epilogue4(const KParams& p, int split, int64_t m, int64_t n, f32x4_t v,
+__device__ __forceinline__ void epilogue4(const KParams& p, int64_t m, int64_t n, f32x4_t v,
                                           const AuxQuad& ax) {
   if constexpr (kEpi == Epi::kStore) {
     store_bf16x4(static_cast<uint16_t*>(p.C) + m * p.ldc + n, v.x, v.y, v.z, v.w);
@@ -243,12 +258,8 @@ __device__ __forceinline__ void epilogue4(const KParams& p, int split, int64_t m
     store_bf16x4(dp + n, dg[0], dg[1], dg[2], dg[3]);
     store_bf16x4(dp + p.f_s + n, du[0], du[1], du[2], du[3]);
   } else if constexpr (kEpi == Epi::kF32) {
-    if (p.splits > 1) {
-      *reinterpret_cast<f32x4_t*>(p.ws + int64_t(split) * p.M * p.N + m * p.N + n) = v;
-    } else {
-      f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + m * p.ldc + n);
-      *dst = p.accumulate ? (*dst + v) : v;
-    }
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + m * p.ldc + n);
+    *dst = p.accumulate ? (*dst + v) : v;
   }
 }
 
@@ -277,28 +288,34 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Tile index: XCD-contiguous remap, then M-grouped order within the range.
-  int bid = blockIdx.x;
-  const int nwg = gridDim.x, full = (nwg / 8) * 8;
-  if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+  // Work item. Blocks 0 .. dp_tiles−1 compute whole tiles; the rest compute one k-slice of
+  // one of the remaining tiles, slice-major. Workgroups are dispatched round-robin over
+  // the 8 XCDs, so each range is remapped to give every XCD a contiguous run of items
+  // (neighbouring tiles share operand rows in that XCD's L2).
+  const int kt_total = int((p.K + BK - 1) / BK);
   const int tiles = p.tiles_m * p.tiles_n;
-  const int split = bid / tiles;
-  const int t = bid - split * tiles;
-  constexpr int kGroup = 8;
-  const int per_group = kGroup * p.tiles_n;
-  const int first_m = (t / per_group) * kGroup;
-  const int gsize = min(p.tiles_m - first_m, kGroup);
-  const int tm = first_m + (t % per_group) % gsize;
-  const int tn = (t % per_group) / gsize;
+  const bool part = int(blockIdx.x) >= p.dp_tiles;
+  int t, split = 0, kt_begin = 0, kt_end = kt_total;
+  if (!part) {
+    const int full = (p.dp_tiles / 8) * 8;
+    const int b = blockIdx.x;
+    t = b < full ? (b % 8) * (full / 8) + b / 8 : b;
+  } else {
+    const int rest = tiles - p.dp_tiles, items = rest * p.splits, full = (items / 8) * 8;
+    const int b = blockIdx.x - p.dp_tiles;
+    const int u = b < full ? (b % 8) * (full / 8) + b / 8 : b;
+    split = u / rest;
+    t = p.dp_tiles + (u - split * rest);
+    kt_begin = split * p.kt_per_split;
+    kt_end = min(kt_total, kt_begin + p.kt_per_split);
+  }
+  int tm, tn;
+  tile_coords(t, p.tiles_m, p.tiles_n, tm, tn);
 
   const int64_t m0 = int64_t(tm) * BM;
   const int64_t n0 = kSw ? int64_t(tn) * (BN / 2) : int64_t(tn) * BN;
   const RowMap rmA{m0, p.M, 0};
   const RowMap rmB{n0, kSw ? p.f_s : p.N, p.f_s};
-
-  const int kt_total = int((p.K + BK - 1) / BK);
-  const int kt_begin = split * p.kt_per_split;
-  const int kt_end = min(kt_total, kt_begin + p.kt_per_split);
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -389,6 +406,25 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 
   // Epilogue. With the operands swapped, lane l holds, for block (i, j) and q = 0..3,
   // C[m][n .. n+3] with m = row0 + l%32 and n = col0 + 8q + 4·(l/32).
+  if (part) {
+    // A k-slice: raw fp32 sums into this slice's [BM][BN] slot, by tile-local output
+    // column (for SwiGLU: FFN columns 0..BN/2−1 hold gate, BN/2.. the matching up).
+    float* slot = p.ws + (int64_t(t - p.dp_tiles) * p.splits + split) * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float* row = slot + (wm * WM + i * 32 + (lane & 31)) * BN;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = kSw ? (j < TN / 2 ? 0 : BN / 2 - TN / 2 * 32) + wn * (BN / 4) + j * 32 + q * 8 + 4 * (lane >> 5)
+                            : wn * WN + j * 32 + q * 8 + 4 * (lane >> 5);
+          *reinterpret_cast<f32x4_t*>(row + c) =
+              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t m = m0 + wm * WM + i * 32 + (lane & 31);
@@ -421,9 +457,40 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           const int64_t n = n0 + wn * WN + j * 32 + q * 8 + 4 * (lane >> 5);
           if (n >= p.N) continue;
           const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epilogue4<kEpi>(p, split, m, n, v, ax[j][q]);
+          epilogue4<kEpi>(p, m, n, v, ax[j][q]);
         }
     }
+  }
+}
+
+// Finishes the k-split tiles: sums each tile's slices in slice order (a fixed order, so the
+// result does not depend on which workgroup ran first) and applies the product's epilogue.
+template <int BM, int BN, Epi kEpi>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(KParams p) {
+  constexpr bool kSw = kEpi == Epi::kSwiglu;
+  constexpr int kCols = kSw ? BN / 2 : BN;  // output columns of a tile (FFN columns for SwiGLU)
+  constexpr int kQuads = kCols / 4;
+  constexpr int kRows = 256 / kQuads;       // tile rows per workgroup
+  constexpr int kPerTile = BM / kRows;
+  static_assert(256 % kQuads == 0 && BM % kRows == 0, "fixup thread layout");
+  const int tt = blockIdx.x / kPerTile;
+  const int r = (blockIdx.x - tt * kPerTile) * kRows + threadIdx.x / kQuads;
+  const int c = (threadIdx.x % kQuads) * 4;
+  int tm, tn;
+  tile_coords(p.dp_tiles + tt, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m = int64_t(tm) * BM + r;
+  if (m >= p.M) return;
+  const float* src = p.ws + int64_t(tt) * p.splits * (BM * BN) + r * BN + c;
+  f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
+  for (int z = 1; z < p.splits; ++z) v += *reinterpret_cast<const f32x4_t*>(src + int64_t(z) * (BM * BN));
+  if constexpr (kSw) {
+    f32x4_t u = *reinterpret_cast<const f32x4_t*>(src + BN / 2);
+    for (int z = 1; z < p.splits; ++z) u += *reinterpret_cast<const f32x4_t*>(src + int64_t(z) * (BM * BN) + BN / 2);
+    const int64_t j = int64_t(tn) * (BN / 2) + c;
+    if (j < p.f_s) epilogue_swiglu4(p, m, j, v, u);
+  } else {
+    const int64_t n = int64_t(tn) * BN + c;
+    if (n < p.N) epilogue4<kEpi>(p, m, n, v, load_aux4<kEpi>(p, m, n));
   }
 }
 
@@ -459,6 +526,21 @@ hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <Epi kEpi>
+hipError_t dispatch_fixup(int ti, const KParams& kp, int rest, hipStream_t s) {
+  const TileCfg& tc = kTiles[ti];
+  char name[64];
+  snprintf(name, sizeof name, "gemm_fixup_kernel<%d, %d, (domino::Epi)%d>", tc.bm, tc.bn, int(kEpi));
+  note_kernel(name);
+  const int cols = kEpi == Epi::kSwiglu ? tc.bn / 2 : tc.bn;
+  const int blocks = rest * (tc.bm / (256 / (cols / 4)));
+  if (tc.bm == 128 && tc.bn == 128)
+    hipLaunchKernelGGL((gemm_fixup_kernel<128, 128, kEpi>), dim3(blocks), dim3(256), 0, s, kp);
+  else
+    hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, kEpi>), dim3(blocks), dim3(256), 0, s, kp);
+  return hipGetLastError();
+}
+
 // Neff: output columns (FFN column pairs for the SwiGLU forward, whose 256-wide tile holds
 // 128 pairs).
 int choose_tile(int64_t M, int64_t Neff, int64_t K, bool a_kcontig, bool b_kcontig, bool swiglu) {
@@ -469,51 +551,92 @@ int choose_tile(int64_t M, int64_t Neff, int64_t K, bool a_kcontig, bool b_kcont
   return 1;
 }
 
-}  // namespace
+// The launch plan of one product: its tile configuration, the tiles computed whole, and
+// the k-split of the rest.
+struct Plan {
+  int ti, tiles_m, tiles_n, dp_tiles, splits, kt_per_split;
+  int64_t ws_elems;  // fp32 slots the k-split tiles need
+};
 
-int64_t gemm_splitk_ws_elems(int64_t M, int64_t N, int64_t K) {
-  // Split-K applies to the weight gradients (both operands transposed) whose output grid
-  // fills less than 3/4 of one round of workgroups: the largest split that still fits in
-  // one round (each split keeping at least 1024 of k).
-  const TileCfg& tc = kTiles[choose_tile(M, N, K, false, false, false)];
-  const int64_t slots = 256 * tc.occ;
-  const int64_t tiles = ((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
-  if (tiles * 4 >= slots * 3) return 0;
-  int64_t splits = 1;
-  for (int64_t sp = 2; sp <= 8; ++sp)
-    if (tiles * sp <= slots && K / sp >= 1024) splits = sp;
-  return splits > 1 ? splits * M * N : 0;
+constexpr int64_t kMinSliceK = 512;  // k per slice of a split tile, at least
+
+Plan make_plan(const GemmArgs& g) {
+  const bool sw = g.epi == Epi::kSwiglu;
+  Plan pl{};
+  pl.ti = choose_tile(g.M, g.N, g.K, g.a_kcontig, g.b_kcontig, sw);
+  const TileCfg& tc = kTiles[pl.ti];
+  const int64_t bn_cols = sw ? tc.bn / 2 : tc.bn;
+  pl.tiles_m = int((g.M + tc.bm - 1) / tc.bm);
+  pl.tiles_n = int((g.N + bn_cols - 1) / bn_cols);
+  const int tiles = pl.tiles_m * pl.tiles_n;
+  const int kt_total = int((g.K + tc.bk - 1) / tc.bk);
+  pl.dp_tiles = tiles;
+  pl.splits = 1;
+  pl.kt_per_split = kt_total;
+  pl.ws_elems = 0;
+  // Whole rounds of the 256·occ resident workgroups run whole tiles. When the tiles left
+  // over would fill at most 3/4 of a last round, they are split along k so that their
+  // slices fill that round instead (each slice keeping at least kMinSliceK of k).
+  const int slots = 256 * tc.occ;
+  const int rest = tiles % slots;
+  if (rest == 0 || rest * 4 > slots * 3) return pl;
+  int sp = slots / rest;
+  sp = std::min<int64_t>(sp, std::min<int64_t>(16, g.K / kMinSliceK));
+  if (sp < 2) return pl;
+  pl.kt_per_split = (kt_total + sp - 1) / sp;
+  pl.splits = (kt_total + pl.kt_per_split - 1) / pl.kt_per_split;  // no empty slice
+  if (pl.splits < 2) {
+    pl.kt_per_split = kt_total;
+    pl.splits = 1;
+    return pl;
+  }
+  pl.dp_tiles = tiles - rest;
+  pl.ws_elems = int64_t(rest) * pl.splits * tc.bm * tc.bn;
+  return pl;
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* splits_out) {
-  const bool sw = g.epi == Epi::kSwiglu;
-  const int ti = choose_tile(g.M, g.N, g.K, g.a_kcontig, g.b_kcontig, sw);
-  const TileCfg& tc = kTiles[ti];
+KParams make_params(const GemmArgs& g, const Plan& pl) {
   KParams kp{};
   kp.A = static_cast<const uint16_t*>(g.A); kp.lda = g.lda;
   kp.B = static_cast<const uint16_t*>(g.B); kp.ldb = g.ldb;
   kp.C = g.C; kp.ldc = g.ldc;
   kp.C2 = static_cast<uint16_t*>(g.C2); kp.ldc2 = g.ldc2;
   kp.aux = static_cast<const uint16_t*>(g.aux); kp.ldaux = g.ldaux;
-  kp.M = g.M; kp.N = g.N; kp.K = g.K; kp.f_s = g.f_s;
-  kp.accumulate = g.accumulate;
-  const int64_t bn_cols = sw ? tc.bn / 2 : tc.bn;
-  kp.tiles_m = int((g.M + tc.bm - 1) / tc.bm);
-  kp.tiles_n = int((g.N + bn_cols - 1) / bn_cols);
-  const int kt_total = int((g.K + tc.bk - 1) / tc.bk);
-  int splits = 1;
-  if (g.epi == Epi::kF32 && g.ws) {
-    const int64_t need = gemm_splitk_ws_elems(g.M, g.N, g.K);
-    if (need && need <= g.ws_elems) splits = int(need / (g.M * g.N));
-  }
-  kp.splits = splits;
-  kp.kt_per_split = (kt_total + splits - 1) / splits;
   kp.ws = g.ws;
-  const int blocks = kp.tiles_m * kp.tiles_n * splits;
-  if (splits_out) *splits_out = 1;
+  kp.M = g.M; kp.N = g.N; kp.K = g.K; kp.f_s = g.f_s;
+  kp.tiles_m = pl.tiles_m; kp.tiles_n = pl.tiles_n;
+  kp.dp_tiles = pl.dp_tiles; kp.splits = pl.splits; kp.kt_per_split = pl.kt_per_split;
+  kp.accumulate = g.accumulate;
+  return kp;
+}
+
+// The plan a launch with this workspace uses: without room for the slices, every tile
+// runs whole.
+Plan plan_for(const GemmArgs& g) {
+  Plan pl = make_plan(g);
+  if (pl.splits > 1 && (!g.ws || g.ws_elems < pl.ws_elems)) {
+    pl.dp_tiles = pl.tiles_m * pl.tiles_n;
+    pl.splits = 1;
+    pl.kt_per_split = int((g.K + kTiles[pl.ti].bk - 1) / kTiles[pl.ti].bk);
+    pl.ws_elems = 0;
+  }
+  return pl;
+}
+
+}  // namespace
+
+int64_t gemm_bf16_ws_elems(const GemmArgs& g) { return make_plan(g).ws_elems; }
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, GemmSplit* split) {
+  const Plan pl = plan_for(g);
+  const KParams kp = make_params(g, pl);
+  const int tiles = pl.tiles_m * pl.tiles_n;
+  const int blocks = pl.dp_tiles + (tiles - pl.dp_tiles) * pl.splits;
+  if (split) *split = GemmSplit{};
   if (blocks == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   const bool ak = g.a_kcontig, bk = g.b_kcontig;
+  const int ti = pl.ti;
   switch (g.epi) {
     case Epi::kStore:
       if (ak && !bk) e = dispatch_tile<true, false, Epi::kStore>(ti, kp, blocks, s);
@@ -536,8 +659,36 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* splits_out) {
       e = (!ak && !bk) ? dispatch_tile<false, false, Epi::kF32>(ti, kp, blocks, s) : hipErrorInvalidValue;
       break;
   }
-  if (splits_out) *splits_out = splits;
+  if (e == hipSuccess && split && pl.splits > 1) {
+    split->pending = 1;
+    split->tile = pl.ti;
+    split->tiles_m = pl.tiles_m;
+    split->tiles_n = pl.tiles_n;
+    split->dp_tiles = pl.dp_tiles;
+    split->splits = pl.splits;
+  }
   return e;
+}
+
+hipError_t launch_gemm_bf16_fixup(const GemmArgs& g, const GemmSplit& sp, hipStream_t s) {
+  if (!sp.pending) return hipSuccess;
+  Plan pl{};
+  pl.ti = sp.tile;
+  pl.tiles_m = sp.tiles_m;
+  pl.tiles_n = sp.tiles_n;
+  pl.dp_tiles = sp.dp_tiles;
+  pl.splits = sp.splits;
+  const KParams kp = make_params(g, pl);
+  const int rest = sp.tiles_m * sp.tiles_n - sp.dp_tiles;
+  switch (g.epi) {
+    case Epi::kStore: return dispatch_fixup<Epi::kStore>(sp.tile, kp, rest, s);
+    case Epi::kGelu: return dispatch_fixup<Epi::kGelu>(sp.tile, kp, rest, s);
+    case Epi::kSwiglu: return dispatch_fixup<Epi::kSwiglu>(sp.tile, kp, rest, s);
+    case Epi::kDGelu: return dispatch_fixup<Epi::kDGelu>(sp.tile, kp, rest, s);
+    case Epi::kDSwiglu: return dispatch_fixup<Epi::kDSwiglu>(sp.tile, kp, rest, s);
+    case Epi::kF32: return dispatch_fixup<Epi::kF32>(sp.tile, kp, rest, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace domino

@@ -7,7 +7,9 @@
 
 namespace domino {
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, int* splits_out);
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, GemmSplit* split);
+hipError_t launch_gemm_bf16_fixup(const GemmArgs& g, const GemmSplit& split, hipStream_t s);
+int64_t gemm_bf16_ws_elems(const GemmArgs& g);
 
 namespace {
 
@@ -185,10 +187,16 @@ hipError_t launch_fill_zero_f32(float* out, int64_t ld, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* splits_out) {
-  if (splits_out) *splits_out = 1;
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, GemmSplit* split) {
+  if (split) *split = GemmSplit{};
   int launches = 0;
-  return g.bf16 ? launch_gemm_bf16(g, s, splits_out) : launch_gemm_f32_path(g, s, &launches);
+  return g.bf16 ? launch_gemm_bf16(g, s, split) : launch_gemm_f32_path(g, s, &launches);
 }
+
+hipError_t launch_gemm_fixup(const GemmArgs& g, const GemmSplit& split, hipStream_t s) {
+  return g.bf16 ? launch_gemm_bf16_fixup(g, split, s) : hipSuccess;
+}
+
+int64_t gemm_ws_elems(const GemmArgs& g) { return g.bf16 ? gemm_bf16_ws_elems(g) : 0; }
 
 }  // namespace domino

@@ -23,8 +23,6 @@ struct ReduceArgs {
   bool bf16;
 };
 hipError_t launch_shard_reduce(const ReduceArgs& a, hipStream_t s);
-hipError_t launch_splitk_sum(float* out, int64_t ldc, const float* ws, int splits, int64_t rows, int64_t cols,
-                             int accumulate, hipStream_t s);
 hipError_t launch_fill_zero_f32(float* out, int64_t ld, int64_t rows, int64_t cols, hipStream_t s);
 
 // GEMM epilogues. C(m, n) = Σ_k A(m, k)·B(k, n), accumulated in fp32.
@@ -47,16 +45,22 @@ struct GemmArgs {
   int64_t f_s;                // gate/up offset for kSwiglu / kDSwiglu
   Epi epi;
   int accumulate;             // kF32
-  float* ws;                  // kF32 split-K slices [splits][M][N]; null disables split-K
+  float* ws;                  // fp32 slices of k-split tiles; null: every tile runs whole
   int64_t ws_elems;           // capacity of ws in floats
   bool bf16;                  // operand dtype: bf16 (MFMA path) or fp32 (vector-ALU path)
 };
-// Launches the product. With split-K (weight gradients with a workspace), the kernel
-// writes fp32 slices to g.ws and *splits_out > 1: the caller then launches
-// launch_splitk_sum(g.C, g.ldc, g.ws, *splits_out, g.M, g.N, g.accumulate).
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, int* splits_out);
-// Number of float slots a split-K launch of this GEMM would use (0 = no split).
-int64_t gemm_splitk_ws_elems(int64_t M, int64_t N, int64_t K);
+
+// Set by launch_gemm when the product left k-split tiles for launch_gemm_fixup, which the
+// caller launches next on the same stream (it sums their slices and applies the epilogue).
+struct GemmSplit {
+  int pending = 0;
+  int tile = 0, tiles_m = 0, tiles_n = 0, dp_tiles = 0, splits = 1;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, GemmSplit* split);
+hipError_t launch_gemm_fixup(const GemmArgs& g, const GemmSplit& split, hipStream_t s);
+// Floats of workspace the product's k-split tiles use (0: it splits none); shapes, layouts
+// and epilogue of g are read, its pointers are not.
+int64_t gemm_ws_elems(const GemmArgs& g);
 
 struct AttnArgs {
   const void* qkv; int64_t ld_qkv;   // [T, 3·H·d] = [Q | K | V]

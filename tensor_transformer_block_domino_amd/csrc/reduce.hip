@@ -125,35 +125,4 @@ hipError_t launch_shard_reduce(const ReduceArgs& a, hipStream_t s) {
   return a.bf16 ? launch_reduce_t<uint16_t>(a, s) : launch_reduce_t<float>(a, s);
 }
 
-// out[m, n] = (accumulate ? out[m, n] : 0) + Σ_z ws[z][m, n], z = 0..splits−1 in order:
-// the fixed-order sum of split-K weight-gradient slices (deterministic).
-__global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ out, int64_t ldc,
-                                                         const float* __restrict__ ws, int64_t slice,
-                                                         int splits, uint32_t rows, uint32_t cols4,
-                                                         int accumulate) {
-  const uint32_t total = rows * cols4;
-  for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += gridDim.x * blockDim.x) {
-    const uint32_t r = g / cols4, c = (g - r * cols4) * 4;
-    f32x4_t acc = accumulate ? *reinterpret_cast<const f32x4_t*>(out + int64_t(r) * ldc + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float* src = ws + int64_t(r) * (int64_t(cols4) * 4) + c;
-    for (int z = 0; z < splits; ++z) {
-      acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + z * slice));
-    }
-    *reinterpret_cast<f32x4_t*>(out + int64_t(r) * ldc + c) = acc;
-  }
-}
-
-hipError_t launch_splitk_sum(float* out, int64_t ldc, const float* ws, int splits, int64_t rows, int64_t cols,
-                             int accumulate, hipStream_t s) {
-  const uint32_t cols4 = uint32_t(cols / 4);
-  const uint32_t total = uint32_t(rows) * cols4;
-  if (!total) return hipSuccess;
-  const uint32_t want = (total + 255) / 256;
-  const uint32_t blocks = want < 2048u ? want : 2048u;
-  note_kernel("splitk_sum_kernel");
-  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, out, ldc, ws, rows * cols, splits,
-                     uint32_t(rows), cols4, accumulate);
-  return hipGetLastError();
-}
-
 }  // namespace domino

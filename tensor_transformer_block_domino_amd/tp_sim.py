@@ -79,9 +79,12 @@ class MlpGroup:
             self.dX = torch.empty(T, h, **e)
             self.dA = torch.zeros(h, n1, device=device, dtype=torch.float32)
             self.dB = torch.zeros(f, h, device=device, dtype=torch.float32)
-            nbytes = L.domino_block_bwd_workspace_size(self.desc())
-            self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-            self.ws_bytes = nbytes
+        # One workspace for every call this group makes: the split as configured and the
+        # unsplit (peer and comparison) calls.
+        descs = [self.desc(), self.desc(rank_alone=True, row_chunks=1, col_chunks=1)]
+        nbytes = max(max(L.domino_block_fwd_workspace_size(d), L.domino_block_bwd_workspace_size(d)) for d in descs)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        self.ws_bytes = nbytes
 
     def desc(self, *, rank_alone=False, row_chunks=None, col_chunks=None, no_join=0) -> L.MlpDesc:
         return L.MlpDesc(batch=self.batch, seq=self.seq, hidden=self.hidden, ffn_shard=self.f,
@@ -95,7 +98,8 @@ class MlpGroup:
     def peer_forward(self, stream=None):
         for r in self.ranks[1:]:
             L.domino_block_fwd(self.desc(rank_alone=True, row_chunks=1, col_chunks=1), self.X, self.A_s[r],
-                               self.B_s[r], self.Hpre[r], self.H[r], self.Y_own[r], None, None, stream, None)
+                               self.B_s[r], self.Hpre[r], self.H[r], self.Y_own[r], None, None, self.ws,
+                               self.ws_bytes, stream, None)
 
     def peer_backward(self, stream=None):
         dA = torch.empty_like(self.dA)
@@ -112,7 +116,7 @@ class MlpGroup:
     def forward(self, compute=None, comm=None, **desc_kw):
         r = self.ranks[0]
         L.domino_block_fwd(self.desc(**desc_kw), self.X, self.A_s[r], self.B_s[r], self.Hpre[r], self.H[r],
-                           self.Y_own[r], self.peers(self.Y_own), self.Y, compute, comm)
+                           self.Y_own[r], self.peers(self.Y_own), self.Y, self.ws, self.ws_bytes, compute, comm)
 
     def backward(self, compute=None, comm=None, accumulate=0, **desc_kw):
         r = self.ranks[0]
@@ -142,6 +146,10 @@ class AttnGroup:
         self.O = {r: torch.empty(self.T, hd, **e) for r in range(n_partials)}
         self.Y_own = {r: torch.empty(self.T, hidden, **e) for r in range(n_partials)}
         self.Y = torch.empty(self.T, hidden, **e)
+        nbytes = max(L.domino_attn_block_fwd_workspace_size(d)
+                     for d in (self.desc(), self.desc(rank_alone=True, row_chunks=1)))
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        self.ws_bytes = nbytes
 
     def desc(self, *, rank_alone=False, row_chunks=None, no_join=0) -> L.AttnDesc:
         return L.AttnDesc(batch=self.batch, seq=self.seq, hidden=self.hidden, heads=self.hs, head_dim=self.d,
@@ -152,9 +160,10 @@ class AttnGroup:
     def peer_forward(self, stream=None):
         for r in range(1, self.P):
             L.domino_attn_block_fwd(self.desc(rank_alone=True, row_chunks=1), self.X, self.A_s[r], self.B_s[r],
-                                    self.QKV[r], self.O[r], self.Y_own[r], None, None, stream, None)
+                                    self.QKV[r], self.O[r], self.Y_own[r], None, None, self.ws, self.ws_bytes,
+                                    stream, None)
 
     def forward(self, compute=None, comm=None, **desc_kw):
         peers = [self.Y_own[r] for r in range(1, self.P)] if self.P > 1 else None
         L.domino_attn_block_fwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
-                                self.Y_own[0], peers, self.Y, compute, comm)
+                                self.Y_own[0], peers, self.Y, self.ws, self.ws_bytes, compute, comm)

@@ -138,7 +138,7 @@ def test_edge_empty_batch_is_noop():
     d = dev()
     desc = D.MlpDesc(batch=0, seq=128, hidden=64, ffn_shard=64, act=0, dtype=1, row_chunks=1, col_chunks=1,
                      n_partials=2, no_join=0)
-    D.domino_block_fwd(desc, None, None, None, None, None, None, None, None, None, torch.cuda.Stream())
+    D.domino_block_fwd(desc, None, None, None, None, None, None, None, None, comm=torch.cuda.Stream())
     sync()
 
 
@@ -148,8 +148,8 @@ def test_edge_n_partials_one_in_place():
     inp = synth.mlp_inputs(w)
     g = make_group(w, inp)
     d = g.desc()
-    D.domino_block_fwd(d, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, None,
-                       torch.cuda.Stream())
+    D.domino_block_fwd(d, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, g.ws, g.ws_bytes,
+                       comm=torch.cuda.Stream())
     sync()
     X, A, B = (oracle.to_f64(inp[k]) for k in ("X", "A", "B"))
     check("Y_own", f64(g.Y_own[0]), oracle.mlp_forward_unsharded(X, A, B, "gelu_tanh"), BF16_TOL)
