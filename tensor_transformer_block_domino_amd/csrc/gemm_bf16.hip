@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           const f32x4_t u = {ua[4 * q], ua[4 * q + 1], ua[4 * q + 2], ua[4 * q + 3]};
           epilogue_swiglu4(p, m, jj, g, u);
         }
-    } else {
+    } else if constexpr (kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu) {
       AuxQuad ax[TN][4];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -458,6 +458,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
           if (n >= p.N) continue;
           const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           epilogue4<kEpi>(p, m, n, v, ax[j][q]);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = n0 + wn * WN + j * 32 + q * 8 + 4 * (lane >> 5);
+          if (n >= p.N) continue;
+          const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epilogue4<kEpi>(p, m, n, v, AuxQuad{});
         }
     }
   }
@@ -499,17 +509,26 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(KParams p) {
 struct TileCfg {
   int bm, bn, bk, ns, occ;
 };
-// Three configurations, chosen by shape (measured on the MLP and attention products):
-// the 256×256 tile has the least LDS and L2 traffic per FLOP and wins when there are at
-// least two rounds of such tiles and a long k loop; smaller grids fill the GPU better
-// with 128×128 tiles at two or three workgroups per CU, whose resident workgroups also
-// hide each other's memory latency.
+// Per-CU rates on gfx950, measured in shader cycles: global→LDS copies 64 B/clk, LDS
+// ds_read_b128 ~158 B/clk, ds_read_b64_tr_b16 ~103 B/clk, LDS writes ~75 B/clk, one
+// 32×32×16 MFMA per 32 cycles per SIMD. At the MFMA rate a 128×128 tile needs all 64 B/clk
+// of copies and more LDS time than there is; 256-wide tiles halve both per FLOP but cut
+// the number of tiles, which small products need to fill 256 CUs.
+enum TileId { kT128 = 0, kT128o3 = 1, kT256 = 2, kT256x128 = 3, kT128x256 = 4 };
 constexpr TileCfg kTiles[] = {
     {128, 128, 64, 2, 2},  // 64 KB LDS, 2 workgroups per CU
     {128, 128, 32, 3, 3},  // 48 KB LDS, 3 per CU
     {256, 256, 64, 2, 1},  // 128 KB LDS, 1 per CU
+    {256, 128, 32, 3, 2},  // 72 KB LDS, 2 per CU
+    {128, 256, 32, 3, 2},  // 72 KB LDS, 2 per CU
 };
 
+template <int BM, int BN, int BK, int NS, int kOcc, bool kAK, bool kBKc, Epi kEpi>
+void launch_tile(const KParams& kp, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, kOcc, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
+}
+
+// Each operand layout is built only with the tiles make_plan can choose for it.
 template <bool kAK, bool kBKc, Epi kEpi>
 hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
   const TileCfg& tc = kTiles[ti];
@@ -517,38 +536,65 @@ hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
   snprintf(name, sizeof name, "gemm_bf16_kernel<%d, %d, %d, %d, %d, %s, %s, (domino::Epi)%d>", tc.bm, tc.bn, tc.bk,
            tc.ns, tc.occ, kAK ? "true" : "false", kBKc ? "true" : "false", int(kEpi));
   note_kernel(name);
-  if (ti == 0)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 64, 2, 2, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
-  else if (ti == 1)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 32, 3, 3, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 64, 2, 1, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
+  if constexpr (kAK && !kBKc) {  // forward products: the [in, out] weight is n-major
+    if (ti == kT128x256) launch_tile<128, 256, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s);
+    else if (ti == kT128o3) launch_tile<128, 128, 32, 3, 3, kAK, kBKc, kEpi>(kp, blocks, s);
+    else return hipErrorInvalidValue;
+  } else if constexpr (kAK && kBKc) {  // input gradients: both operands k-contiguous
+    if (ti == kT128) {
+      launch_tile<128, 128, 64, 2, 2, kAK, kBKc, kEpi>(kp, blocks, s);
+    } else {
+      if constexpr (kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu) {
+        return hipErrorInvalidValue;  // epilogues reading the saved activation: 128×128 only
+      } else {
+        if (ti != kT256) return hipErrorInvalidValue;
+        launch_tile<256, 256, 64, 2, 1, kAK, kBKc, kEpi>(kp, blocks, s);
+      }
+    }
+  } else {  // weight gradients: both operands m/n-major
+    switch (ti) {
+      case kT128: launch_tile<128, 128, 64, 2, 2, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      case kT128o3: launch_tile<128, 128, 32, 3, 3, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      case kT256: launch_tile<256, 256, 64, 2, 1, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      case kT256x128: launch_tile<256, 128, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      case kT128x256: launch_tile<128, 256, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
+template <int BM, int BN, Epi kEpi>
+void launch_fixup(const KParams& kp, int rest, hipStream_t s) {
+  constexpr int kCols = kEpi == Epi::kSwiglu ? BN / 2 : BN;
+  constexpr int kPerTile = BM / (256 / (kCols / 4));
+  hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, kEpi>), dim3(rest * kPerTile), dim3(256), 0, s, kp);
+}
+
+// k-split tiles occur for input gradients (tiles kT128, kT256) and weight gradients (any
+// tile); forward products never split.
 template <Epi kEpi>
 hipError_t dispatch_fixup(int ti, const KParams& kp, int rest, hipStream_t s) {
   const TileCfg& tc = kTiles[ti];
   char name[64];
   snprintf(name, sizeof name, "gemm_fixup_kernel<%d, %d, (domino::Epi)%d>", tc.bm, tc.bn, int(kEpi));
   note_kernel(name);
-  const int cols = kEpi == Epi::kSwiglu ? tc.bn / 2 : tc.bn;
-  const int blocks = rest * (tc.bm / (256 / (cols / 4)));
-  if (tc.bm == 128 && tc.bn == 128)
-    hipLaunchKernelGGL((gemm_fixup_kernel<128, 128, kEpi>), dim3(blocks), dim3(256), 0, s, kp);
-  else
-    hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, kEpi>), dim3(blocks), dim3(256), 0, s, kp);
+  if constexpr (kEpi == Epi::kF32) {
+    if (tc.bm == 128 && tc.bn == 128) launch_fixup<128, 128, kEpi>(kp, rest, s);
+    else if (tc.bm == 256 && tc.bn == 256) launch_fixup<256, 256, kEpi>(kp, rest, s);
+    else if (tc.bm == 256 && tc.bn == 128) launch_fixup<256, 128, kEpi>(kp, rest, s);
+    else launch_fixup<128, 256, kEpi>(kp, rest, s);
+  } else if constexpr (kEpi == Epi::kStore) {
+    if (ti == kT256) launch_fixup<256, 256, kEpi>(kp, rest, s);
+    else if (ti == kT128) launch_fixup<128, 128, kEpi>(kp, rest, s);
+    else return hipErrorInvalidValue;
+  } else if constexpr (kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu) {
+    if (ti == kT128) launch_fixup<128, 128, kEpi>(kp, rest, s);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
-}
-
-// Neff: output columns (FFN column pairs for the SwiGLU forward, whose 256-wide tile holds
-// 128 pairs).
-int choose_tile(int64_t M, int64_t Neff, int64_t K, bool a_kcontig, bool b_kcontig, bool swiglu) {
-  const int64_t bn = swiglu ? 128 : 256;
-  const int64_t big_tiles = ((M + 255) / 256) * ((Neff + bn - 1) / bn);
-  if (big_tiles >= 2 * 256 && K >= 1024) return 2;
-  if (a_kcontig && b_kcontig) return 0;  // input gradients (both operands k-contiguous)
-  return 1;
 }
 
 // The launch plan of one product: its tile configuration, the tiles computed whole, and
@@ -558,12 +604,67 @@ struct Plan {
   int64_t ws_elems;  // fp32 slots the k-split tiles need
 };
 
+constexpr int kCUs = 256;
 constexpr int64_t kMinSliceK = 512;  // k per slice of a split tile, at least
+
+int tile_count(const TileCfg& tc, int64_t M, int64_t N, bool sw) {
+  const int64_t bn = sw ? tc.bn / 2 : tc.bn;
+  return int(((M + tc.bm - 1) / tc.bm) * ((N + bn - 1) / bn));
+}
+
+// Slices per leftover tile when the tiles beyond whole rounds of the 256·occ resident
+// workgroups would fill at most 3/4 of a last round: enough to fill that round, each
+// slice keeping at least kMinSliceK of k (1: no split).
+int fill_split(int tiles, const TileCfg& tc, int64_t K) {
+  const int slots = kCUs * tc.occ, rest = tiles % slots;
+  if (rest == 0 || rest * 4 > slots * 3) return 1;
+  const int64_t sp = std::min<int64_t>(std::min<int64_t>(slots / rest, 16), K / kMinSliceK);
+  return sp >= 2 ? int(sp) : 1;
+}
+
+// Mean work per CU over the largest (1 = every CU equally busy), in tiles: the whole tiles
+// spread over the CUs, then the leftover tiles' slices.
+double cu_fill(int tiles, const TileCfg& tc, int sp) {
+  const int slots = kCUs * tc.occ, rest = sp > 1 ? tiles % slots : 0, whole = tiles - rest;
+  const double most = double((whole + kCUs - 1) / kCUs) + double((rest * sp + kCUs - 1) / kCUs) / sp;
+  return most > 0 ? (double(tiles) / kCUs) / most : 1.0;
+}
 
 Plan make_plan(const GemmArgs& g) {
   const bool sw = g.epi == Epi::kSwiglu;
   Plan pl{};
-  pl.ti = choose_tile(g.M, g.N, g.K, g.a_kcontig, g.b_kcontig, sw);
+  int sp = 1;
+  if (g.a_kcontig && !g.b_kcontig) {
+    // Forward products: 128×256 tiles when there are at least two per CU, else 128×128 at
+    // three workgroups per CU; they are not split (the fixed-order slice sum costs more
+    // than the idle tail it saves at these k).
+    pl.ti = tile_count(kTiles[kT128x256], g.M, g.N, sw) >= 2 * kCUs ? kT128x256 : kT128o3;
+  } else if (g.a_kcontig && g.b_kcontig) {
+    // Input gradients: 256×256 for large grids with k ≥ 2048, unless the epilogue reads the
+    // saved activation (its loads then overlap other workgroups' loops only with two
+    // workgroups per CU); a half-empty last round splits in two when k ≥ 2048.
+    const bool aux = g.epi == Epi::kDGelu || g.epi == Epi::kDSwiglu;
+    pl.ti = !aux && g.K >= 2048 && tile_count(kTiles[kT256], g.M, g.N, false) >= 2 * kCUs ? kT256 : kT128;
+    const TileCfg& tc = kTiles[pl.ti];
+    const int slots = kCUs * tc.occ, rest = tile_count(tc, g.M, g.N, false) % slots;
+    if (rest > 0 && rest * 2 <= slots && g.K >= 2048) sp = 2;
+  } else {
+    // Weight gradients (k = tokens, long): the tile whose k-split fills the CUs best,
+    // weighted by its measured relative rate on these operands.
+    constexpr TileId kCand[] = {kT256x128, kT128x256, kT128o3, kT128, kT256};
+    constexpr double kRate[] = {1.00, 0.98, 0.96, 0.93, 0.90};
+    double best = -1.0;
+    for (int c = 0; c < 5; ++c) {
+      const TileCfg& tc = kTiles[kCand[c]];
+      const int tiles = tile_count(tc, g.M, g.N, false), s = fill_split(tiles, tc, g.K);
+      const double score = cu_fill(tiles, tc, s) * kRate[c];
+      if (score > best) {
+        best = score;
+        pl.ti = kCand[c];
+        sp = s;
+      }
+    }
+  }
   const TileCfg& tc = kTiles[pl.ti];
   const int64_t bn_cols = sw ? tc.bn / 2 : tc.bn;
   pl.tiles_m = int((g.M + tc.bm - 1) / tc.bm);
@@ -574,18 +675,11 @@ Plan make_plan(const GemmArgs& g) {
   pl.splits = 1;
   pl.kt_per_split = kt_total;
   pl.ws_elems = 0;
-  // Whole rounds of the 256·occ resident workgroups run whole tiles. When the tiles left
-  // over would fill at most 3/4 of a last round, they are split along k so that their
-  // slices fill that round instead (each slice keeping at least kMinSliceK of k).
-  const int slots = 256 * tc.occ;
-  const int rest = tiles % slots;
-  if (rest == 0 || rest * 4 > slots * 3) return pl;
-  int sp = slots / rest;
-  sp = std::min<int64_t>(sp, std::min<int64_t>(16, g.K / kMinSliceK));
-  if (sp < 2) return pl;
+  if (sp < 2 || tiles == 0) return pl;
+  const int rest = tiles % (kCUs * tc.occ);
   pl.kt_per_split = (kt_total + sp - 1) / sp;
   pl.splits = (kt_total + pl.kt_per_split - 1) / pl.kt_per_split;  // no empty slice
-  if (pl.splits < 2) {
+  if (pl.splits < 2 || rest == 0) {
     pl.kt_per_split = kt_total;
     pl.splits = 1;
     return pl;
