@@ -58,14 +58,15 @@ hipError_t events_for_current_device(EventSet** out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   EventSet& es = t_events[dev];
   if (!es.ready) {
-    // Both streams run on this device, so a device-scope release orders the chunk's
-    // products before its reduction; the default system-scope fence costs several
-    // microseconds of idle compute stream at every chunk boundary.
+    // The events only order kernels of this device's two streams: each kernel's own
+    // completion already makes its writes visible device-wide, so the record skips the
+    // system-scope fence (host visibility), which leaves the compute stream idle for
+    // ~2 us more at every chunk boundary (measured: 5.1 vs 7.1 us between two kernels).
     for (int i = 0; i < kMaxChunks; ++i) {
-      e = hipEventCreateWithFlags(&es.done[i], hipEventDisableTiming | hipEventReleaseToDevice);
+      e = hipEventCreateWithFlags(&es.done[i], hipEventDisableTiming | hipEventDisableSystemFence);
       if (e != hipSuccess) return e;
     }
-    e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming | hipEventReleaseToDevice);
+    e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) return e;
     es.ready = true;
   }
