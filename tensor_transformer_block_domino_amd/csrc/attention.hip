@@ -7,19 +7,23 @@
 // block with a running maximum and running sum (online softmax), so the seq×seq score
 // matrix never leaves registers.
 //
-// Design (gfx950): one workgroup = 4 waves = 128 query rows of one (sequence, head);
-// each wave owns 32 query rows. Keys advance 64 at a time through two LDS stages.
-//  * Scores are computed transposed, Sᵀ = K·Qᵀ (K fragment as the matrix-core's A), so a
-//    lane holds 4 keys of one query: the softmax statistics of a query live in one lane
-//    column (reduced over 4 lanes with cross-lane shuffles), and the probabilities are
-//    already laid out as the B operand of Oᵀ += Vᵀ·Pᵀ.
-//  * The 8 keys a lane feeds to one 16x16x32 MFMA are {4g..4g+3} ∪ {16+4g..16+4g+3} of the
-//    32-key step (g = lane/16); the V fragment reads the same keys, so the contraction is
-//    exact whatever order the matrix core sums them in.
-//  * Q stays in registers (read once from global memory); K is staged as [key][d], V as
-//    Vᵀ [d][key] (transposed in registers on the way into LDS).
-//  * Workgroups are issued longest-first (last query block of every sequence and head
-//    first) to balance the causal triangle.
+// Design (gfx950): one workgroup = 4 waves = 128 query rows of one (sequence, head); each
+// wave owns 32 query rows. Keys advance 64 at a time; K and V blocks reach LDS through
+// buffer loads that write LDS directly, two stages deep, one barrier per block.
+//  * S = Q·Kᵀ on 32×32×16 MFMAs with the operands swapped, so lane l holds the scores of
+//    query l%32 for keys 8j + 4·(l/32) + r (j, r = 0..3) of each 32-key block: a query's
+//    row lives in two lanes (l, l^32), and its running max and sum need one cross-lane
+//    exchange each.
+//  * The exponentiated scores of a 16-key step are then already the A operand of O += P·V
+//    (keys 4·(l/32) + r and 8 + 4·(l/32) + r of the step, in that k order); the V operand
+//    reads the same keys, transposed out of LDS with ds_read_b64_tr_b16, so P never leaves
+//    registers.
+//  * Q stays in registers (read once). K is staged [key][d] with a 16-byte-chunk XOR
+//    swizzle (a fragment read, 16 keys × one chunk, hits distinct banks); V is staged
+//    [key][d] with a 32-byte-chunk swizzle for the transposed reads.
+//  * Causal balance: the first half of the grid takes query blocks longest first, the
+//    second half shortest first, so the two workgroups a CU holds at once carry the same
+//    total work.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,14 +32,12 @@ namespace {
 
 constexpr int kD = 128;   // head_dim
 constexpr int kQB = 128;  // query rows per workgroup
-constexpr int kKB = 64;   // keys per stage
+constexpr int kKB = 64;   // keys per block
 
-// K tile: [64 keys][128 d], 16 chunks of 16 B per row; chunk c stored at c ^ (row & 7).
-__device__ __forceinline__ int k_off(int key, int chunk) { return key * kD + ((chunk ^ (key & 7)) << 3); }
-// Vᵀ tile: [128 d][64 keys], 8 chunks per row; chunk c stored at c ^ (row&7) ^ ((row>>3)&7).
-__device__ __forceinline__ int v_off(int d, int chunk) {
-  return d * kKB + ((chunk ^ ((d & 7) ^ ((d >> 3) & 7))) << 3);
-}
+// K tile [64 keys][128 d]: 16-byte chunk c of key k at c ^ (k & 15).
+__device__ __forceinline__ int k_off(int key, int chunk) { return key * kD + ((chunk ^ (key & 15)) << 3); }
+// V tile [64 keys][128 d]: 32-byte chunk c of key k at c ^ 2·(k & 3).
+__device__ __forceinline__ int v_off(int key, int d) { return key * kD + (((d >> 4) ^ ((key & 3) << 1)) << 4) + (d & 15); }
 
 struct AttnParams {
   const uint16_t* qkv; int64_t ld_qkv;
@@ -45,17 +47,21 @@ struct AttnParams {
   float scale_log2;    // scale · log2(e)
 };
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kD * kKB];
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kKB * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kKB * kD];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, lq = lane & 15;
-  // Longest-first order: the first heads·batch workgroups take the last query block.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+
+  // Grid order: positions 0 .. G/2−1 longest query block first, the rest shortest first.
+  const int hb = p.heads * p.batch, G = p.nqb * hb, half = (G + 1) / 2;
   const int lin = blockIdx.x;
-  const int hb = p.heads * p.batch;
-  const int qb = p.nqb - 1 - lin / hb;
-  const int head = (lin % hb) % p.heads;
-  const int b = (lin % hb) / p.heads;
+  const int srt = lin < half ? lin : G - 1 - (lin - half);
+  const int qb = p.nqb - 1 - srt / hb;
+  const int head = (srt % hb) % p.heads;
+  const int b = (srt % hb) / p.heads;
 
   const int64_t row0 = int64_t(b) * p.seq;  // first token of this sequence
   const uint16_t* Qg = p.qkv + head * kD;
@@ -63,173 +69,156 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   const uint16_t* Vg = p.qkv + 2 * p.hd + head * kD;
 
   const int q0 = qb * kQB;
-  const int qw = q0 + w * 32;  // this wave's first query
+  const int qw = q0 + w * 32;     // this wave's first query
+  const int q = qw + l32;         // this lane's query
 
-  // Q fragments: B operand of Sᵀ = K·Qᵀ; lane (q = qw + nq·16 + lq) holds d = 32s + 8g .. +7.
-  u32x4_t qf[2][4];
+  // Q fragments (A operand of S): d = 16s + 8h .. +7 of query q.
+  u32x4_t qf[8];
 #pragma unroll
-  for (int nq = 0; nq < 2; ++nq) {
-    const int q = qw + nq * 16 + lq;
+  for (int s = 0; s < 8; ++s)
+    qf[s] = q < p.seq ? *reinterpret_cast<const u32x4_t*>(Qg + (row0 + q) * p.ld_qkv + s * 16 + h * 8)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+
+  f32x16_t oacc[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qf[nq][s] = q < p.seq ? *reinterpret_cast<const u32x4_t*>(Qg + (row0 + q) * p.ld_qkv + s * 32 + g * 8)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mrun = -1e30f, lrun = 0.f;
+
+  const int q_hi = min(q0 + kQB, p.seq);   // exclusive
+  const int nkb = (q_hi + kKB - 1) / kKB;  // key blocks this workgroup needs
+
+  // Copies of one key block: wave w fills 1 KB pieces w, w+4, w+8, w+12 of each tile.
+  // Piece byte offset 16·(64·piece + lane) holds key (64·piece + lane)/16 and, for K,
+  // 16-byte chunk (lane & 15) ^ (key & 15); for V, 32-byte chunk ((lane & 15) >> 1) ^ 2·(key & 3).
+  int32_t koff[4], voff[4];
+  int kkey[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (w + 4 * i) * 64 + lane, key = pos >> 4, c16 = pos & 15;
+    kkey[i] = key;
+    koff[i] = int32_t((int64_t(key) * p.ld_qkv + ((c16 ^ (key & 15)) << 3)) * 2);
+    const int c32 = (c16 >> 1) ^ ((key & 3) << 1);
+    voff[i] = int32_t((int64_t(key) * p.ld_qkv + (c32 << 4) + ((c16 & 1) << 3)) * 2);
   }
-
-  f32x4_t oacc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) oacc[i][0] = oacc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-1e30f, -1e30f}, lrun[2] = {0.f, 0.f};
-
-  const int q_hi = min(q0 + kQB, p.seq);               // exclusive
-  const int nkb = (q_hi + kKB - 1) / kKB;              // key blocks this workgroup needs
-
-  // Global → register staging for one key block.
-  u32x4_t kst[4];
-  uint32_t vst[8][2];
-  auto load_kv = [&](int kb) {
+  auto issue = [&](int kb, int st) {
     const int key0 = kb * kKB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (row0 + key0) * p.ld_qkv);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (row0 + key0) * p.ld_qkv);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = (tid >> 4) + 16 * j, c = tid & 15;
-      kst[j] = key0 + key < p.seq ? *reinterpret_cast<const u32x4_t*>(Kg + (row0 + key0 + key) * p.ld_qkv + c * 8)
-                                  : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    const int db = tid & 31, kb8 = tid >> 5;  // d block of 4, key block of 8
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int key = key0 + kb8 * 8 + kk;
-      const u32x2_t t = key < p.seq ? *reinterpret_cast<const u32x2_t*>(Vg + (row0 + key) * p.ld_qkv + db * 4)
-                                    : u32x2_t{0u, 0u};
-      vst[kk][0] = t.x;
-      vst[kk][1] = t.y;
-    }
-  };
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = (tid >> 4) + 16 * j, c = tid & 15;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][k_off(key, c)]) = kst[j];
-    }
-    const int db = tid & 31, kb8 = tid >> 5;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t d4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = vst[2 * q][e >> 1], hi = vst[2 * q + 1][e >> 1];
-        d4[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      *reinterpret_cast<u32x4_t*>(&sV[buf][v_off(db * 4 + e, kb8)]) = u32x4_t{d4[0], d4[1], d4[2], d4[3]};
+    for (int i = 0; i < 4; ++i) {
+      const bool in = key0 + kkey[i] < p.seq;
+      dma16(rk, &sK[st][(w + 4 * i) * 512], in ? koff[i] : kOOB);
+      dma16(rv, &sV[st][(w + 4 * i) * 512], in ? voff[i] : kOOB);
     }
   };
 
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
-
+  issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    const bool has_next = kb + 1 < nkb;
-    if (has_next) load_kv(kb + 1);
+    const int st = kb & 1;
+    // Block kb has landed (the only copies in flight) and every wave is done with kb−1,
+    // whose stage the next copies overwrite.
+    wait_vm_barrier<0>();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
 
     const int key0 = kb * kKB;
-    if (key0 <= qw + 31 && qw < p.seq) {  // some key of this block is visible to this wave
-      // Sᵀ = K·Qᵀ for 64 keys × 32 queries.
-      f32x4_t sacc[4][2];
+    if (key0 > qw + 31 || qw >= p.seq) continue;  // every key of this block is in this wave's future
+
+    // S = Q·Kᵀ for 32 queries × 64 keys (two 32-key blocks).
+    f32x16_t sacc[2];
 #pragma unroll
-      for (int mk = 0; mk < 4; ++mk) sacc[mk][0] = sacc[mk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
 #pragma unroll
-        for (int mk = 0; mk < 4; ++mk) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&sK[buf][k_off(mk * 16 + lq, s * 4 + g)]);
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-          for (int nq = 0; nq < 2; ++nq)
-            sacc[mk][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
-                                                                  __builtin_bit_cast(bf16x8_t, qf[nq][s]),
-                                                                  sacc[mk][nq], 0, 0, 0);
-        }
+      for (int nb = 0; nb < 2; ++nb) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                          __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
       }
-      // Online softmax per query (lane column); scores in the log2 domain.
-      uint32_t pf[2][2][4];  // [nq][key step t][packed bf16 pairs]
+
+    // Online softmax over this block (log2 domain): mask the causal future and keys past
+    // the sequence, then update the running max and sum of query q.
+    const bool diag = key0 + kKB - 1 > qw;
+    float mx = -1e30f;
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-        const int q = qw + nq * 16 + lq;
-        float sv[4][4];
-        float mx = -1e30f;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mk = 0; mk < 4; ++mk)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = key0 + mk * 16 + 4 * g + r;
-            const float v = (key <= q && key < p.seq) ? sacc[mk][nq][r] * p.scale_log2 : -INFINITY;
-            sv[mk][r] = v;
-            mx = fmaxf(mx, v);
+        for (int r = 0; r < 4; ++r) {
+          float v = sacc[nb][4 * j + r] * p.scale_log2;
+          if (diag) {
+            const int key = key0 + nb * 32 + 8 * j + 4 * h + r;
+            v = (key <= q && key < p.seq) ? v : -INFINITY;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[nq], mx);
-        const float alpha = exp2f(mrun[nq] - mnew);
-        float rs = 0.f;
-        float pv[4][4];
-#pragma unroll
-        for (int mk = 0; mk < 4; ++mk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pv[mk][r] = exp2f(sv[mk][r] - mnew);
-            rs += pv[mk][r];
-          }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        lrun[nq] = lrun[nq] * alpha + rs;
-        mrun[nq] = mnew;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) oacc[md][nq] *= alpha;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          pf[nq][t][0] = pack_bf16x2(pv[2 * t][0], pv[2 * t][1]);
-          pf[nq][t][1] = pack_bf16x2(pv[2 * t][2], pv[2 * t][3]);
-          pf[nq][t][2] = pack_bf16x2(pv[2 * t + 1][0], pv[2 * t + 1][1]);
-          pf[nq][t][3] = pack_bf16x2(pv[2 * t + 1][2], pv[2 * t + 1][3]);
+          sacc[nb][4 * j + r] = v;
+          mx = fmaxf(mx, v);
         }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    float rs = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sacc[nb][e] - mnew);
+        sacc[nb][e] = pe;
+        rs += pe;
       }
-      // Oᵀ += Vᵀ·Pᵀ over the block's 64 keys (two 32-key steps).
+    rs += __shfl_xor(rs, 32);
+    lrun = lrun * alpha + rs;
+    mrun = mnew;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+
+    // O += P·V over the block's 64 keys: four 16-key steps; step t = 2·nb + tt uses the
+    // scores j = 2tt, 2tt+1 of 32-key block nb.
 #pragma unroll
-        for (int md = 0; md < 8; ++md) {
-          const int d = md * 16 + lq;
-          const int c0 = 4 * t + (g >> 1), c1 = 4 * t + 2 + (g >> 1), half = (g & 1) * 4;
-          const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(&sV[buf][v_off(d, c0) + half]);
-          const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(&sV[buf][v_off(d, c1) + half]);
-          const u32x4_t vf = {v0.x, v0.y, v1.x, v1.y};
+    for (int t = 0; t < 4; ++t) {
+      const int nb = t >> 1, tt = t & 1;
+      const u32x4_t pf = {pack_bf16x2(sacc[nb][8 * tt + 0], sacc[nb][8 * tt + 1]),
+                          pack_bf16x2(sacc[nb][8 * tt + 2], sacc[nb][8 * tt + 3]),
+                          pack_bf16x2(sacc[nb][8 * tt + 4], sacc[nb][8 * tt + 5]),
+                          pack_bf16x2(sacc[nb][8 * tt + 6], sacc[nb][8 * tt + 7])};
+      // V rows of this lane's keys: 16t + 4h + (0..3) and 16t + 8 + 4h + (0..3); the
+      // transposed read gives lane i of each 16-lane group column n0 + i of 4 rows.
+      const int g = lane >> 4, i16 = lane & 15;
+      const int krow = 16 * t + 4 * h + (i16 >> 2);
 #pragma unroll
-          for (int nq = 0; nq < 2; ++nq) {
-            const u32x4_t pfr = {pf[nq][t][0], pf[nq][t][1], pf[nq][t][2], pf[nq][t][3]};
-            oacc[md][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf),
-                                                                  __builtin_bit_cast(bf16x8_t, pfr), oacc[md][nq],
-                                                                  0, 0, 0);
-          }
-        }
+      for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow, d)]);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow + 8, d)]);
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t vf = {l2.x, l2.y, h2.x, h2.y};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                          __builtin_bit_cast(bf16x8_t, pf), oacc[db], 0, 0, 0);
       }
     }
-    if (has_next) store_kv(buf ^ 1);
-    __syncthreads();
   }
+  // No LDS write may land after the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // O[q][d .. d+3] = Oᵀ / l.
-#pragma unroll
-  for (int nq = 0; nq < 2; ++nq) {
-    const int q = qw + nq * 16 + lq;
-    if (q >= p.seq) continue;
-    const float inv = 1.0f / lrun[nq];
+  // O[q][d .. d+3] = O / l; lane holds d = 32·db + 8j + 4h + (0..3).
+  if (q < p.seq) {
+    const float inv = 1.0f / lrun;
     uint16_t* dst = p.o + (row0 + q) * p.ld_o + head * kD;
 #pragma unroll
-    for (int md = 0; md < 8; ++md) {
-      const f32x4_t v = oacc[md][nq] * inv;
-      *reinterpret_cast<u32x2_t*>(dst + md * 16 + 4 * g) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-    }
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t v = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
+                           oacc[db][4 * j + 3] * inv};
+        *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * j + 4 * h) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      }
   }
 }
 

@@ -59,4 +59,37 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float x) {
 
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoidf_(x); }
 
+// Global → LDS copies are buffer loads that write LDS directly (no registers): lane l of
+// one instruction writes 16 bytes at LDS address base + 16·l, so a wave instruction
+// fills one contiguous 1 KB block, and each lane picks which 16-byte chunk of the tile it
+// fetches. A lane outside the matrix uses byte offset kOOB; the buffer range check turns
+// it into zeros written to LDS, without a branch.
+constexpr int32_t kOOB = int32_t(0x80000000u);
+constexpr int32_t kRangeBytes = 0x7fffffff;
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+// The descriptor must be wave-uniform (scalar registers); the compiler cannot always
+// prove that of a pointer kept in a per-thread struct, and would then wrap every load in
+// a loop over lanes. readfirstlane states the uniformity explicitly.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  void* b = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, kRangeBytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight and all its
+// LDS operations are done, then barrier. A workgroup fence would wait for every LDS
+// write in flight (vmcnt(0)), which serialises the stage ring, so the wait is explicit.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 }  // namespace domino
