@@ -131,50 +131,86 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
+    // All K fragments of the block are read before the first MFMA, so the reads overlap
+    // each other instead of each MFMA waiting on its own.
+    u32x4_t kf[8][2];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
+      for (int nb = 0; nb < 2; ++nb)
+        kf[s][nb] = *reinterpret_cast<const u32x4_t*>(&sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s][nb]),
                                                           __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
-      }
 
-    // Online softmax over this block (log2 domain): mask the causal future and keys past
-    // the sequence, then update the running max and sum of query q.
-    const bool diag = key0 + kKB - 1 > qw;
+    // The V fragments do not depend on the softmax: read them now, behind it. Lane keys
+    // of step t: 16t + 4h + (0..3) and 16t + 8 + 4h + (0..3); the transposed read gives
+    // lane i of each 16-lane group column n0 + i of 4 rows.
+    u32x4_t vf[4][4];
+    {
+      const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int krow = 16 * t + 4 * h + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow, d)]);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow + 8, d)]);
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+          vf[t][db] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+        }
+      }
+    }
+
+    // Online softmax over this block in the log2 domain, with scores scaled inside the
+    // exponent (c = scale·log2 e > 0, so max(c·s) = c·max(s)). Key key0 + 4h + off
+    // (off = 32·nb + 8j + r) is visible iff off ≤ lim; only blocks that reach the wave's
+    // diagonal (or the sequence end) are masked.
     float mx = -1e30f;
+    if (key0 + kKB - 1 > qw || key0 + kKB > p.seq) {  // wave-uniform
+      const int lim = min(q, p.seq - 1) - key0 - 4 * h;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = nb * 32 + 8 * (e >> 2) + (e & 3);
+          sacc[nb][e] = off <= lim ? sacc[nb][e] : -INFINITY;
+        }
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = sacc[nb][4 * j + r] * p.scale_log2;
-          if (diag) {
-            const int key = key0 + nb * 32 + 8 * j + 4 * h + r;
-            v = (key <= q && key < p.seq) ? v : -INFINITY;
-          }
-          sacc[nb][4 * j + r] = v;
-          mx = fmaxf(mx, v);
-        }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[nb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    const float c = p.scale_log2;
+    const float mnew = fmaxf(mrun, mx * c);
     float rs = 0.f;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sacc[nb][e] - mnew);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[nb][e], c, -mnew));
         sacc[nb][e] = pe;
         rs += pe;
       }
     rs += __shfl_xor(rs, 32);
-    lrun = lrun * alpha + rs;
-    mrun = mnew;
+    // Rescale O and l only when some row's maximum grew (after the first blocks it
+    // rarely does).
+    if (__ballot(mnew > mrun)) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lrun *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    lrun += rs;
+    mrun = mnew;
 
     // O += P·V over the block's 64 keys: four 16-key steps; step t = 2·nb + tt uses the
     // scores j = 2tt, 2tt+1 of 32-key block nb.
@@ -185,23 +221,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
                           pack_bf16x2(sacc[nb][8 * tt + 2], sacc[nb][8 * tt + 3]),
                           pack_bf16x2(sacc[nb][8 * tt + 4], sacc[nb][8 * tt + 5]),
                           pack_bf16x2(sacc[nb][8 * tt + 6], sacc[nb][8 * tt + 7])};
-      // V rows of this lane's keys: 16t + 4h + (0..3) and 16t + 8 + 4h + (0..3); the
-      // transposed read gives lane i of each 16-lane group column n0 + i of 4 rows.
-      const int g = lane >> 4, i16 = lane & 15;
-      const int krow = 16 * t + 4 * h + (i16 >> 2);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-        typedef short v4i16 __attribute__((ext_vector_type(4)));
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow, d)]);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow + 8, d)]);
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        const u32x4_t vf = {l2.x, l2.y, h2.x, h2.y};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[t][db]),
                                                           __builtin_bit_cast(bf16x8_t, pf), oacc[db], 0, 0, 0);
-      }
     }
   }
   // No LDS write may land after the workgroup ends.
