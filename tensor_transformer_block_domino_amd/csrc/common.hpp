@@ -83,6 +83,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// LDS byte address of a pointer into a __shared__ array (for inline-assembly LDS reads).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight and all its
 // LDS operations are done, then barrier. A workgroup fence would wait for every LDS
 // write in flight (vmcnt(0)), which serialises the stage ring, so the wait is explicit.

@@ -8,9 +8,10 @@
 // "反向：扩展与权重梯度计算的重叠"; page "04 · TP/SP 的通信-计算 overlap 与工程优化", §1).
 //
 // Design (gfx950, 64-wide waves, 160 KB LDS per CU):
-//  * 256 threads = 4 waves in a 2×2 grid; block tile BM×BN with BM, BN ∈ {128, 256};
-//    each wave owns (BM/2)×(BN/2) as 32×32 MFMA blocks (the 32×32×16 shape sustains a
-//    higher issue rate than 16×16×32 with one wave per SIMD).
+//  * 256 threads = 4 waves; block tile BM×BN with BM ∈ {128, 256}, BN ∈ {128, 160, 256}.
+//    The waves form a 2×2 grid, or a 4×1 stack along M when BN/2 is not a whole number
+//    of 32-column blocks (BN = 160); each wave owns its part as 32×32 MFMA blocks (the
+//    32×32×16 shape sustains a higher issue rate than 16×16×32 with one wave per SIMD).
 //  * K advances through a ring of NS LDS stages of BK k each. Stages are filled by
 //    buffer loads that write LDS directly (no staging registers), NS−1 stages ahead of
 //    the one being consumed; one barrier per stage.
@@ -72,6 +73,7 @@ template <int R, int BK>
 struct OpK {
   static constexpr int CPR = BK / 8;
   static constexpr int kLoads = R * BK / 2048;  // 1 KB instructions per wave per stage
+  static_assert(R * BK % 2048 == 0, "whole 1 KB copies per wave");
   static __device__ __forceinline__ int f(int row) {
     return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 7)) : (((row >> 2) ^ (row >> 1)) & 3);
   }
@@ -94,9 +96,11 @@ struct OpK {
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) dma16(rs, stage + (wave + 4 * q) * 512, kc[q] < krem ? voff[q] : kOOB);
   }
-  // MFMA fragment: row `row0 + lane%32`, k = 16·s + 8·(lane/32) .. +7.
-  static __device__ __forceinline__ u32x4_t frag(const uint16_t* stage, int row0, int s, int lane) {
-    return *reinterpret_cast<const u32x4_t*>(stage + off(row0 + (lane & 31), s * 2 + (lane >> 5)));
+  // MFMA fragment: row `row0 + lane%32`, k = 16·s + 8·(lane/32) .. +7, one 16-byte read.
+  static constexpr int kRd = 1;
+  static __device__ __forceinline__ void read(const uint16_t* stage, int row0, int s, int lane, int,
+                                              u32x4_t& dst) {
+    asm volatile("ds_read_b128 %0, %1" : "=v"(dst) : "v"(lds_addr(stage + off(row0 + (lane & 31), s * 2 + (lane >> 5)))));
   }
 };
 
@@ -106,12 +110,17 @@ struct OpK {
 // element i%4 of the 4-element blocks addressed by lanes 4e + i/4 (e = 0..3). With lane
 // j of the group addressing k-row k0 + j/4 at columns n0 + 4·(j%4), lane i receives
 // column n0 + i at k-rows k0 .. k0+3. h(r) spreads the 4 k-rows × 4 chunks that 32
-// lanes read at once over distinct banks.
+// lanes read at once over distinct banks. With R = 160 a k-row is 80 banks long, so
+// k-rows k0 .. k0+3 (k0 a multiple of 4) already start 16 banks apart and need no swizzle.
 template <int R, int BK, bool kSw>
 struct OpMN {
   static constexpr int CPR = R / 8;
   static constexpr int kLoads = R * BK / 2048;
-  static __device__ __forceinline__ int h(int krow) { return ((krow & 3) << 2) ^ (((krow >> 1) & 1) << 1); }
+  static_assert(R * BK % 2048 == 0, "whole 1 KB copies per wave");
+  static constexpr bool kSwz = R % 128 == 0;
+  static __device__ __forceinline__ int h(int krow) {
+    return kSwz ? ((krow & 3) << 2) ^ (((krow >> 1) & 1) << 1) : 0;
+  }
   static __device__ __forceinline__ int off(int krow, int c) { return krow * R + ((c ^ h(krow)) << 3); }
   const uint16_t* base;
   int64_t ld;
@@ -134,18 +143,23 @@ struct OpMN {
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) dma16(rs, stage + (wave + 4 * q) * 512, kr[q] < krem ? voff[q] : kOOB);
   }
-  static __device__ __forceinline__ u32x4_t frag(const uint16_t* stage, int row0, int s, int lane) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
+  // MFMA fragment in two transposed reads: part 0 = k-rows k0 .. k0+3, part 1 = k0+4 .. k0+7.
+  static constexpr int kRd = 2;
+  static __device__ __forceinline__ void read(const uint16_t* stage, int row0, int s, int lane, int part,
+                                              u32x4_t& dst) {
     const int g = lane >> 4, j = lane & 15;
-    const int k0 = s * 16 + 8 * (g >> 1) + (j >> 2);
+    const int k0 = s * 16 + 8 * (g >> 1) + (j >> 2) + 4 * part;
     const int mn = row0 + 16 * (g & 1) + 4 * (j & 3);
     const int c = mn >> 3, e = mn & 7;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(stage + off(k0, c) + e));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(stage + off(k0 + 4, c) + e));
-    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-    return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+    u32x2_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr(stage + off(k0, c) + e)));
+    if (part == 0) {
+      dst.x = v.x;
+      dst.y = v.y;
+    } else {
+      dst.z = v.x;
+      dst.w = v.y;
+    }
   }
 };
 
@@ -240,10 +254,13 @@ __device__ __forceinline__ void epilogue_swiglu4(const KParams& p, int64_t m, in
 
 template <int BM, int BN, int BK, int NS, int kOcc, bool kAK, bool kBKc, Epi kEpi>
 __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
-  // Wave tile WM×WN as 32×32 blocks of v_mfma_f32_32x32x16_bf16 (k = 16 per MFMA).
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32, NSUB = BK / 16;
+  // Wave tile WM×WN as 32×32 blocks of v_mfma_f32_32x32x16_bf16 (k = 16 per MFMA); the
+  // waves form WGM rows × WGN columns over the block tile.
+  constexpr int WGM = (BN / 2) % 32 == 0 ? 2 : 4, WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, NSUB = BK / 16;
   constexpr bool kSw = kEpi == Epi::kSwiglu;
-  static_assert(!kSw || TN % 2 == 0, "SwiGLU pairs gate and up blocks within a wave");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32×32 blocks per wave");
+  static_assert(!kSw || (WGM == 2 && TN % 2 == 0), "SwiGLU pairs gate and up blocks within a wave");
   static_assert(NSUB % 2 == 0, "sub-steps alternate between two fragment sets");
   using OA = typename std::conditional<kAK, OpK<BM, BK>, OpMN<BM, BK, false>>::type;
   using OB = typename std::conditional<kBKc, OpK<BN, BK>, OpMN<BN, BK, kSw>>::type;
@@ -253,7 +270,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // Work item. Blocks 0 .. dp_tiles−1 compute whole tiles; the rest compute one k-slice of
   // one of the remaining tiles, slice-major. Workgroups are dispatched round-robin over
@@ -301,21 +318,50 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
     u32x4_t a[TM], b[TN];
   };
   Frag f0, f1;
-  auto read_frags = [&](Frag& f, int slot, int s) {
+  // Fragment reads are inline assembly, so their order against the MFMAs is the order
+  // written here and the compiler adds no waits of its own: through the builtins, each
+  // transposed read would wait for every global→LDS copy in flight (the compiler cannot
+  // tell which LDS they write), stalling every k-step on the copies it has just issued.
+  // Read op r of a sub-step: the B fragments' reads first, then the A fragments'.
+  constexpr int kReads = TN * OB::kRd + TM * OA::kRd;
+  auto read_op = [&](Frag& f, int slot, int s, int r) {
     const uint16_t* sa = smem + slot * kStage;
     const uint16_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = OB::frag(sb, wn * WN + j * 32, s, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) f.a[i] = OA::frag(sa, wm * WM + i * 32, s, lane);
+    if (r < TN * OB::kRd) {
+      OB::read(sb, wn * WN + (r / OB::kRd) * 32, s, lane, r % OB::kRd, f.b[r / OB::kRd]);
+    } else {
+      const int q = r - TN * OB::kRd;
+      OA::read(sa, wm * WM + (q / OA::kRd) * 32, s, lane, q % OA::kRd, f.a[q / OA::kRd]);
+    }
   };
-  auto mma = [&](const Frag& f) {
+  // Waits until this wave's fragment reads have landed; tying the fragments keeps their
+  // MFMAs after the wait.
+  auto wait_frags = [&](Frag& f) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(f.b[j]));
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
-                                                           __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(f.a[i]));
+  };
+  // One sub-step: the TM·TN MFMAs of `cur`, with the reads of the next sub-step's
+  // fragments spread over the first MFMAs (kLead of them go last without reads, so the
+  // reads land before the next wait). MFMA issue blocks the wave, so the reads must not
+  // form a run.
+  constexpr int NQ = TM * TN;
+  constexpr int kLead = NQ >= 8 ? 3 : 1;
+  constexpr int kSpread = NQ - kLead;
+  auto step = [&](const Frag& cur, Frag& nxt, int rslot, int rs) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.b[j]),
+                                                         __builtin_bit_cast(bf16x8_t, cur.a[i]), acc[i][j], 0, 0, 0);
+      const int r0 = q < kSpread ? q * kReads / kSpread : kReads;
+      const int r1 = q < kSpread ? (q + 1) * kReads / kSpread : kReads;
+#pragma unroll
+      for (int r = r0; r < r1; ++r) read_op(nxt, rslot, rs, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto issue = [&](int kt, int slot) {
     uint16_t* sa = smem + slot * kStage;
@@ -329,45 +375,31 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) issue(kt_begin + st, st);
     wait_vm_barrier<(NS - 1) * kLPS>();
-    read_frags(f0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) read_op(f0, 0, 0, r);
     int slot = 0;
     for (int kt = kt_begin; kt < kt_end; ++kt) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         Frag& cur = (s & 1) ? f1 : f0;
         Frag& nxt = (s & 1) ? f0 : f1;
+        wait_frags(cur);
         if (s + 1 < NSUB) {
-          read_frags(nxt, slot, s + 1);
+          step(cur, nxt, slot, s + 1);
         } else {
           // Every wave has read all of this stage (its last fragments are in registers):
-          // wait for the next stage, then refill this slot NS stages ahead.
+          // wait for the next stage, refill this slot NS stages ahead, and read the next
+          // stage's first fragments during this sub-step.
           wait_vm_barrier<(NS - 2) * kLPS>();
           issue(kt + NS, slot);
           slot = slot + 1 == NS ? 0 : slot + 1;
-          read_frags(nxt, slot, 0);
+          step(cur, nxt, slot, 0);
         }
-        // One LDS read (and, on a stage's last sub-step, one global→LDS issue) between
-        // consecutive MFMAs: MFMA issue blocks the wave, so a run of other instructions
-        // would leave the matrix pipe idle.
-        mma(cur);
-        if (s + 1 < NSUB) {
-#pragma unroll
-          for (int q = 0; q < TM * TN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < TM * TN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // No LDS write may land after the workgroup ends.
+    // The reads of the sub-step after the last are never used; they must land before their
+    // registers are reused, and no LDS write may land after the workgroup ends.
+    wait_frags(f0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
@@ -481,13 +513,14 @@ struct TileCfg {
 // 32×32×16 MFMA per 32 cycles per SIMD. At the MFMA rate a 128×128 tile needs all 64 B/clk
 // of copies and more LDS time than there is; 256-wide tiles halve both per FLOP but cut
 // the number of tiles, which small products need to fill 256 CUs.
-enum TileId { kT128 = 0, kT128o3 = 1, kT256 = 2, kT256x128 = 3, kT128x256 = 4 };
+enum TileId { kT128 = 0, kT128o3 = 1, kT256 = 2, kT256x128 = 3, kT128x256 = 4, kT256x160 = 5 };
 constexpr TileCfg kTiles[] = {
     {128, 128, 64, 2, 2},  // 64 KB LDS, 2 workgroups per CU
     {128, 128, 32, 3, 3},  // 48 KB LDS, 3 per CU
     {256, 256, 64, 2, 1},  // 128 KB LDS, 1 per CU
     {256, 128, 32, 3, 2},  // 72 KB LDS, 2 per CU
     {128, 256, 32, 3, 2},  // 72 KB LDS, 2 per CU
+    {256, 160, 64, 3, 1},  // 156 KB LDS, 1 per CU; waves stacked along M (64×160 each)
 };
 
 template <int BM, int BN, int BK, int NS, int kOcc, bool kAK, bool kBKc, Epi kEpi>
@@ -504,12 +537,23 @@ hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
            tc.ns, tc.occ, kAK ? "true" : "false", kBKc ? "true" : "false", int(kEpi));
   note_kernel(name);
   if constexpr (kAK && !kBKc) {  // forward products: the [in, out] weight is n-major
-    if (ti == kT128x256) launch_tile<128, 256, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s);
-    else if (ti == kT128o3) launch_tile<128, 128, 32, 3, 3, kAK, kBKc, kEpi>(kp, blocks, s);
-    else return hipErrorInvalidValue;
+    if (ti == kT128x256) {
+      launch_tile<128, 256, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s);
+    } else if (ti == kT128o3) {
+      launch_tile<128, 128, 32, 3, 3, kAK, kBKc, kEpi>(kp, blocks, s);
+    } else {
+      if constexpr (kEpi == Epi::kSwiglu) {
+        return hipErrorInvalidValue;  // gate/up pairing needs two waves along N
+      } else {
+        if (ti != kT256x160) return hipErrorInvalidValue;
+        launch_tile<256, 160, 64, 3, 1, kAK, kBKc, kEpi>(kp, blocks, s);
+      }
+    }
   } else if constexpr (kAK && kBKc) {  // input gradients: both operands k-contiguous
     if (ti == kT128) {
       launch_tile<128, 128, 64, 2, 2, kAK, kBKc, kEpi>(kp, blocks, s);
+    } else if (ti == kT256x160) {
+      launch_tile<256, 160, 64, 3, 1, kAK, kBKc, kEpi>(kp, blocks, s);
     } else {
       if constexpr (kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu) {
         return hipErrorInvalidValue;  // epilogues reading the saved activation: 128×128 only
@@ -597,11 +641,21 @@ double cu_fill(int tiles, const TileCfg& tc, int sp) {
   return most > 0 ? (double(tiles) / kCUs) / most : 1.0;
 }
 
+// A product whose 256×160 tiles make one round of at least 3/4 of the CUs runs them:
+// one workgroup per CU with the LDS and copy traffic per MFMA of the large tiles.
+bool one_round_256x160(const GemmArgs& g, bool sw) {
+  if (sw) return false;
+  const int t = tile_count(kTiles[kT256x160], g.M, g.N, false);
+  return t <= kCUs && 4 * t >= 3 * kCUs;
+}
+
 Plan make_plan(const GemmArgs& g) {
   const bool sw = g.epi == Epi::kSwiglu;
   Plan pl{};
   int sp = 1;
-  if (g.a_kcontig && !g.b_kcontig) {
+  if (g.a_kcontig && one_round_256x160(g, sw)) {
+    pl.ti = kT256x160;
+  } else if (g.a_kcontig && !g.b_kcontig) {
     // Forward products: 128×256 tiles when there are at least two per CU, else 128×128 at
     // three workgroups per CU; they are not split (the fixed-order slice sum costs more
     // than the idle tail it saves at these k).
