@@ -90,11 +90,17 @@ struct OpK {
       voff[q] = map_row<false, R>(rm, row) >= 0 ? int32_t((row * ld + c * 8) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(uint16_t* stage, int64_t k0, int64_t K, int wave) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
-    const int krem = K - k0 > BK ? BK : int(K - k0);
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) dma16(rs, stage + (wave + 4 * q) * 512, kc[q] < krem ? voff[q] : kOOB);
+  // The copies of one stage: a buffer resource at k0 and the k left, then kLoads 1 KB
+  // copies per wave.
+  struct Src {
+    __amdgpu_buffer_rsrc_t rs;
+    int krem;
+  };
+  __device__ __forceinline__ Src src(int64_t k0, int64_t K) const {
+    return Src{make_rsrc(base + k0), K - k0 > BK ? BK : int(K - k0)};
+  }
+  __device__ __forceinline__ void issue_one(const Src& sr, uint16_t* stage, int wave, int q) const {
+    dma16(sr.rs, stage + (wave + 4 * q) * 512, kc[q] < sr.krem ? voff[q] : kOOB);
   }
   // MFMA fragment: row `row0 + lane%32`, k = 16·s + 8·(lane/32) .. +7, one 16-byte read.
   static constexpr int kRd = 1;
@@ -137,11 +143,15 @@ struct OpMN {
       voff[q] = g >= 0 ? int32_t((krow * ld_ + (g - rm.base)) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(uint16_t* stage, int64_t k0, int64_t K, int wave) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld);
-    const int krem = K - k0 > BK ? BK : int(K - k0);
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) dma16(rs, stage + (wave + 4 * q) * 512, kr[q] < krem ? voff[q] : kOOB);
+  struct Src {
+    __amdgpu_buffer_rsrc_t rs;
+    int krem;
+  };
+  __device__ __forceinline__ Src src(int64_t k0, int64_t K) const {
+    return Src{make_rsrc(base + k0 * ld), K - k0 > BK ? BK : int(K - k0)};
+  }
+  __device__ __forceinline__ void issue_one(const Src& sr, uint16_t* stage, int wave, int q) const {
+    dma16(sr.rs, stage + (wave + 4 * q) * 512, kr[q] < sr.krem ? voff[q] : kOOB);
   }
   // MFMA fragment in two transposed reads: part 0 = k-rows k0 .. k0+3, part 1 = k0+4 .. k0+7.
   static constexpr int kRd = 2;
@@ -322,20 +332,28 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
   // written here and the compiler adds no waits of its own: through the builtins, each
   // transposed read would wait for every global→LDS copy in flight (the compiler cannot
   // tell which LDS they write), stalling every k-step on the copies it has just issued.
-  // Read op r of a sub-step: the B fragments' reads first, then the A fragments'.
-  constexpr int kReads = TN * OB::kRd + TM * OA::kRd;
+  // Read order of a sub-step: A0, B0 .. B(TN−1), A1 .. A(TM−1) (each fragment one 16-byte
+  // read, or two transposed ones), the order in which the MFMAs (i outer, j inner) first
+  // need them.
+  constexpr int kRA = OA::kRd, kRB = OB::kRd;
+  constexpr int kReads = TN * kRB + TM * kRA;
   auto read_op = [&](Frag& f, int slot, int s, int r) {
     const uint16_t* sa = smem + slot * kStage;
     const uint16_t* sb = sa + BM * BK;
-    if (r < TN * OB::kRd) {
-      OB::read(sb, wn * WN + (r / OB::kRd) * 32, s, lane, r % OB::kRd, f.b[r / OB::kRd]);
+    if (r < kRA) {
+      OA::read(sa, wm * WM, s, lane, r, f.a[0]);
+    } else if (r < kRA + TN * kRB) {
+      const int q = r - kRA;
+      OB::read(sb, wn * WN + (q / kRB) * 32, s, lane, q % kRB, f.b[q / kRB]);
     } else {
-      const int q = r - TN * OB::kRd;
-      OA::read(sa, wm * WM + (q / OA::kRd) * 32, s, lane, q % OA::kRd, f.a[q / OA::kRd]);
+      const int q = r - kRA - TN * kRB + kRA;  // ≥ kRA: fragments A1 ..
+      OA::read(sa, wm * WM + (q / kRA) * 32, s, lane, q % kRA, f.a[q / kRA]);
     }
   };
-  // Waits until this wave's fragment reads have landed; tying the fragments keeps their
-  // MFMAs after the wait.
+  // Last read (in the order above) that MFMA (i, j) needs.
+  auto need = [&](int i, int j) { return i == 0 ? kRA + (j + 1) * kRB - 1 : kRA + TN * kRB + i * kRA - 1; };
+  // Waits until this wave's fragment reads have all landed; tying the fragments keeps
+  // their MFMAs after the wait.
   auto wait_frags = [&](Frag& f) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -344,29 +362,58 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
     for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(f.a[i]));
   };
   // One sub-step: the TM·TN MFMAs of `cur`, with the reads of the next sub-step's
-  // fragments spread over the first MFMAs (kLead of them go last without reads, so the
-  // reads land before the next wait). MFMA issue blocks the wave, so the reads must not
-  // form a run.
+  // fragments spread over the first kSpread MFMAs (MFMA issue blocks the wave, so the
+  // reads must not form a run). Before each MFMA the wave waits only for the reads that
+  // MFMA uses: LDS reads complete in order, so "at most n in flight" with n = the reads
+  // issued after them covers exactly those.
   constexpr int NQ = TM * TN;
   constexpr int kLead = NQ >= 8 ? 3 : 1;
   constexpr int kSpread = NQ - kLead;
-  auto step = [&](const Frag& cur, Frag& nxt, int rslot, int rs) {
+  auto issued_after = [&](int q) { return q < kSpread ? (q + 1) * kReads / kSpread : kReads; };
+  // The refill of a freed slot. With one workgroup per CU and at least three stages, its
+  // copies (kLPS per wave) are spread over the MFMAs of NSUB sub-steps, window position
+  // w = 0 being the sub-step of the barrier that frees the slot and w = NSUB−1 the one
+  // before the next barrier (whose stage wait counts them): issued all at once, the four
+  // waves' copies queue behind each other in the CU's address unit while no wave issues
+  // MFMAs. With two stages the spread copies would land just before they are waited for,
+  // and with more workgroups per CU the others' MFMAs cover the burst, so there all of a
+  // stage's copies are issued at the barrier.
+  constexpr bool kSpreadCopies = kOcc == 1 && NS >= 3;
+  // The refill's k-step and slot are kept as plain integers and the buffer resources
+  // rebuilt per sub-step from them, which keeps them in scalar registers.
+  int dkt = 0, dslot = 0;
+  auto dma_at = [&](int w, int q) { return (w * NQ + q) * kLPS / (NSUB * NQ); };
+  auto step = [&](Frag& cur, Frag& nxt, int rslot, int rs, int w, bool dma) {
+    const typename OA::Src ra = kSpreadCopies ? oa.src(int64_t(dkt) * BK, p.K) : typename OA::Src{};
+    const typename OB::Src rb = kSpreadCopies ? ob.src(int64_t(dkt) * BK, p.K) : typename OB::Src{};
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int i = q / TN, j = q % TN;
+      const int before = q == 0 ? 0 : issued_after(q - 1);
+      lgkm_wait_tied(min(15, kReads - 1 - need(i, j) + before), cur.a[i], cur.b[j]);
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.b[j]),
                                                          __builtin_bit_cast(bf16x8_t, cur.a[i]), acc[i][j], 0, 0, 0);
-      const int r0 = q < kSpread ? q * kReads / kSpread : kReads;
-      const int r1 = q < kSpread ? (q + 1) * kReads / kSpread : kReads;
 #pragma unroll
-      for (int r = r0; r < r1; ++r) read_op(nxt, rslot, rs, r);
+      for (int r = before; r < issued_after(q); ++r) read_op(nxt, rslot, rs, r);
+      if (kSpreadCopies && dma) {
+        uint16_t* const dst = smem + dslot * kStage;
+#pragma unroll
+        for (int d = dma_at(w, q); d < dma_at(w, q + 1); ++d) {
+          if (d < OA::kLoads) oa.issue_one(ra, dst, wave, d);
+          else ob.issue_one(rb, dst + BM * BK, wave, d - OA::kLoads);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto issue = [&](int kt, int slot) {
     uint16_t* sa = smem + slot * kStage;
-    oa.issue(sa, int64_t(kt) * BK, p.K, wave);
-    ob.issue(sa + BM * BK, int64_t(kt) * BK, p.K, wave);
+    const typename OA::Src ra = oa.src(int64_t(kt) * BK, p.K);
+    const typename OB::Src rb = ob.src(int64_t(kt) * BK, p.K);
+#pragma unroll
+    for (int q = 0; q < OA::kLoads; ++q) oa.issue_one(ra, sa, wave, q);
+#pragma unroll
+    for (int q = 0; q < OB::kLoads; ++q) ob.issue_one(rb, sa + BM * BK, wave, q);
   };
 
   // The saved activation the backward epilogues read, for this lane's output quads in the
@@ -405,17 +452,21 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
       for (int s = 0; s < NSUB; ++s) {
         Frag& cur = (s & 1) ? f1 : f0;
         Frag& nxt = (s & 1) ? f0 : f1;
-        wait_frags(cur);
         if (s + 1 < NSUB) {
-          step(cur, nxt, slot, s + 1);
+          step(cur, nxt, slot, s + 1, s + 1, kSpreadCopies && kt > kt_begin);
         } else {
           // Every wave has read all of this stage (its last fragments are in registers):
-          // wait for the next stage, refill this slot NS stages ahead, and read the next
-          // stage's first fragments during this sub-step.
+          // wait for the next stage, start refilling this slot NS stages ahead, and read the
+          // next stage's first fragments during this sub-step.
           wait_vm_barrier<(NS - 2) * kLPS>();
-          issue(kt + NS, slot);
+          if constexpr (kSpreadCopies) {
+            dkt = __builtin_amdgcn_readfirstlane(kt + NS);
+            dslot = __builtin_amdgcn_readfirstlane(slot);
+          } else {
+            issue(kt + NS, slot);
+          }
           slot = slot + 1 == NS ? 0 : slot + 1;
-          step(cur, nxt, slot, 0);
+          step(cur, nxt, slot, 0, 0, kSpreadCopies);
         }
       }
     }
