@@ -416,24 +416,28 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
     for (int q = 0; q < OB::kLoads; ++q) ob.issue_one(rb, sa + BM * BK, wave, q);
   };
 
-  // The saved activation the backward epilogues read, for this lane's output quads in the
-  // row-contiguous epilogue layout (rows 8u + l/8 of each 32-row block, columns 4·(l%8) ..
-  // +3 of each 32-column block). Loaded before the stage ring is filled, so the loads
-  // overlap the whole k loop; being older than every copy, they never delay a stage wait.
+  // Epilogue layout: each 32-row band i of the wave tile is handled in kPasses passes of
+  // the wave, pass u covering output quad item = 64u + lane of the band, i.e. band row
+  // item / QPR, columns 4·(item % QPR) .. +3 of the wave's WN columns (for SwiGLU: of its
+  // WN/2 FFN columns), so consecutive lanes cover whole contiguous rows.
+  constexpr int QPR = (kSw ? WN / 2 : WN) / 4;
+  constexpr int kPasses = 32 * QPR / 64;
+  static_assert(32 * QPR % 64 == 0, "whole passes");
+  // The saved activation the backward epilogues read, in that layout. Loaded before the
+  // stage ring is filled, so the loads overlap the whole k loop; being older than every
+  // copy, they never delay a stage wait.
   constexpr bool kAux = kEpi == Epi::kDGelu || kEpi == Epi::kDSwiglu;
-  AuxQuad ax[kAux ? TM : 1][kAux ? TN : 1][4];
+  AuxQuad ax[kAux ? TM : 1][kAux ? kPasses : 1];
   if constexpr (kAux) {
     if (!part) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t n = n0 + wn * WN + j * 32 + 4 * (lane & 7);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t m = m0 + wm * WM + i * 32 + 8 * u + (lane >> 3);
-            ax[i][j][u] = m < p.M && n < p.N ? load_aux4<kEpi>(p, m, n) : AuxQuad{};
-          }
+        for (int u = 0; u < kPasses; ++u) {
+          const int item = 64 * u + lane;
+          const int64_t m = m0 + wm * WM + i * 32 + item / QPR;
+          const int64_t n = n0 + wn * WN + 4 * (item % QPR);
+          ax[i][u] = m < p.M && n < p.N ? load_aux4<kEpi>(p, m, n) : AuxQuad{};
         }
     }
   }
@@ -478,61 +482,61 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 
   // Epilogue. With the operands swapped, lane l holds, for block (i, j) and q = 0..3,
   // C[m][n .. n+3] with m = row0 + l%32 and n = col0 + 8q + 4·(l/32): written from there,
-  // one store instruction would touch 32 rows 16 bytes each. Each 32×32 block is staged in
-  // fp32 through a wave-private LDS region instead and read back as rows 8t + l/8,
-  // columns 4·(l%8) .. +3 (t = 0..3), so stores and the saved-activation loads cover 8 rows
-  // of 64–128 contiguous bytes each; the epilogue still sees the fp32 sums.
+  // one store instruction would touch 32 rows 16 bytes each. Each 32-row band of the wave
+  // tile is staged in fp32 through a wave-private LDS region instead and read back in the
+  // epilogue layout above, so stores (and the saved-activation loads) run along whole
+  // rows; the epilogue still sees the fp32 sums.
   // Every wave has to be done with the stage ring before any overwrites it.
   __syncthreads();
-  constexpr int PS = 36;                             // floats per staged row: rows start 36 banks apart
-  constexpr int kBlocks = kSw ? 2 : 1;               // gate and up are staged together
-  constexpr int kRegion = kBlocks * 32 * PS;         // floats per wave
+  constexpr int RS = WN + 4;          // floats per staged row: rows 4 or 36 banks apart
+  constexpr int kRegion = 32 * RS;    // floats per wave
   static_assert(4 * kRegion * 4 <= NS * kStage * 2, "staging fits in the stage ring");
   float* const stg = reinterpret_cast<float*>(smem) + wave * kRegion;
-  const int rr = lane >> 3, cc = 4 * (lane & 7);
-  auto stage = [&](float* dst, const f32x16_t& a) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4_t*>(dst + (lane & 31) * PS + 8 * q + 4 * (lane >> 5)) =
-          f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-  };
-  auto unstage = [&](const float* src, int pass) -> f32x4_t {
-    return *reinterpret_cast<const f32x4_t*>(src + (8 * pass + rr) * PS + cc);
-  };
-  // Tile-local column of block j in a k-slice's slot (for SwiGLU: FFN columns 0..BN/2−1
-  // hold gate, BN/2.. the matching up).
-  auto slot_col = [&](int j) {
-    return kSw ? (j < TN / 2 ? 0 : BN / 2 - TN / 2 * 32) + wn * (BN / 4) + j * 32 : wn * WN + j * 32;
-  };
   float* const slot = part ? p.ws + (int64_t(t - p.dp_tiles) * p.splits + split) * (BM * BN) : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int row0 = wm * WM + i * 32;  // tile-local
 #pragma unroll
-    for (int j = 0; j < TN / kBlocks; ++j) {
-      stage(stg, acc[i][j]);
-      if constexpr (kSw) stage(stg + 32 * PS, acc[i][j + TN / 2]);
-      if (part) {
-        // A k-slice: raw fp32 sums into this slice's [BM][BN] slot.
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          float* row = slot + (row0 + 8 * t4 + rr) * BN;
-          *reinterpret_cast<f32x4_t*>(row + slot_col(j) + cc) = unstage(stg, t4);
-          if constexpr (kSw) *reinterpret_cast<f32x4_t*>(row + slot_col(j + TN / 2) + cc) = unstage(stg + 32 * PS, t4);
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(stg + (lane & 31) * RS + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    const int band = wm * WM + i * 32;  // tile-local first row
+    // All of the band's values are read back before any is stored, so the LDS reads
+    // overlap each other instead of each store waiting for its own.
+    f32x4_t v[kPasses], v2[kSw ? kPasses : 1];
+#pragma unroll
+    for (int u = 0; u < kPasses; ++u) {
+      const int item = 64 * u + lane;
+      const float* src = stg + (item / QPR) * RS + 4 * (item % QPR);
+      v[u] = *reinterpret_cast<const f32x4_t*>(src);
+      if constexpr (kSw) v2[u] = *reinterpret_cast<const f32x4_t*>(src + WN / 2);
+    }
+    if (part) {
+      // A k-slice: raw fp32 sums into this slice's [BM][BN] slot, by tile-local output
+      // column (for SwiGLU: FFN columns 0..BN/2−1 hold gate, BN/2.. the matching up).
+#pragma unroll
+      for (int u = 0; u < kPasses; ++u) {
+        const int item = 64 * u + lane, c = 4 * (item % QPR);
+        float* row = slot + (band + item / QPR) * BN;
+        if constexpr (kSw) {
+          *reinterpret_cast<f32x4_t*>(row + wn * (BN / 4) + c) = v[u];
+          *reinterpret_cast<f32x4_t*>(row + BN / 2 + wn * (BN / 4) + c) = v2[kSw ? u : 0];
+        } else {
+          *reinterpret_cast<f32x4_t*>(row + wn * WN + c) = v[u];
         }
-      } else if constexpr (kSw) {
-        const int64_t jj = n0 + wn * (BN / 4) + j * 32 + cc;
+      }
+    } else {
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          const int64_t m = m0 + row0 + 8 * t4 + rr;
-          if (m < p.M && jj < p.f_s) epilogue_swiglu4(p, m, jj, unstage(stg, t4), unstage(stg + 32 * PS, t4));
-        }
-      } else {
-        const int64_t n = n0 + wn * WN + j * 32 + cc;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          const int64_t m = m0 + row0 + 8 * t4 + rr;
-          if (m < p.M && n < p.N) epilogue4<kEpi>(p, m, n, unstage(stg, t4), ax[kAux ? i : 0][kAux ? j : 0][t4]);
+      for (int u = 0; u < kPasses; ++u) {
+        const int item = 64 * u + lane, c = 4 * (item % QPR);
+        const int64_t m = m0 + band + item / QPR;
+        if constexpr (kSw) {
+          const int64_t jj = n0 + wn * (BN / 4) + c;
+          if (m < p.M && jj < p.f_s) epilogue_swiglu4(p, m, jj, v[u], v2[kSw ? u : 0]);
+        } else {
+          const int64_t n = n0 + wn * WN + c;
+          if (m < p.M && n < p.N) epilogue4<kEpi>(p, m, n, v[u], ax[kAux ? i : 0][kAux ? u : 0]);
         }
       }
     }
