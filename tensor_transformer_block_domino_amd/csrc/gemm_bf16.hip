@@ -545,17 +545,18 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
 
 // Finishes the k-split tiles: sums each tile's slices in slice order (a fixed order, so the
 // result does not depend on which workgroup ran first) and applies the product's epilogue.
+// One thread per output quad: item = 256·block + thread over the split tiles' BM rows ×
+// kQuads quads.
 template <int BM, int BN, Epi kEpi>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(KParams p) {
   constexpr bool kSw = kEpi == Epi::kSwiglu;
   constexpr int kCols = kSw ? BN / 2 : BN;  // output columns of a tile (FFN columns for SwiGLU)
   constexpr int kQuads = kCols / 4;
-  constexpr int kRows = 256 / kQuads;       // tile rows per workgroup
-  constexpr int kPerTile = BM / kRows;
-  static_assert(256 % kQuads == 0 && BM % kRows == 0, "fixup thread layout");
-  const int tt = blockIdx.x / kPerTile;
-  const int r = (blockIdx.x - tt * kPerTile) * kRows + threadIdx.x / kQuads;
-  const int c = (threadIdx.x % kQuads) * 4;
+  const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int tt = int(item / (BM * kQuads));
+  if (tt >= p.tiles_m * p.tiles_n - p.dp_tiles) return;
+  const int r = int(item % (BM * kQuads)) / kQuads;
+  const int c = int(item % kQuads) * 4;
   int tm, tn;
   tile_coords(p.dp_tiles + tt, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m = int64_t(tm) * BM + r;
@@ -640,6 +641,7 @@ hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
       case kT256: launch_tile<256, 256, 64, 2, 1, kAK, kBKc, kEpi>(kp, blocks, s); break;
       case kT256x128: launch_tile<256, 128, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s); break;
       case kT128x256: launch_tile<128, 256, 32, 3, 2, kAK, kBKc, kEpi>(kp, blocks, s); break;
+      case kT256x160: launch_tile<256, 160, 64, 3, 1, kAK, kBKc, kEpi>(kp, blocks, s); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -649,8 +651,8 @@ hipError_t dispatch_tile(int ti, const KParams& kp, int blocks, hipStream_t s) {
 template <int BM, int BN, Epi kEpi>
 void launch_fixup(const KParams& kp, int rest, hipStream_t s) {
   constexpr int kCols = kEpi == Epi::kSwiglu ? BN / 2 : BN;
-  constexpr int kPerTile = BM / (256 / (kCols / 4));
-  hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, kEpi>), dim3(rest * kPerTile), dim3(256), 0, s, kp);
+  const int64_t items = int64_t(rest) * BM * (kCols / 4);
+  hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, kEpi>), dim3(unsigned((items + 255) / 256)), dim3(256), 0, s, kp);
 }
 
 // k-split tiles occur for input gradients (tiles kT128, kT256) and weight gradients (any
@@ -665,6 +667,7 @@ hipError_t dispatch_fixup(int ti, const KParams& kp, int rest, hipStream_t s) {
     if (tc.bm == 128 && tc.bn == 128) launch_fixup<128, 128, kEpi>(kp, rest, s);
     else if (tc.bm == 256 && tc.bn == 256) launch_fixup<256, 256, kEpi>(kp, rest, s);
     else if (tc.bm == 256 && tc.bn == 128) launch_fixup<256, 128, kEpi>(kp, rest, s);
+    else if (tc.bm == 256 && tc.bn == 160) launch_fixup<256, 160, kEpi>(kp, rest, s);
     else launch_fixup<128, 256, kEpi>(kp, rest, s);
   } else if constexpr (kEpi == Epi::kStore) {
     if (ti == kT256) launch_fixup<256, 256, kEpi>(kp, rest, s);
@@ -743,10 +746,10 @@ Plan make_plan(const GemmArgs& g) {
   } else {
     // Weight gradients (k = tokens, long): the tile whose k-split fills the CUs best,
     // weighted by its measured relative rate on these operands.
-    constexpr TileId kCand[] = {kT256x128, kT128x256, kT128o3, kT128, kT256};
-    constexpr double kRate[] = {1.00, 0.98, 0.96, 0.93, 0.90};
+    constexpr TileId kCand[] = {kT256x160, kT256x128, kT128x256, kT128o3, kT128, kT256};
+    constexpr double kRate[] = {0.84, 1.00, 0.98, 0.96, 0.93, 0.90};
     double best = -1.0;
-    for (int c = 0; c < 5; ++c) {
+    for (int c = 0; c < 6; ++c) {
       const TileCfg& tc = kTiles[kCand[c]];
       const int tiles = tile_count(tc, g.M, g.N, false), s = fill_split(tiles, tc, g.K);
       const double score = cu_fill(tiles, tc, s) * kRate[c];
