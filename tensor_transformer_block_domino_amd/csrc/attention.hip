@@ -131,20 +131,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
-    // All K fragments of the block are read before the first MFMA, so the reads overlap
-    // each other instead of each MFMA waiting on its own.
+    // LDS reads are inline assembly with explicit waits: through the builtins the
+    // compiler makes them wait for every global→LDS copy in flight (it cannot tell which
+    // LDS they write), which would serialise the next block's copies with this block.
+    // All K fragments are read before the first MFMA; the MFMAs of sub-step s wait only
+    // for the reads of fragments s (LDS reads complete in order).
     u32x4_t kf[8][2];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        kf[s][nb] = *reinterpret_cast<const u32x4_t*>(&sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
+      for (int nb = 0; nb < 2; ++nb) lds_read_b128(kf[s][nb], &sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 8; ++s) {
+      lgkm_wait_tied(14 - 2 * s, kf[s][0], kf[s][1]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s][nb]),
                                                           __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
+    }
 
     // The V fragments do not depend on the softmax: read them now, behind it. Lane keys
     // of step t: 16t + 4h + (0..3) and 16t + 8 + 4h + (0..3); the transposed read gives
@@ -158,13 +162,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-          typedef short v4i16 __attribute__((ext_vector_type(4)));
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow, d)]);
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)&sV[st][v_off(krow + 8, d)]);
-          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-          vf[t][db] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+          u32x2_t lo, hi;
+          lds_read_tr16_b64(lo, &sV[st][v_off(krow, d)]);
+          lds_read_tr16_b64(hi, &sV[st][v_off(krow + 8, d)]);
+          vf[t][db] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
         }
       }
     }
@@ -213,7 +214,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     mrun = mnew;
 
     // O += P·V over the block's 64 keys: four 16-key steps; step t = 2·nb + tt uses the
-    // scores j = 2tt, 2tt+1 of 32-key block nb.
+    // scores j = 2tt, 2tt+1 of 32-key block nb. The V reads have landed behind the softmax.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(vf[t][db]));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int nb = t >> 1, tt = t & 1;

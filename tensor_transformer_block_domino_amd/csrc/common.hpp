@@ -88,6 +88,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 }
 
+// LDS reads as inline assembly: the compiler neither reorders them against other inline
+// assembly nor inserts waits for them, so every use must follow an explicit lgkmcnt wait
+// that ties the destination (lgkm_wait_tied, or a wait plus empty "+v" asm statements).
+__device__ __forceinline__ void lds_read_b128(u32x4_t& d, const void* p) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(lds_addr(p)));
+}
+__device__ __forceinline__ void lds_read_tr16_b64(u32x2_t& d, const void* p) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(d) : "v"(lds_addr(p)));
+}
+
 // Waits until at most n (0..15) LDS operations of this wave are in flight, tying a and b
 // (their consumers stay after the wait). n is a constant after unrolling, so the switch
 // folds to one instruction.
