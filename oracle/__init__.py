@@ -41,5 +41,6 @@ from .mlp import (  # noqa: F401
 )
 from .attention import (  # noqa: F401
     attn_shard_weights, causal_attention, attn_shard_forward, attn_forward_unsharded,
-    attn_y_rows, domino_attn_forward,
+    attn_y_rows, domino_attn_forward, causal_attention_lse, causal_attention_backward,
+    attn_lse, attn_shard_backward, attn_backward_unsharded, domino_attn_backward,
 )

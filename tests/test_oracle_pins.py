@@ -5,7 +5,10 @@ The pages print no tensor values, so the oracle is pinned by:
   * the identities the pages fix: row-chunk, column-chunk and 2D-chunk outputs equal
     the unsplit Y; the sum of shard partials equals the unsharded layer (for attention,
     the sum over head-slice shards equals full multi-head attention);
-  * central finite differences and the adjoint identity for the backward;
+  * central finite differences and the adjoint identity for the backward (MLP and
+    attention), torch autograd through scaled-dot-product attention for the attention
+    backward, and its closed forms (one token: dV = dO, dQ = dK = 0; Q = 0: dV_k =
+    Σ_{i≥k} dO_i/(i+1); V = ones: dQ = dK = 0), scipy's logsumexp for the LSE;
   * closed forms and special cases (gelu(0)=0, gelu'(0)=1/2, first causal row = V_0,
     Q = 0 gives prefix means, softmax rows sum to 1);
   * library routines for special cases (torch's tanh-GeLU and SiLU, torch autograd,
@@ -347,6 +350,100 @@ def test_attention_head_shards_sum_to_full_mha(row_chunks):
 
 
 # ------------------------------------------------------------------------------------------
+# Attention backward: torch autograd (per head and through the whole shard), finite
+# differences, closed forms, the log-sum-exp, chunked == unsplit.
+# ------------------------------------------------------------------------------------------
+def test_attention_backward_matches_torch_autograd():
+    batch, seq, heads, d, h = 2, 6, 2, 4, 5
+    scale = 0.37
+    X, A, Bo, dY = rnd(batch * seq, h), rnd(h, 3 * heads * d, scale=0.5), rnd(heads * d, h, scale=0.5), rnd(batch * seq, h)
+    tX, tA, tB = (torch.tensor(v, requires_grad=True) for v in (X, A, Bo))
+    QKV = tX @ tA
+    q, k, v = (QKV[:, i * heads * d:(i + 1) * heads * d].reshape(batch, seq, heads, d).transpose(1, 2) for i in range(3))
+    q.retain_grad()
+    O = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+    O2 = O.transpose(1, 2).reshape(batch * seq, heads * d)
+    O2.retain_grad()
+    Y = O2 @ tB
+    (Y * torch.tensor(dY)).sum().backward()
+    dO, dQKV, dX, dA, dBo = oattn.attn_shard_backward(X, A, Bo, dY, batch, seq, heads, d, scale)
+    assert np.max(np.abs(dO - O2.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dX - tX.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dA - tA.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dBo - tB.grad.numpy())) < 1e-12
+    dq = q.grad.transpose(1, 2).reshape(batch * seq, heads * d).numpy()
+    assert np.max(np.abs(dQKV[:, :heads * d] - dq)) < 1e-12
+
+
+def test_attention_backward_finite_differences():
+    batch, seq, heads, d, h = 1, 4, 2, 2, 3
+    rng = np.random.default_rng(11)
+    X, A, Bo, dY = rnd(batch * seq, h, rng=rng), rnd(h, 3 * heads * d, scale=0.7, rng=rng), \
+        rnd(heads * d, h, scale=0.7, rng=rng), rnd(batch * seq, h, rng=rng)
+    _, _, dX, dA, dBo = oattn.attn_shard_backward(X, A, Bo, dY, batch, seq, heads, d)
+
+    def loss(X_, A_, B_):
+        return float(np.sum(dY * oattn.attn_shard_forward(X_, A_, B_, batch, seq, heads, d)[2]))
+
+    eps = 1e-6
+    for M, G, which in [(X, dX, 0), (A, dA, 1), (Bo, dBo, 2)]:
+        num = np.zeros_like(M)
+        for idx in np.ndindex(M.shape):
+            args_p = [X.copy(), A.copy(), Bo.copy()]
+            args_m = [X.copy(), A.copy(), Bo.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.max(np.abs(num - G)) < 1e-7, which
+
+
+def test_attention_backward_closed_forms():
+    d = 3
+    # One token: O = V whatever Q and K, so dV = dO and dQ = dK = 0.
+    Q, K, V, dO = rnd(1, d), rnd(1, d), rnd(1, d), rnd(1, d)
+    dQ, dK, dV = oattn.causal_attention_backward(Q, K, V, dO, 0.9)
+    assert np.max(np.abs(dV - dO)) < 1e-15 and np.max(np.abs(dQ)) < 1e-15 and np.max(np.abs(dK)) < 1e-15
+    # Q = 0: row i averages V_0..V_i, so dV_k = Σ_{i ≥ k} dO_i / (i + 1).
+    n = 7
+    K, V, dO = rnd(n, d), rnd(n, d), rnd(n, d)
+    _, _, dV = oattn.causal_attention_backward(np.zeros((n, d)), K, V, dO, 0.5)
+    ref = np.array([sum(dO[i] / (i + 1) for i in range(k, n)) for k in range(n)])
+    assert np.max(np.abs(dV - ref)) < 1e-13
+    # V = ones: O is all ones whatever the scores, so dQ = dK = 0.
+    Q = rnd(n, d)
+    dQ, dK, _ = oattn.causal_attention_backward(Q, K, np.ones((n, d)), dO, 0.5)
+    assert np.max(np.abs(dQ)) < 1e-13 and np.max(np.abs(dK)) < 1e-13
+
+
+def test_attention_lse():
+    from scipy.special import logsumexp
+    n, d, scale = 9, 4, 0.6
+    Q, K = rnd(n, d), rnd(n, d)
+    L = oattn.causal_attention_lse(Q, K, scale)
+    ref = np.array([logsumexp(scale * (K[: i + 1] @ Q[i])) for i in range(n)])
+    assert np.max(np.abs(L - ref)) < 1e-13
+    # exp(S − LSE) over the visible keys is the attention row: it reproduces O.
+    V = rnd(n, d)
+    O = np.array([np.exp(scale * (K[: i + 1] @ Q[i]) - L[i]) @ V[: i + 1] for i in range(n)])
+    assert np.max(np.abs(O - oattn.causal_attention(Q, K, V, scale))) < 1e-13
+
+
+@pytest.mark.parametrize("row_chunks", [1, 2, 4])
+def test_domino_attn_backward_chunks_equal_unsplit(row_chunks):
+    batch, seq, heads, d, h, P = 4, 5, 4, 3, 7, 2
+    X, dY = rnd(batch * seq, h), rnd(batch * seq, h)
+    Aqkv, Bo = rnd(h, 3 * heads * d, scale=0.4), rnd(heads * d, h, scale=0.4)
+    s = 1
+    dX, dA, dBo = oattn.domino_attn_backward(X, Aqkv, Bo, dY, batch, seq, heads, d, P, s, row_chunks)
+    assert not np.isnan(dX).any()
+    assert np.max(np.abs(dX - oattn.attn_backward_unsharded(X, Aqkv, Bo, dY, batch, seq, heads, d))) < 1e-12
+    A_s, Bo_s = oattn.attn_shard_weights(Aqkv, Bo, heads, d, P, s)
+    _, _, _, rA, rB = oattn.attn_shard_backward(X, A_s, Bo_s, dY, batch, seq, heads // P, d)
+    assert np.max(np.abs(dA - rA)) < 1e-12
+    assert np.max(np.abs(dBo - rB)) < 1e-12
+
+
+# ------------------------------------------------------------------------------------------
 # Planted mistakes: each plausible slip in the oracle must make at least one pin fail.
 # ------------------------------------------------------------------------------------------
 def _pins():
@@ -360,6 +457,9 @@ def _pins():
         lambda: test_domino_forward_chunks_equal_unsharded_layer("swiglu", (2, 2)),
         lambda: test_domino_backward_chunks_equal_unsplit("swiglu", (1, 2)),
         lambda: test_mlp_forward_vs_brute_force("swiglu"),
+        lambda: test_attention_backward_matches_torch_autograd(),
+        lambda: test_attention_backward_closed_forms(),
+        lambda: test_attention_lse(),
     ]
 
 
@@ -409,3 +509,32 @@ def test_planted_attention_mistakes_are_caught(monkeypatch):
     assert _any_pin_fails()
     monkeypatch.setattr(oattn, "causal_attention", lambda Q, K, V, scale: orig(Q, K, V, 1.0))
     assert _any_pin_fails()
+
+
+ATTN_BWD_MUTATIONS = {
+    # the row term of the softmax rule dropped
+    "no_row_term": lambda Q, K, V, dO, scale: _mut_attn_bwd(Q, K, V, dO, scale, row_term=False),
+    # dK from dS instead of its transpose
+    "dk_untransposed": lambda Q, K, V, dO, scale: _mut_attn_bwd(Q, K, V, dO, scale, transpose_dk=False),
+    # the score scale left out of dQ and dK
+    "scale_dropped": lambda Q, K, V, dO, scale: _mut_attn_bwd(Q, K, V, dO, scale, use_scale=False),
+}
+
+
+def _mut_attn_bwd(Q, K, V, dO, scale, row_term=True, transpose_dk=True, use_scale=True):
+    n = Q.shape[0]
+    S = (Q @ K.T) * scale
+    S = np.where(np.triu(np.ones((n, n), dtype=bool), k=1), -np.inf, S)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    Pm = E / E.sum(axis=1, keepdims=True)
+    dV = Pm.T @ dO
+    dP = dO @ V.T
+    dS = Pm * (dP - np.sum(Pm * dP, axis=1, keepdims=True)) if row_term else Pm * dP
+    c = scale if use_scale else 1.0
+    return c * (dS @ K), c * ((dS.T if transpose_dk else dS) @ Q), dV
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_BWD_MUTATIONS))
+def test_planted_attention_backward_mistakes_are_caught(name, monkeypatch):
+    monkeypatch.setattr(oattn, "causal_attention_backward", ATTN_BWD_MUTATIONS[name])
+    assert _any_pin_fails(), name
