@@ -177,15 +177,47 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
  *   X [T, hidden]; A_qkv_s [hidden, 3·heads·head_dim] = [Q | K | V] blocks, head j at
  *   columns j·head_dim within each block; B_o_s [heads·head_dim, hidden]   (inputs)
  *   QKV [T, 3·heads·head_dim], O [T, heads·head_dim]   saved activations   (outputs)
+ *   lse [T, heads] fp32 or NULL: per query row and head, ln Σ_{k ≤ q} exp(scale·q·k), the
+ *                                       statistic the backward needs (output)
  *   Y_own, Y [T, hidden]; peer_Y HOST array of n_partials-1 device pointers
  *   workspace, workspace_bytes          optional device scratch (see Workspace above)
  * head_dim must be 128; bf16 only.
  */
 domino_status domino_attn_block_fwd(const domino_attn_desc* desc, const void* X, const void* A_qkv_s,
-                                    const void* B_o_s, void* QKV, void* O, void* Y_own,
+                                    const void* B_o_s, void* QKV, void* O, float* lse, void* Y_own,
                                     const void* const* peer_Y, void* Y, void* workspace, size_t workspace_bytes,
                                     hipStream_t compute, hipStream_t comm);
 size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* desc);
+
+/*
+ * domino_attn_block_bwd — attention shard backward ("反向：扩展与权重梯度计算的重叠";
+ * overlap page §1: input gradients need the reduction, weight gradients are local).
+ *   dO = dY·B_o_sᵀ                            (one GEMM over all rows)
+ *   dQKV = [dQ | dK | dV] of causal attention per (sequence, head), from QKV, O, dO and
+ *          lse: with P = exp(scale·Q·Kᵀ − lse) (causal), dV = Pᵀ·dO, dS = P ⊙ (dO·Vᵀ − Δ),
+ *          Δ = rowsum(dO ⊙ O), dQ = scale·dS·K, dK = scale·dSᵀ·Q    (one pass over all rows)
+ * then per row chunk (whole sequences):
+ *   dX_own[chunk] = dQKV·A_qkv_sᵀ            (this rank's partial input gradient)
+ *   dX[chunk] = dX_own + Σ peer_dX            (reduction on `comm`)
+ * then the independent weight gradients, which hide the last reduction:
+ *   dB_o_s (+)= Oᵀ·dY,  dA_qkv_s (+)= Xᵀ·dQKV  (fp32; accumulate != 0 adds to their contents)
+ *   X, A_qkv_s, B_o_s, QKV, O as in the forward; lse from the forward (required);
+ *   dY [T, hidden]                                                         (inputs)
+ *   dO [T, heads·head_dim], dQKV [T, 3·heads·head_dim]   caller-provided scratch/outputs
+ *   dX_own, dX [T, hidden]; peer_dX HOST array of n_partials-1 device pointers
+ *   dA_qkv_s [hidden, 3·heads·head_dim], dB_o_s [heads·head_dim, hidden]   fp32
+ *   workspace, workspace_bytes          device scratch of at least
+ *                                       domino_attn_block_bwd_workspace_size bytes (required:
+ *                                       it also holds the attention statistics)
+ * Deterministic: no atomics; the reduction order is fixed.
+ */
+domino_status domino_attn_block_bwd(const domino_attn_desc* desc, const void* X, const void* A_qkv_s,
+                                    const void* B_o_s, const void* QKV, const void* O, const float* lse,
+                                    const void* dY, void* dO, void* dQKV, void* dX_own,
+                                    const void* const* peer_dX, void* dX, float* dA_qkv_s, float* dB_o_s,
+                                    int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                    hipStream_t compute, hipStream_t comm);
+size_t domino_attn_block_bwd_workspace_size(const domino_attn_desc* desc);
 
 /* Human-readable name of a status code (static storage). */
 const char* domino_status_string(domino_status status);
@@ -212,7 +244,12 @@ typedef enum {
   DOMINO_K_ATTN = 8,
   DOMINO_K_OUTPROJ = 9,
   DOMINO_K_AUX = 10,        /* k-split tiles' fixed-order slice sums with their epilogues */
-  DOMINO_K_COUNT = 11
+  DOMINO_K_ATTN_BWD = 11,   /* attention backward: Δ, dK/dV and dQ kernels */
+  DOMINO_K_OUTPROJ_DGRAD = 12,  /* dY·B_o_sᵀ */
+  DOMINO_K_QKV_DGRAD = 13,  /* dQKV·A_qkv_sᵀ */
+  DOMINO_K_OUTPROJ_WGRAD = 14,  /* Oᵀ·dY */
+  DOMINO_K_QKV_WGRAD = 15,  /* Xᵀ·dQKV */
+  DOMINO_K_COUNT = 16
 } domino_kernel_kind;
 
 domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */

@@ -130,7 +130,9 @@ def mlp_inputs(w: MlpWorkload, *, seed: Optional[int] = None, tokens: Optional[i
 
 
 def attn_inputs(w: AttnWorkload, *, seed: Optional[int] = None, tokens: Optional[int] = None):
-    """Full attention tensors: X [T,h], Aqkv [h, 3*H*d] ([Q|K|V]), Bo [H*d, h]."""
+    """Full attention tensors: X [T,h], Aqkv [h, 3*H*d] ([Q|K|V]), Bo [H*d, h], and the
+    output gradient dY [T,h] for the backward (drawn last, so the forward tensors do not
+    depend on it)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
     T = w.tokens if tokens is None else tokens
@@ -138,7 +140,8 @@ def attn_inputs(w: AttnWorkload, *, seed: Optional[int] = None, tokens: Optional
     X = torch.randn(T, h, generator=g, dtype=torch.float32)
     Aqkv = torch.randn(h, 3 * Hd, generator=g, dtype=torch.float32) * 0.02
     Bo = torch.randn(Hd, h, generator=g, dtype=torch.float32) * 0.02
-    return {k: _cast(v, w.dtype) for k, v in dict(X=X, Aqkv=Aqkv, Bo=Bo).items()}
+    dY = torch.randn(T, h, generator=g, dtype=torch.float32)
+    return {k: _cast(v, w.dtype) for k, v in dict(X=X, Aqkv=Aqkv, Bo=Bo, dY=dY).items()}
 
 
 def randn(shape, *, seed: int, dtype: str = "bf16", scale: float = 1.0) -> torch.Tensor:

@@ -5,8 +5,9 @@ thin Python binding plus a driver that simulates a tensor-parallel group on one 
 """
 from ._lib import (  # noqa: F401
     DOMINO_ACT_GELU_TANH, DOMINO_ACT_SWIGLU, DOMINO_BF16, DOMINO_F32, DOMINO_MAX_PARTIALS, EXPORTED, KERNEL_KINDS,
-    LIB_PATH, AttnDesc, DominoError, MlpDesc, domino_attn_block_fwd, domino_block_bwd,
-    domino_attn_block_fwd_workspace_size, domino_block_bwd_workspace_size, domino_block_fwd,
+    LIB_PATH, AttnDesc, DominoError, MlpDesc, domino_attn_block_fwd, domino_attn_block_bwd, domino_block_bwd,
+    domino_attn_block_fwd_workspace_size, domino_attn_block_bwd_workspace_size, domino_block_bwd_workspace_size,
+    domino_block_fwd,
     domino_block_fwd_workspace_size, domino_status_string, domino_timing_enable,
     domino_timing_kernel, domino_timing_read, load, shard_reduce,
 )

@@ -19,11 +19,13 @@ DOMINO_MAX_PARTIALS = 16
 STATUS_NAMES = {0: "DOMINO_OK", 1: "DOMINO_ERR_INVALID_ARG", 2: "DOMINO_ERR_SHAPE", 3: "DOMINO_ERR_ALIGN",
                 4: "DOMINO_ERR_UNSUPPORTED", 5: "DOMINO_ERR_HIP"}
 KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgrad_a": 4, "wgrad_b": 5,
-                "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10}
+                "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10, "attn_bwd": 11, "outproj_dgrad": 12,
+                "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15}
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
             "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
+            "domino_attn_block_bwd", "domino_attn_block_bwd_workspace_size",
             "domino_status_string", "domino_last_error", "domino_timing_enable",
             "domino_timing_read", "domino_timing_kernel")
 
@@ -68,15 +70,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      vp, vp]
     lib.domino_block_fwd.restype = i32
     for name, desc in (("domino_block_fwd_workspace_size", MlpDesc), ("domino_block_bwd_workspace_size", MlpDesc),
-                       ("domino_attn_block_fwd_workspace_size", AttnDesc)):
+                       ("domino_attn_block_fwd_workspace_size", AttnDesc),
+                       ("domino_attn_block_bwd_workspace_size", AttnDesc)):
         getattr(lib, name).argtypes = [ctypes.POINTER(desc)]
         getattr(lib, name).restype = ctypes.c_size_t
     lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32,
                                      vp, ctypes.c_size_t, vp, vp]
     lib.domino_block_bwd.restype = i32
-    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp,
+    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, pp, vp, vp,
                                           ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_fwd.restype = i32
+    lib.domino_attn_block_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp,
+                                          vp, vp, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.domino_attn_block_bwd.restype = i32
     lib.domino_status_string.argtypes = [i32]
     lib.domino_status_string.restype = ctypes.c_char_p
     lib.domino_last_error.argtypes = []
@@ -157,10 +163,24 @@ def domino_block_bwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, pee
 
 
 def domino_attn_block_fwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, Y_own, peer_Y, Y, workspace=None,
-                          workspace_bytes: int = 0, compute=None, comm=None):
+                          workspace_bytes: int = 0, compute=None, comm=None, lse=None):
     _check(load().domino_attn_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
-                                        _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace),
+                                        _ptr(lse), _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace),
                                         int(workspace_bytes), _stream(compute), _stream(comm)))
+
+
+def domino_attn_block_bwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, lse, dY, dO, dQKV, dX_own, peer_dX, dX,
+                          dA_qkv_s, dB_o_s, accumulate: int = 0, workspace=None, workspace_bytes: int = 0,
+                          compute=None, comm=None):
+    _check(load().domino_attn_block_bwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
+                                        _ptr(lse), _ptr(dY), _ptr(dO), _ptr(dQKV), _ptr(dX_own),
+                                        _ptr_array(peer_dX), _ptr(dX), _ptr(dA_qkv_s), _ptr(dB_o_s),
+                                        int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
+                                        _stream(comm)))
+
+
+def domino_attn_block_bwd_workspace_size(desc: AttnDesc) -> int:
+    return int(load().domino_attn_block_bwd_workspace_size(ctypes.byref(desc)))
 
 
 def domino_status_string(status: int) -> str:

@@ -367,6 +367,49 @@ GemmArgs attn_out(const domino_attn_desc* d, const void* O, const void* B_o_s, v
   return g;
 }
 
+// dO = dY·B_o_sᵀ over all rows (B_o_s [hd, h] read as [n = hd][k = h]).
+GemmArgs attn_dout(const domino_attn_desc* d, const void* dY, const void* B_o_s, void* dO) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  GemmArgs g = gemm_base(T, hd, h, true);
+  g.A = dY; g.lda = h; g.a_kcontig = true;
+  g.B = B_o_s; g.ldb = h; g.b_kcontig = true;
+  g.C = dO; g.ldc = hd;
+  g.epi = Epi::kStore;
+  return g;
+}
+// dX_own chunk i = dQKV[rows_i]·A_qkv_sᵀ (A_qkv_s [h, 3hd] read as [n = h][k = 3hd]).
+GemmArgs attn_dx(const domino_attn_desc* d, const void* dQKV, const void* A_qkv_s, void* dX_own, int i) {
+  const int64_t h = d->hidden, hd = d->heads * d->head_dim, Tc = (d->batch / d->row_chunks) * d->seq;
+  GemmArgs g = gemm_base(Tc, h, 3 * hd, true);
+  g.A = at(dQKV, i * Tc * 3 * hd, 2); g.lda = 3 * hd; g.a_kcontig = true;
+  g.B = A_qkv_s; g.ldb = 3 * hd; g.b_kcontig = true;
+  g.C = at(dX_own, i * Tc * h, 2); g.ldc = h;
+  g.epi = Epi::kStore;
+  return g;
+}
+// dB_o_s (+)= Oᵀ·dY: [hd, h], k = tokens.
+GemmArgs attn_wgrad_o(const domino_attn_desc* d, const void* O, const void* dY, float* dB_o_s, int accumulate) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  GemmArgs g = gemm_base(hd, h, T, true);
+  g.A = O; g.lda = hd; g.a_kcontig = false;
+  g.B = dY; g.ldb = h; g.b_kcontig = false;
+  g.C = dB_o_s; g.ldc = h;
+  g.epi = Epi::kF32;
+  g.accumulate = accumulate;
+  return g;
+}
+// dA_qkv_s (+)= Xᵀ·dQKV: [h, 3hd], k = tokens.
+GemmArgs attn_wgrad_qkv(const domino_attn_desc* d, const void* X, const void* dQKV, float* dA_qkv_s, int accumulate) {
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  GemmArgs g = gemm_base(h, 3 * hd, T, true);
+  g.A = X; g.lda = h; g.a_kcontig = false;
+  g.B = dQKV; g.ldb = 3 * hd; g.b_kcontig = false;
+  g.C = dA_qkv_s; g.ldc = 3 * hd;
+  g.epi = Epi::kF32;
+  g.accumulate = accumulate;
+  return g;
+}
+
 // One product on stream s: the GEMM (timed as `kind`), then, if it split tiles along k,
 // the fixed-order sum of their slices with the epilogue (timed as auxiliary work).
 hipError_t run_gemm(int kind, GemmArgs g, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -570,7 +613,7 @@ size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* d) {
 }
 
 domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
-                                    void* QKV, void* O, void* Y_own, const void* const* peer_Y, void* Y,
+                                    void* QKV, void* O, float* lse, void* Y_own, const void* const* peer_Y, void* Y,
                                     void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_attn_desc(d);
@@ -581,6 +624,7 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
   const bool heads = d->heads > 0;
   if ((st = check_ptr(X, "X", heads)) || (st = check_ptr(A_qkv_s, "A_qkv_s", heads)) ||
       (st = check_ptr(B_o_s, "B_o_s", heads)) || (st = check_ptr(QKV, "QKV", heads)) || (st = check_ptr(O, "O", heads)) ||
+      (st = check_ptr(lse, "lse", heads && lse)) ||
       (st = check_ptr(Y_own, "Y_own", true)) || (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) ||
       (st = check_ptr(Y ? Y : Y_own, "Y", red)))
     return st;
@@ -597,6 +641,7 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
     AttnArgs aa{};
     aa.qkv = QKV; aa.ld_qkv = 3 * hd;
     aa.o = O; aa.ld_o = hd;
+    aa.lse = lse; aa.ld_lse = d->heads;
     aa.batch = d->batch; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
     aa.scale = scale;
     if (hip_ok(run_gemm(DOMINO_K_QKV, attn_qkv(d, X, A_qkv_s, QKV), workspace, workspace_bytes, sc.cs), &msg,
@@ -612,6 +657,81 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
                       "reduce Y"))
       return fail(DOMINO_ERR_HIP, msg);
   }
+  if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+size_t domino_attn_block_bwd_workspace_size(const domino_attn_desc* d) {
+  if (check_attn_desc(d) != DOMINO_OK) return 0;
+  const size_t stats = size_t(attn_bwd_stats_floats(d->batch * d->seq, d->heads)) * sizeof(float);
+  return std::max(stats, ws_bytes_of({attn_dout(d, nullptr, nullptr, nullptr), attn_dx(d, nullptr, nullptr, nullptr, 0),
+                                      attn_wgrad_o(d, nullptr, nullptr, nullptr, 0),
+                                      attn_wgrad_qkv(d, nullptr, nullptr, nullptr, 0)}));
+}
+
+domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
+                                    const void* QKV, const void* O, const float* lse, const void* dY, void* dO,
+                                    void* dQKV, void* dX_own, const void* const* peer_dX, void* dX, float* dA_qkv_s,
+                                    float* dB_o_s, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                    hipStream_t compute, hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_attn_desc(d);
+  if (st != DOMINO_OK) return st;
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim;
+  if (h == 0) return DOMINO_OK;
+  const bool red = T > 0 && needs_reduce(d->n_partials, dX_own, dX);
+  const bool tok = T > 0, heads = d->heads > 0;
+  if ((st = check_ptr(X, "X", tok && heads)) || (st = check_ptr(A_qkv_s, "A_qkv_s", tok && heads)) ||
+      (st = check_ptr(B_o_s, "B_o_s", tok && heads)) || (st = check_ptr(QKV, "QKV", tok && heads)) ||
+      (st = check_ptr(O, "O", tok && heads)) || (st = check_ptr(lse, "lse", tok && heads)) ||
+      (st = check_ptr(dY, "dY", tok && heads)) || (st = check_ptr(dO, "dO", tok && heads)) ||
+      (st = check_ptr(dQKV, "dQKV", tok && heads)) || (st = check_ptr(dX_own, "dX_own", tok)) ||
+      (st = check_peers(peer_dX, d->n_partials, "peer_dX", red)) || (st = check_ptr(dX ? dX : dX_own, "dX", red)) ||
+      (st = check_ptr(dA_qkv_s, "dA_qkv_s", heads)) || (st = check_ptr(dB_o_s, "dB_o_s", heads)))
+    return st;
+  const size_t stats_bytes = size_t(attn_bwd_stats_floats(T, d->heads)) * sizeof(float);
+  if (tok && heads && (!workspace || workspace_bytes < stats_bytes))
+    return fail(DOMINO_ERR_INVALID_ARG, "workspace smaller than domino_attn_block_bwd_workspace_size");
+  if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+  const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
+  const int64_t Tc = (d->batch / d->row_chunks) * d->seq;
+  std::string msg;
+  // dO and the attention backward feed no reduction: one launch each over all sequences
+  // (the attention statistics live in the workspace until the products after it reuse it).
+  // The input gradient runs per chunk (whole sequences), each followed by its reduction;
+  // the weight gradients follow, behind the last reduction.
+  if (tok && heads) {
+    AttnBwdArgs ab{};
+    ab.qkv = QKV; ab.ld_qkv = 3 * hd;
+    ab.o = O; ab.dout = dO; ab.ld_o = hd;
+    ab.lse = lse; ab.ld_lse = d->heads;
+    ab.dqkv = dQKV; ab.ld_dqkv = 3 * hd;
+    ab.stats = static_cast<float*>(workspace);
+    ab.batch = d->batch; ab.seq = d->seq; ab.heads = d->heads; ab.head_dim = d->head_dim;
+    ab.scale = scale;
+    if (hip_ok(run_gemm(DOMINO_K_OUTPROJ_DGRAD, attn_dout(d, dY, B_o_s, dO), workspace, workspace_bytes, sc.cs), &msg,
+               "dO GEMM") ||
+        hip_ok(timed(DOMINO_K_ATTN_BWD, sc.cs, [&] { return launch_attention_bwd(ab, sc.cs); }), &msg,
+               "attention backward"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  for (int i = 0; i < d->row_chunks && tok; ++i) {
+    // (no heads: k = 0 and the product writes zeros)
+    if (hip_ok(run_gemm(DOMINO_K_QKV_DGRAD, attn_dx(d, dQKV, A_qkv_s, dX_own, i), workspace, workspace_bytes, sc.cs),
+               &msg, "dX GEMM"))
+      return fail(DOMINO_ERR_HIP, msg);
+    if (red && hip_ok(sc.reduce(dX ? dX : dX_own, dX_own, peer_dX, d->n_partials, h, i * Tc * h, Tc, h, DOMINO_BF16),
+                      &msg, "reduce dX"))
+      return fail(DOMINO_ERR_HIP, msg);
+  }
+  // (no tokens: k = 0 and the products write zeros, or add nothing when accumulating)
+  if (heads && (hip_ok(run_gemm(DOMINO_K_OUTPROJ_WGRAD, attn_wgrad_o(d, O, dY, dB_o_s, accumulate), workspace,
+                                workspace_bytes, sc.cs), &msg, "dB_o GEMM") ||
+                hip_ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(d, X, dQKV, dA_qkv_s, accumulate), workspace,
+                                workspace_bytes, sc.cs), &msg, "dA_qkv GEMM")))
+    return fail(DOMINO_ERR_HIP, msg);
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
 }

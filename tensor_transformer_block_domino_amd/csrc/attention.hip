@@ -42,6 +42,7 @@ __device__ __forceinline__ int v_off(int key, int d) { return key * kD + (((d >>
 struct AttnParams {
   const uint16_t* qkv; int64_t ld_qkv;
   uint16_t* o; int64_t ld_o;
+  float* lse; int64_t ld_lse;  // optional [T, heads]: natural log of each row's softmax sum
   int seq, heads, batch, nqb;
   int64_t hd;          // heads · head_dim (width of each of the Q, K, V blocks)
   float scale_log2;    // scale · log2(e)
@@ -238,6 +239,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 
   // O[q][d .. d+3] = O / l; lane holds d = 32·db + 8j + 4h + (0..3).
   if (q < p.seq) {
+    // ln Σ_k exp(scale·s_k) = (m + log2 l)·ln 2 with m, l the running max and sum (log2 units).
+    if (p.lse && h == 0) p.lse[(row0 + q) * p.ld_lse + head] = (mrun + log2f(lrun)) * 0.69314718055994531f;
     const float inv = 1.0f / lrun;
     uint16_t* dst = p.o + (row0 + q) * p.ld_o + head * kD;
 #pragma unroll
@@ -260,6 +263,8 @@ hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.ld_qkv = a.ld_qkv;
   p.o = static_cast<uint16_t*>(a.o);
   p.ld_o = a.ld_o;
+  p.lse = a.lse;
+  p.ld_lse = a.ld_lse;
   p.seq = int(a.seq);
   p.heads = int(a.heads);
   p.batch = int(a.batch);

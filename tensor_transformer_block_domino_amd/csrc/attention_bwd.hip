@@ -1,0 +1,467 @@
+// Causal self-attention backward for one rank's head slice (bf16, head_dim 128): dQ, dK and
+// dV from Q, K, V (the saved QKV), O, dO and the forward's per-row log-sum-exp. The
+// attention is the layer's A on the rank's heads (page "DeepSpeed-Domino 深度解析",
+// sections "TP 的数据依赖：通信为何难以隐藏" and "反向：扩展与权重梯度计算的重叠"); causal
+// self-attention only (section "如何尝试 DeepSpeed-Domino").
+//
+// With P rebuilt from the LSE (P = exp(scale·s − LSE), no renormalising):
+//   dV = Pᵀ·dO,  dP = dO·Vᵀ,  dS = P ⊙ (dP − Δ) with Δ_q = Σ_d dO_qd·O_qd (= Σ_k P_qk·dP_qk),
+//   dQ = scale·dS·K,  dK = scale·dSᵀ·Q.
+// Three launches and no atomics, so results do not depend on timing:
+//  * prep: Δ per (token, head), and LSE·log2 e, stored head-major so the values of a block
+//    of queries are one contiguous run;
+//  * dK/dV: one workgroup per (sequence, head, 128 keys), each wave 32 keys whose K and V
+//    fragments stay in registers; blocks of 64 queries (from the diagonal on) stream
+//    through LDS. S and dP come out of the MFMAs with one key per lane (16 queries in its
+//    registers), so P and dS are already the B operand of dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS,
+//    whose A operand is dO or Q read transposed out of LDS (ds_read_b64_tr_b16);
+//  * dQ: one workgroup per (sequence, head, 128 queries), as in the forward: blocks of 64
+//    keys stream through LDS, S and dP come out with one query per lane, and
+//    dQᵀ += Kᵀ·dSᵀ reads K transposed.
+// Every LDS tile is [row][d] with the 16-byte chunk c of row r at c ^ (r & 15): row reads
+// (16 rows × one chunk) and transposed reads (4 rows × 32 bytes per 16 lanes) both spread
+// over the banks. LDS reads are inline assembly with explicit waits (through the builtins
+// the compiler would make them wait for the global→LDS copies of the next block).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace domino {
+namespace {
+
+constexpr int kD = 128;    // head_dim
+constexpr int kWG = 128;   // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kBlk = 64;   // queries (dK/dV) or keys (dQ) per streamed block
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int t_off(int row, int chunk) { return row * kD + ((chunk ^ (row & 15)) << 3); }
+
+struct BwdParams {
+  const uint16_t* qkv; int64_t ld_qkv;
+  const uint16_t* o; const uint16_t* dout; int64_t ld_o;
+  const float* lse; int64_t ld_lse;
+  uint16_t* dqkv; int64_t ld_dqkv;
+  float* stats;          // [heads][T] LSE·log2 e, then [heads][T] Δ, then padding
+  int64_t T, hd;
+  int seq, heads, batch;
+  float scale, scale_log2;
+};
+
+// One 16-byte fragment of d-chunk `chunk` (8 values) for the MFMA: row = the lane's row.
+__device__ __forceinline__ u32x4_t ld_frag(const uint16_t* g) { return *reinterpret_cast<const u32x4_t*>(g); }
+
+// Copy offsets (bytes) of a [64][128] tile in the swizzled layout: wave w fills 1 KB pieces
+// w, w+4, w+8, w+12; lane byte 16·(64·piece + lane) holds row (64·piece + lane)/16 and
+// logical chunk (lane & 15) ^ (row & 15).
+struct TileCopy {
+  int32_t off[4];
+  int row[4];
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = (w + 4 * i) * 64 + lane, r = pos >> 4, c16 = pos & 15;
+      row[i] = r;
+      off[i] = int32_t((int64_t(r) * ld + ((c16 ^ (r & 15)) << 3)) * 2);
+    }
+  }
+  // Rows at or beyond `valid` load zeros.
+  __device__ __forceinline__ void issue(const uint16_t* src, uint16_t* tile, int valid, int w) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rs, tile + (w + 4 * i) * 512, row[i] < valid ? off[i] : kOOB);
+  }
+};
+
+// Transposed fragment for the A operand of an MFMA whose k runs over the tile's rows: the
+// lane's column d = 32·db + lane%32 at rows 16t + 4·(lane/32) + (0..3) and the same + 8.
+__device__ __forceinline__ void read_tr_frag(u32x4_t& f, const uint16_t* tile, int t, int db, int lane) {
+  const int g = lane >> 4, i16 = lane & 15, h = lane >> 5;
+  const int r = 16 * t + 4 * h + (i16 >> 2);
+  const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+  u32x2_t lo, hi;
+  lds_read_tr16_b64(lo, tile + t_off(r, d >> 3) + (d & 7));
+  lds_read_tr16_b64(hi, tile + t_off(r + 8, d >> 3) + (d & 7));
+  f = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void tie(u32x4_t& v) { asm volatile("" : "+v"(v)); }
+
+// Scores j = 2tt, 2tt+1 of a 32-row block (16 values) as the 8 bf16 B-operand values of
+// 16-row step tt: rows 4h + (0..3) and 8 + 4h + (0..3) of the step.
+__device__ __forceinline__ u32x4_t pack_step(const f32x16_t& v, int tt) {
+  return u32x4_t{pack_bf16x2(v[8 * tt + 0], v[8 * tt + 1]), pack_bf16x2(v[8 * tt + 2], v[8 * tt + 3]),
+                 pack_bf16x2(v[8 * tt + 4], v[8 * tt + 5]), pack_bf16x2(v[8 * tt + 6], v[8 * tt + 7])};
+}
+
+// Δ and LSE·log2 e per (token, head): 16 threads per pair, 8 d each, a fixed xor tree.
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
+  const int64_t item = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  const bool ok = item < p.T * p.heads;
+  const int64_t tok = ok ? item / p.heads : 0;
+  const int head = ok ? int(item % p.heads) : 0;
+  float acc = 0.f;
+  if (ok) {
+    const u32x4_t a = ld_frag(p.o + tok * p.ld_o + head * kD + 8 * j);
+    const u32x4_t b = ld_frag(p.dout + tok * p.ld_o + head * kD + 8 * j);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(aw[e]), bf16_lo(bw[e]), acc);
+      acc = fmaf(bf16_hi(aw[e]), bf16_hi(bw[e]), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (ok && j == 0) {
+    p.stats[head * p.T + tok] = p.lse[tok * p.ld_lse + head] * kLog2e;
+    p.stats[(int64_t(p.heads) + head) * p.T + tok] = acc;
+  }
+}
+
+// dK and dV of 128 keys of one (sequence, head).
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][kBlk * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[2][kBlk * kD];
+  __shared__ __attribute__((aligned(1024))) float sSt[2][256];  // LSE·log2 e [64], Δ [64], copy tail
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+
+  // Grid order: the first half longest key block first (key block 0 sees every query
+  // block), the second half shortest first, so co-resident workgroups balance.
+  const int nkb = (p.seq + kWG - 1) / kWG, nqb = (p.seq + kBlk - 1) / kBlk;
+  const int hb = p.heads * p.batch, G = nkb * hb, half = (G + 1) / 2;
+  const int lin = blockIdx.x;
+  const int srt = lin < half ? lin : G - 1 - (lin - half);
+  const int kb = srt / hb;
+  const int head = (srt % hb) % p.heads;
+  const int b = (srt % hb) / p.heads;
+
+  const int64_t row0 = int64_t(b) * p.seq;
+  const uint16_t* Qg = p.qkv + head * kD;
+  const uint16_t* Kg = p.qkv + p.hd + head * kD;
+  const uint16_t* Vg = p.qkv + 2 * p.hd + head * kD;
+  const uint16_t* dOg = p.dout + head * kD;
+  const float* stg = p.stats + head * p.T + row0;
+
+  const int k0 = kb * kWG;
+  const int kw = k0 + w * 32;   // this wave's first key
+  const int key = kw + l32;     // this lane's key
+
+  // K and V of the lane's key as B operands (d = 16s + 8h .. +7).
+  u32x4_t kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = key < p.seq ? ld_frag(Kg + (row0 + key) * p.ld_qkv + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    vf[s] = key < p.seq ? ld_frag(Vg + (row0 + key) * p.ld_qkv + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
+
+  TileCopy cq, co;
+  cq.init(p.ld_qkv, w, lane);
+  co.init(p.ld_o, w, lane);
+  const int qb0 = k0 / kBlk;  // first query block that reaches these keys
+  auto issue = [&](int qb, int st) {
+    const int q0 = qb * kBlk;
+    cq.issue(Qg + (row0 + q0) * p.ld_qkv, sQ[st], p.seq - q0, w);
+    co.issue(dOg + (row0 + q0) * p.ld_o, sO[st], p.seq - q0, w);
+    if (w == 0) {
+      // lanes 0–15: LSE·log2 e of the block's 64 queries; lanes 16–31: their Δ (values past
+      // the sequence belong to the next one and are masked; the buffer is padded at its end).
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint16_t*>(stg + q0));
+      const int32_t o = lane < 16 ? 16 * lane : lane < 32 ? int32_t(int64_t(p.heads) * p.T * 4) + 16 * (lane - 16) : kOOB;
+      dma16(rs, reinterpret_cast<uint16_t*>(sSt[st]), o);
+    }
+  };
+
+  const float c = p.scale_log2;
+  issue(qb0, 0);
+  for (int qb = qb0; qb < nqb; ++qb) {
+    const int st = (qb - qb0) & 1;
+    wait_vm_barrier<0>();
+    if (qb + 1 < nqb) issue(qb + 1, st ^ 1);
+    const int q0 = qb * kBlk;
+    if (q0 + kBlk - 1 < kw || kw >= p.seq) continue;  // every query of the block precedes these keys
+
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int qn = q0 + nb * 32;  // first query of this 32-query half
+      if (qn + 31 < kw) continue;   // wave-uniform
+      // The LSE·log2 e and Δ of queries qn + 8j + 4h + (0..3), read first; then
+      // S[query][key] and dP[query][key] for those queries (X = the tile's rows).
+      u32x4_t lse4[4], del4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lds_read_b128(lse4[j], &sSt[st][nb * 32 + 8 * j + 4 * h]);
+        lds_read_b128(del4[j], &sSt[st][64 + nb * 32 + 8 * j + 4 * h]);
+      }
+      u32x4_t qr[8], dr[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        lds_read_b128(qr[s], &sQ[st][t_off(nb * 32 + l32, 2 * s + h)]);
+        lds_read_b128(dr[s], &sO[st][t_off(nb * 32 + l32, 2 * s + h)]);
+      }
+      f32x16_t sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        lgkm_wait_tied(14 - 2 * s, qr[s], dr[s]);  // reads complete in order
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qr[s]),
+                                                      __builtin_bit_cast(bf16x8_t, kf[s]), sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dr[s]),
+                                                      __builtin_bit_cast(bf16x8_t, vf[s]), pacc, 0, 0, 0);
+      }
+      // Every read issued so far has landed (the last wait above was lgkmcnt(0)).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tie(lse4[j]);
+        tie(del4[j]);
+      }
+      // Transposed dO and Q for this half's two 16-query steps.
+      u32x4_t dot[2][4], qt[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          read_tr_frag(dot[tt][db], sO[st], 2 * nb + tt, db, lane);
+          read_tr_frag(qt[tt][db], sQ[st], 2 * nb + tt, db, lane);
+        }
+      // P and dS; query qn + 8j + 4h + r sees the key iff key ≤ query < seq.
+      const bool edge = qn < kw + 31 || qn + 32 > p.seq;  // wave-uniform
+      const int lo = key - qn - 4 * h, hi = p.seq - 1 - qn - 4 * h;
+      f32x16_t pm, ds;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = e >> 2, r = e & 3, off = 8 * j + r;
+        const float l2 = __uint_as_float(lse4[j][r]), dl = __uint_as_float(del4[j][r]);
+        float pe = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -l2));
+        if (edge) pe = off >= lo && off <= hi ? pe : 0.f;
+        pm[e] = pe;
+        ds[e] = pe * (pacc[e] - dl);
+      }
+      lds_wait_all();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          tie(dot[tt][db]);
+          tie(qt[tt][db]);
+        }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const u32x4_t pf = pack_step(pm, tt), sf = pack_step(ds, tt);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dot[tt][db]),
+                                                          __builtin_bit_cast(bf16x8_t, pf), dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qt[tt][db]),
+                                                          __builtin_bit_cast(bf16x8_t, sf), dk[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // No LDS write may land after the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // The lane holds d = 32·db + 8j + 4h + (0..3) of its key.
+  if (key < p.seq) {
+    uint16_t* dK = p.dqkv + (row0 + key) * p.ld_dqkv + p.hd + head * kD;
+    uint16_t* dV = dK + p.hd;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * h;
+        *reinterpret_cast<u32x2_t*>(dK + d) =
+            u32x2_t{pack_bf16x2(dk[db][4 * j] * p.scale, dk[db][4 * j + 1] * p.scale),
+                    pack_bf16x2(dk[db][4 * j + 2] * p.scale, dk[db][4 * j + 3] * p.scale)};
+        *reinterpret_cast<u32x2_t*>(dV + d) =
+            u32x2_t{pack_bf16x2(dv[db][4 * j], dv[db][4 * j + 1]), pack_bf16x2(dv[db][4 * j + 2], dv[db][4 * j + 3])};
+      }
+  }
+}
+
+// dQ of 128 queries of one (sequence, head).
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kBlk * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kBlk * kD];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+
+  // Grid order: the first half longest query block first, the second half shortest first.
+  const int nqb = (p.seq + kWG - 1) / kWG;
+  const int hb = p.heads * p.batch, G = nqb * hb, half = (G + 1) / 2;
+  const int lin = blockIdx.x;
+  const int srt = lin < half ? lin : G - 1 - (lin - half);
+  const int qb = nqb - 1 - srt / hb;
+  const int head = (srt % hb) % p.heads;
+  const int b = (srt % hb) / p.heads;
+
+  const int64_t row0 = int64_t(b) * p.seq;
+  const uint16_t* Qg = p.qkv + head * kD;
+  const uint16_t* Kg = p.qkv + p.hd + head * kD;
+  const uint16_t* Vg = p.qkv + 2 * p.hd + head * kD;
+  const uint16_t* dOg = p.dout + head * kD;
+
+  const int q0 = qb * kWG;
+  const int qw = q0 + w * 32;   // this wave's first query
+  const int q = qw + l32;       // this lane's query
+
+  // Q and dO of the lane's query as B operands (d = 16s + 8h .. +7), its LSE·log2 e and Δ.
+  u32x4_t qf[8], df[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = q < p.seq ? ld_frag(Qg + (row0 + q) * p.ld_qkv + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    df[s] = q < p.seq ? ld_frag(dOg + (row0 + q) * p.ld_o + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  const float l2 = q < p.seq ? p.stats[head * p.T + row0 + q] : 0.f;
+  const float dl = q < p.seq ? p.stats[(int64_t(p.heads) + head) * p.T + row0 + q] : 0.f;
+
+  f32x16_t dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+
+  TileCopy ck;
+  ck.init(p.ld_qkv, w, lane);
+  const int q_hi = min(q0 + kWG, p.seq);
+  const int nkb = (q_hi + kBlk - 1) / kBlk;  // key blocks these queries see
+  auto issue = [&](int kb, int st) {
+    const int k0 = kb * kBlk;
+    ck.issue(Kg + (row0 + k0) * p.ld_qkv, sK[st], p.seq - k0, w);
+    ck.issue(Vg + (row0 + k0) * p.ld_qkv, sV[st], p.seq - k0, w);
+  };
+
+  const float c = p.scale_log2;
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    wait_vm_barrier<0>();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const int k0 = kb * kBlk;
+    if (k0 > qw + 31 || qw >= p.seq) continue;  // every key of the block is in this wave's future
+
+    // S[key][query] and dP[key][query] for keys 32nb + 8j + 4h + r: X = the tile's rows.
+    u32x4_t kr[8][2], vr[8][2];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        lds_read_b128(kr[s][nb], &sK[st][t_off(nb * 32 + l32, 2 * s + h)]);
+        lds_read_b128(vr[s][nb], &sV[st][t_off(nb * 32 + l32, 2 * s + h)]);
+      }
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = pacc[nb][r] = 0.f;
+    lds_wait_all();
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        tie(kr[s][nb]);
+        tie(vr[s][nb]);
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s][nb]),
+                                                          __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
+        pacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vr[s][nb]),
+                                                          __builtin_bit_cast(bf16x8_t, df[s]), pacc[nb], 0, 0, 0);
+      }
+    // Transposed K for dQᵀ += Kᵀ·dSᵀ, four 16-key steps.
+    u32x4_t kt[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) read_tr_frag(kt[t][db], sK[st], t, db, lane);
+    // dS; key k0 + 4h + off (off = 32nb + 8j + r) is visible iff off ≤ lim.
+    const bool edge = k0 + kBlk - 1 > qw || k0 + kBlk > p.seq;  // wave-uniform
+    const int lim = min(q, p.seq - 1) - k0 - 4 * h;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int off = nb * 32 + 8 * (e >> 2) + (e & 3);
+        float pe = __builtin_amdgcn_exp2f(fmaf(sacc[nb][e], c, -l2));
+        if (edge) pe = off <= lim ? pe : 0.f;
+        sacc[nb][e] = pe * (pacc[nb][e] - dl);
+      }
+    lds_wait_all();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) tie(kt[t][db]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4_t sf = pack_step(sacc[t >> 1], t & 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kt[t][db]),
+                                                        __builtin_bit_cast(bf16x8_t, sf), dq[db], 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // The lane holds d = 32·db + 8j + 4h + (0..3) of its query.
+  if (q < p.seq) {
+    uint16_t* dst = p.dqkv + (row0 + q) * p.ld_dqkv + head * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * j + 4 * h) =
+            u32x2_t{pack_bf16x2(dq[db][4 * j] * p.scale, dq[db][4 * j + 1] * p.scale),
+                    pack_bf16x2(dq[db][4 * j + 2] * p.scale, dq[db][4 * j + 3] * p.scale)};
+  }
+}
+
+}  // namespace
+
+int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads) { return 2 * heads * tokens + 256; }
+
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
+  BwdParams p{};
+  p.qkv = static_cast<const uint16_t*>(a.qkv);
+  p.ld_qkv = a.ld_qkv;
+  p.o = static_cast<const uint16_t*>(a.o);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.ld_o = a.ld_o;
+  p.lse = a.lse;
+  p.ld_lse = a.ld_lse;
+  p.dqkv = static_cast<uint16_t*>(a.dqkv);
+  p.ld_dqkv = a.ld_dqkv;
+  p.stats = a.stats;
+  p.T = a.batch * a.seq;
+  p.hd = a.heads * a.head_dim;
+  p.seq = int(a.seq);
+  p.heads = int(a.heads);
+  p.batch = int(a.batch);
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  const int64_t pairs = p.T * p.heads;
+  note_kernel("attn_bwd_prep_kernel");
+  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((pairs + 15) / 16)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = int((a.seq + kWG - 1) / kWG);
+  note_kernel("attn_bwd_dkdv_kernel");
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  note_kernel("attn_bwd_dq_kernel");
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace domino

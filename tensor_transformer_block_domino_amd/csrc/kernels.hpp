@@ -65,9 +65,24 @@ int64_t gemm_ws_elems(const GemmArgs& g);
 struct AttnArgs {
   const void* qkv; int64_t ld_qkv;   // [T, 3·H·d] = [Q | K | V]
   void* o; int64_t ld_o;             // [T, H·d]
+  float* lse; int64_t ld_lse;        // optional [T, H]: ln Σ_k exp(scale·q·k) per row
   int64_t batch, seq, heads, head_dim;
   float scale;
 };
 hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s);
+
+// Attention backward for one head slice: dQKV [T, 3·H·d] = [dQ | dK | dV] from QKV, O, dO
+// and the forward's LSE. `stats` is scratch of attn_bwd_stats_floats() floats.
+struct AttnBwdArgs {
+  const void* qkv; int64_t ld_qkv;
+  const void* o; const void* dout; int64_t ld_o;
+  const float* lse; int64_t ld_lse;
+  void* dqkv; int64_t ld_dqkv;
+  float* stats;
+  int64_t batch, seq, heads, head_dim;
+  float scale;
+};
+int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads);
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 }  // namespace domino

@@ -129,7 +129,7 @@ class AttnGroup:
     """P ranks of an attention layer (head slices) on one device; rank 0 is measured."""
 
     def __init__(self, *, batch, seq, hidden, heads_shard, head_dim, row_chunks, n_partials, X, Aqkv, Bo,
-                 device="cuda", scale=0.0):
+                 device="cuda", scale=0.0, dY=None):
         self.batch, self.seq, self.hidden = batch, seq, hidden
         self.hs, self.d, self.P, self.row_chunks, self.scale = heads_shard, head_dim, n_partials, row_chunks, scale
         self.T = batch * seq
@@ -146,8 +146,19 @@ class AttnGroup:
         self.O = {r: torch.empty(self.T, hd, **e) for r in range(n_partials)}
         self.Y_own = {r: torch.empty(self.T, hidden, **e) for r in range(n_partials)}
         self.Y = torch.empty(self.T, hidden, **e)
-        nbytes = max(L.domino_attn_block_fwd_workspace_size(d)
-                     for d in (self.desc(), self.desc(rank_alone=True, row_chunks=1)))
+        self.lse = {r: torch.empty(self.T, heads_shard, device=device, dtype=torch.float32) for r in range(n_partials)}
+        if dY is not None:
+            # Backward buffers: dY is the same on every rank (Y was all-reduced).
+            self.dY = dY.to(device=device, dtype=td).contiguous()
+            self.dO = {r: torch.empty(self.T, hd, **e) for r in range(n_partials)}
+            self.dQKV = {r: torch.empty(self.T, 3 * hd, **e) for r in range(n_partials)}
+            self.dX_own = {r: torch.empty(self.T, hidden, **e) for r in range(n_partials)}
+            self.dX = torch.empty(self.T, hidden, **e)
+            self.dA = torch.zeros(hidden, 3 * hd, device=device, dtype=torch.float32)
+            self.dB = torch.zeros(hd, hidden, device=device, dtype=torch.float32)
+        descs = (self.desc(), self.desc(rank_alone=True, row_chunks=1))
+        nbytes = max(max(L.domino_attn_block_fwd_workspace_size(d), L.domino_attn_block_bwd_workspace_size(d))
+                     for d in descs)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.ws_bytes = nbytes
 
@@ -161,9 +172,22 @@ class AttnGroup:
         for r in range(1, self.P):
             L.domino_attn_block_fwd(self.desc(rank_alone=True, row_chunks=1), self.X, self.A_s[r], self.B_s[r],
                                     self.QKV[r], self.O[r], self.Y_own[r], None, None, self.ws, self.ws_bytes,
-                                    stream, None)
+                                    stream, None, lse=self.lse[r])
 
     def forward(self, compute=None, comm=None, **desc_kw):
         peers = [self.Y_own[r] for r in range(1, self.P)] if self.P > 1 else None
         L.domino_attn_block_fwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
-                                self.Y_own[0], peers, self.Y, self.ws, self.ws_bytes, compute, comm)
+                                self.Y_own[0], peers, self.Y, self.ws, self.ws_bytes, compute, comm, lse=self.lse[0])
+
+    def peer_backward(self, stream=None):
+        dA, dB = torch.empty_like(self.dA), torch.empty_like(self.dB)
+        for r in range(1, self.P):
+            L.domino_attn_block_bwd(self.desc(rank_alone=True, row_chunks=1), self.X, self.A_s[r], self.B_s[r],
+                                    self.QKV[r], self.O[r], self.lse[r], self.dY, self.dO[r], self.dQKV[r],
+                                    self.dX_own[r], None, None, dA, dB, 0, self.ws, self.ws_bytes, stream, None)
+
+    def backward(self, compute=None, comm=None, accumulate=0, **desc_kw):
+        peers = [self.dX_own[r] for r in range(1, self.P)] if self.P > 1 else None
+        L.domino_attn_block_bwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
+                                self.lse[0], self.dY, self.dO[0], self.dQKV[0], self.dX_own[0], peers, self.dX,
+                                self.dA, self.dB, accumulate, self.ws, self.ws_bytes, compute, comm)

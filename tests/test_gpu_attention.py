@@ -34,9 +34,11 @@ def test_attention_small(batch, seq, row_chunks):
     check("QKV", f64(g.QKV[0]), QKV_ref, BF16_TOL)
     check("O", f64(g.O[0]), O_ref, BF16_TOL)
     check("Y_own", f64(g.Y_own[0]), Y0_ref, BF16_TOL)
-    # O given the GPU's own (bf16) QKV: isolates the attention kernel.
-    O_from_gpu_qkv = oracle.attention._mha(f64(g.QKV[0]), batch, seq, hs, 128, 1 / np.sqrt(128))
-    check("O | QKV", f64(g.O[0]), O_from_gpu_qkv, 5e-3)
+    # The per-row log-sum-exp the backward uses (fp32 output; absolute error, as it is a log).
+    lse_ref = oracle.attn_lse(QKV_ref, batch, seq, hs, 128)
+    err = float(np.max(np.abs(f64(g.lse[0]) - lse_ref)))
+    print(f"  lse: max abs err {err:.3e}", flush=True)
+    assert err < 0.05, err
 
 
 def test_attention_first_row_is_v0_and_chunks_bitwise():
