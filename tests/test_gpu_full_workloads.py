@@ -79,3 +79,35 @@ def test_full_attention_workload():
         X_seq = oracle.to_f64(inp["X"][b * w.seq:(b + 1) * w.seq])
         ref = oracle.attn_y_rows(X_seq, Aqkv, Bo, w.heads_full, w.head_dim, pos)
         check(f"Y rows (seq {b})", f64(g.Y)[b * w.seq + pos], ref, BF16_TOL)
+
+
+def test_full_attention_backward_workload():
+    """The attention workload's backward at full size (8 ranks of 4 heads, row split x2):
+    rank 0's dO, dQKV and weight gradients in full, and the reduced dX on the first sequence
+    of each row chunk (a sequence's dX depends only on that sequence)."""
+    w = synth.WORKLOADS["gpt3_6p7b_attn_tp8_row"]
+    print("full attention backward: generating inputs", flush=True)
+    inp = synth.attn_inputs(w)
+    g = AttnGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
+                  row_chunks=w.row_chunks, n_partials=w.n_partials, X=inp["X"], Aqkv=inp["Aqkv"], Bo=inp["Bo"],
+                  dY=inp["dY"], device=dev())
+    print("  running the 8 ranks' forward and backward on the GPU", flush=True)
+    g.peer_forward()
+    g.forward(comm=torch.cuda.Stream())
+    g.peer_backward()
+    g.backward(comm=torch.cuda.Stream())
+    sync()
+    X, Aqkv, Bo, dY = (oracle.to_f64(inp[k]) for k in ("X", "Aqkv", "Bo", "dY"))
+    print("  oracle: rank 0's backward over all sequences", flush=True)
+    A0, B0 = oracle.attn_shard_weights(Aqkv, Bo, w.heads_full, w.head_dim, w.n_partials, 0)
+    dO, dQKV, _, dA, dB = oracle.attn_shard_backward(X, A0, B0, dY, w.batch, w.seq, w.heads_shard, w.head_dim)
+    check("dO", f64(g.dO[0]), dO, BF16_TOL)
+    check("dQKV", f64(g.dQKV[0]), dQKV, BF16_TOL)
+    check("dA_qkv_s", f64(g.dA), dA, BF16_TOL)
+    check("dB_o_s", f64(g.dB), dB, BF16_TOL)
+    dX = f64(g.dX)
+    for b in (0, w.batch // w.row_chunks):
+        print(f"  oracle: reduced dX of sequence {b} (all {w.heads_full} heads)", flush=True)
+        r = slice(b * w.seq, (b + 1) * w.seq)
+        ref = oracle.attn_backward_unsharded(X[r], Aqkv, Bo, dY[r], 1, w.seq, w.heads_full, w.head_dim)
+        check(f"dX seq {b}", dX[r], ref, BF16_TOL)
