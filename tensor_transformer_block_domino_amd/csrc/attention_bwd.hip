@@ -131,12 +131,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
 
-  // Grid order: the first half longest key block first (key block 0 sees every query
-  // block), the second half shortest first, so co-resident workgroups balance.
+  // Longest work first (key block 0 sees every query block): with one workgroup per CU, a
+  // CU that finishes a long block early picks up the next longest, which balances the CUs.
   const int nkb = (p.seq + kWG - 1) / kWG, nqb = (p.seq + kBlk - 1) / kBlk;
-  const int hb = p.heads * p.batch, G = nkb * hb, half = (G + 1) / 2;
-  const int lin = blockIdx.x;
-  const int srt = lin < half ? lin : G - 1 - (lin - half);
+  const int hb = p.heads * p.batch;
+  const int srt = blockIdx.x;
   const int kb = srt / hb;
   const int head = (srt % hb) % p.heads;
   const int b = (srt % hb) / p.heads;
@@ -299,11 +298,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
 
-  // Grid order: the first half longest query block first, the second half shortest first.
+  // Longest work first (the last query block sees every key block), as for dK/dV.
   const int nqb = (p.seq + kWG - 1) / kWG;
-  const int hb = p.heads * p.batch, G = nqb * hb, half = (G + 1) / 2;
-  const int lin = blockIdx.x;
-  const int srt = lin < half ? lin : G - 1 - (lin - half);
+  const int hb = p.heads * p.batch;
+  const int srt = blockIdx.x;
   const int qb = nqb - 1 - srt / hb;
   const int head = (srt % hb) % p.heads;
   const int b = (srt % hb) / p.heads;
