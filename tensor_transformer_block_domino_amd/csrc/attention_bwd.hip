@@ -40,7 +40,8 @@ struct BwdParams {
   const uint16_t* o; const uint16_t* dout; int64_t ld_o;
   const float* lse; int64_t ld_lse;
   uint16_t* dqkv; int64_t ld_dqkv;
-  float* stats;          // [heads][T] LSE·log2 e, then [heads][T] Δ, then padding
+  uint16_t* stx;         // [heads][T][8] bf16 stats entries (L = LSE/scale and Δ, three parts each)
+  float* stats;          // [heads][T] LSE·log2 e, then [heads][T] Δ
   int64_t T, hd;
   int seq, heads, batch;
   float scale, scale_log2;
@@ -84,6 +85,21 @@ __device__ __forceinline__ void read_tr_frag(u32x4_t& f, const uint16_t* tile, i
 }
 
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// An accumulation-register operand anywhere in a kernel makes the compiler give its MFMAs
+// their accumulators in AGPRs, which leaves the VGPRs to the operands and the softmax.
+__device__ __forceinline__ void agpr_accumulators() {
+  float z = 0.f;
+  asm volatile("" ::"a"(z));
+}
+
+// x as three bf16 parts whose fp32 sum is x exactly (each part takes the next 8 bits).
+__device__ __forceinline__ void split3(float x, uint32_t& a, uint32_t& b, uint32_t& c) {
+  a = f32_to_bf16_bits(x);
+  const float r = x - bf16_to_f32(uint16_t(a));
+  b = f32_to_bf16_bits(r);
+  c = f32_to_bf16_bits(r - bf16_to_f32(uint16_t(b)));
+}
 __device__ __forceinline__ void tie(u32x4_t& v) { asm volatile("" : "+v"(v)); }
 
 // Scores j = 2tt, 2tt+1 of a 32-row block (16 values) as the 8 bf16 B-operand values of
@@ -93,7 +109,8 @@ __device__ __forceinline__ u32x4_t pack_step(const f32x16_t& v, int tt) {
                  pack_bf16x2(v[8 * tt + 4], v[8 * tt + 5]), pack_bf16x2(v[8 * tt + 6], v[8 * tt + 7])};
 }
 
-// Δ and LSE·log2 e per (token, head): 16 threads per pair, 8 d each, a fixed xor tree.
+// Δ and LSE·log2 e per (token, head): 16 threads per pair, 8 d each, a fixed xor tree; and
+// the pair's stats entry (L_hi, L_mid, L_lo, Δ_hi, Δ_mid, Δ_lo, 0, 0) in bf16, L = LSE/scale.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
   const int64_t item = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
@@ -116,16 +133,31 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
   acc += __shfl_xor(acc, 4);
   acc += __shfl_xor(acc, 8);
   if (ok && j == 0) {
-    p.stats[head * p.T + tok] = p.lse[tok * p.ld_lse + head] * kLog2e;
+    const float lse = p.lse[tok * p.ld_lse + head];
+    p.stats[head * p.T + tok] = lse * kLog2e;
     p.stats[(int64_t(p.heads) + head) * p.T + tok] = acc;
+    uint32_t l0, l1, l2, d0, d1, d2;
+    split3(lse / p.scale, l0, l1, l2);
+    split3(acc, d0, d1, d2);
+    *reinterpret_cast<u32x4_t*>(p.stx + (int64_t(head) * p.T + tok) * 8) =
+        u32x4_t{l0 | (l1 << 16), l2 | (d0 << 16), d1 | (d2 << 16), 0u};
   }
 }
 
 // dK and dV of 128 keys of one (sequence, head).
+//
+// Each wave owns 32 keys; per 32-query half of a block it computes S − L and dP − Δ (the
+// row terms enter as one more MFMA k-step: the query's stats entry times a constant −1
+// column), P = 2^(c·(S − L)) and dS = P·(dP − Δ), then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS.
+// The first two query blocks hold each wave's diagonal half (masked) and the halves that
+// precede its keys (skipped); after them every half is whole, so the main loop has no
+// branches and no masks. Query rows past the sequence are copied as zeros (Q, dO and the
+// stats entry), which makes their contributions zero without a mask.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][kBlk * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t sO[2][kBlk * kD];
-  __shared__ __attribute__((aligned(1024))) float sSt[2][256];  // LSE·log2 e [64], Δ [64], copy tail
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[2][kBlk * 8];  // stats entries of the block's queries
+  agpr_accumulators();
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,13 +171,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int kb = srt / hb;
   const int head = (srt % hb) % p.heads;
   const int b = (srt % hb) / p.heads;
+  (void)nkb;
 
   const int64_t row0 = int64_t(b) * p.seq;
   const uint16_t* Qg = p.qkv + head * kD;
   const uint16_t* Kg = p.qkv + p.hd + head * kD;
   const uint16_t* Vg = p.qkv + 2 * p.hd + head * kD;
   const uint16_t* dOg = p.dout + head * kD;
-  const float* stg = p.stats + head * p.T + row0;
+  const uint16_t* Xg = p.stx + (int64_t(head) * p.T + row0) * 8;
 
   const int k0 = kb * kWG;
   const int kw = k0 + w * 32;   // this wave's first key
@@ -158,6 +191,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     kf[s] = key < p.seq ? ld_frag(Kg + (row0 + key) * p.ld_qkv + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
     vf[s] = key < p.seq ? ld_frag(Vg + (row0 + key) * p.ld_qkv + s * 16 + h * 8) : u32x4_t{0u, 0u, 0u, 0u};
   }
+  // B operands of the stats step: −1 at k = 0..2 (L) or k = 3..5 (Δ) for lanes 0–31; the
+  // lanes 32–63 hold k = 8..15, which are zero.
+  const u32x4_t ys = h == 0 ? u32x4_t{0xBF80BF80u, 0x0000BF80u, 0u, 0u} : u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t yd = h == 0 ? u32x4_t{0u, 0xBF800000u, 0xBF80BF80u, 0u} : u32x4_t{0u, 0u, 0u, 0u};
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -172,101 +209,95 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const int q0 = qb * kBlk;
     cq.issue(Qg + (row0 + q0) * p.ld_qkv, sQ[st], p.seq - q0, w);
     co.issue(dOg + (row0 + q0) * p.ld_o, sO[st], p.seq - q0, w);
-    if (w == 0) {
-      // lanes 0–15: LSE·log2 e of the block's 64 queries; lanes 16–31: their Δ (values past
-      // the sequence belong to the next one and are masked; the buffer is padded at its end).
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint16_t*>(stg + q0));
-      const int32_t o = lane < 16 ? 16 * lane : lane < 32 ? int32_t(int64_t(p.heads) * p.T * 4) + 16 * (lane - 16) : kOOB;
-      dma16(rs, reinterpret_cast<uint16_t*>(sSt[st]), o);
-    }
+    if (w == 0) dma16(make_rsrc(Xg + int64_t(q0) * 8), sX[st], lane < p.seq - q0 ? 16 * lane : kOOB);
   };
 
   const float c = p.scale_log2;
+  // One 32-query half of stage st. diag: the half whose first query is this wave's first
+  // key; query 8j + 4h + r of the half sees the lane's key iff l32 ≤ 8j + 4h + r.
+  auto half = [&](int st, int nb, bool diag) {
+    u32x4_t sx, qr[8], dr[8];
+    lds_read_b128(sx, &sX[st][(nb * 32 + l32) * 8]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      lds_read_b128(qr[s], &sQ[st][t_off(nb * 32 + l32, 2 * s + h)]);
+      lds_read_b128(dr[s], &sO[st][t_off(nb * 32 + l32, 2 * s + h)]);
+    }
+    const f32x16_t zero = {};
+    lgkm_wait_tied1(8, sx);
+    f32x16_t sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, sx),
+                                                           __builtin_bit_cast(bf16x8_t, ys), zero, 0, 0, 0);
+    f32x16_t pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, sx),
+                                                           __builtin_bit_cast(bf16x8_t, yd), zero, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      // Issued so far: sx, then the pairs 0..min(s, 4) + 3; pair s is 2s+1, 2s+2.
+      lgkm_wait_tied(6 + 2 * (s < 4 ? s : 4) - 2 * s, qr[s], dr[s]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qr[s]),
+                                                    __builtin_bit_cast(bf16x8_t, kf[s]), sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dr[s]),
+                                                    __builtin_bit_cast(bf16x8_t, vf[s]), pacc, 0, 0, 0);
+      if (s + 4 < 8) {
+        lds_read_b128(qr[s + 4], &sQ[st][t_off(nb * 32 + l32, 2 * (s + 4) + h)]);
+        lds_read_b128(dr[s + 4], &sO[st][t_off(nb * 32 + l32, 2 * (s + 4) + h)]);
+      }
+    }
+    // Transposed dO and Q for the half's two 16-query steps (4 reads per (tt, db)).
+    u32x4_t dot[2][4], qt[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        read_tr_frag(dot[tt][db], sO[st], 2 * nb + tt, db, lane);
+        read_tr_frag(qt[tt][db], sQ[st], 2 * nb + tt, db, lane);
+      }
+    f32x16_t pm, ds;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pe = __builtin_amdgcn_exp2f(sacc[e] * c);
+      if (diag) pe = l32 <= 8 * (e >> 2) + 4 * h + (e & 3) ? pe : 0.f;
+      pm[e] = pe;
+      ds[e] = pe * pacc[e];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const u32x4_t pf = pack_step(pm, tt), sf = pack_step(ds, tt);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int i = 4 * tt + db;
+        lgkm_wait_tied(28 - 4 * i < 15 ? 28 - 4 * i : 15, dot[tt][db], qt[tt][db]);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dot[tt][db]),
+                                                        __builtin_bit_cast(bf16x8_t, pf), dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qt[tt][db]),
+                                                        __builtin_bit_cast(bf16x8_t, sf), dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // The first two blocks: half i (= 2·block + nb) is wave i's diagonal, earlier ones are
+  // skipped by it.
   issue(qb0, 0);
-  for (int qb = qb0; qb < nqb; ++qb) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qb = qb0 + i;
+    if (qb >= nqb) break;
+    wait_vm_barrier<0>();
+    if (qb + 1 < nqb) issue(qb + 1, (i + 1) & 1);
+    if (kw < p.seq) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int hx = 2 * i + nb;
+        if (hx == w) half(i, nb, true);
+        else if (hx > w) half(i, nb, false);
+      }
+    }
+  }
+  for (int qb = qb0 + 2; qb < nqb; ++qb) {
     const int st = (qb - qb0) & 1;
     wait_vm_barrier<0>();
     if (qb + 1 < nqb) issue(qb + 1, st ^ 1);
-    const int q0 = qb * kBlk;
-    if (q0 + kBlk - 1 < kw || kw >= p.seq) continue;  // every query of the block precedes these keys
-
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int qn = q0 + nb * 32;  // first query of this 32-query half
-      if (qn + 31 < kw) continue;   // wave-uniform
-      // The LSE·log2 e and Δ of queries qn + 8j + 4h + (0..3), read first; then
-      // S[query][key] and dP[query][key] for those queries (X = the tile's rows).
-      u32x4_t lse4[4], del4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lds_read_b128(lse4[j], &sSt[st][nb * 32 + 8 * j + 4 * h]);
-        lds_read_b128(del4[j], &sSt[st][64 + nb * 32 + 8 * j + 4 * h]);
-      }
-      u32x4_t qr[8], dr[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        lds_read_b128(qr[s], &sQ[st][t_off(nb * 32 + l32, 2 * s + h)]);
-        lds_read_b128(dr[s], &sO[st][t_off(nb * 32 + l32, 2 * s + h)]);
-      }
-      f32x16_t sacc, pacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        lgkm_wait_tied(14 - 2 * s, qr[s], dr[s]);  // reads complete in order
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qr[s]),
-                                                      __builtin_bit_cast(bf16x8_t, kf[s]), sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dr[s]),
-                                                      __builtin_bit_cast(bf16x8_t, vf[s]), pacc, 0, 0, 0);
-      }
-      // Every read issued so far has landed (the last wait above was lgkmcnt(0)).
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        tie(lse4[j]);
-        tie(del4[j]);
-      }
-      // Transposed dO and Q for this half's two 16-query steps.
-      u32x4_t dot[2][4], qt[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          read_tr_frag(dot[tt][db], sO[st], 2 * nb + tt, db, lane);
-          read_tr_frag(qt[tt][db], sQ[st], 2 * nb + tt, db, lane);
-        }
-      // P and dS; query qn + 8j + 4h + r sees the key iff key ≤ query < seq.
-      const bool edge = qn < kw + 31 || qn + 32 > p.seq;  // wave-uniform
-      const int lo = key - qn - 4 * h, hi = p.seq - 1 - qn - 4 * h;
-      f32x16_t pm, ds;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = e >> 2, r = e & 3, off = 8 * j + r;
-        const float l2 = __uint_as_float(lse4[j][r]), dl = __uint_as_float(del4[j][r]);
-        float pe = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -l2));
-        if (edge) pe = off >= lo && off <= hi ? pe : 0.f;
-        pm[e] = pe;
-        ds[e] = pe * (pacc[e] - dl);
-      }
-      lds_wait_all();
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          tie(dot[tt][db]);
-          tie(qt[tt][db]);
-        }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const u32x4_t pf = pack_step(pm, tt), sf = pack_step(ds, tt);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, dot[tt][db]),
-                                                          __builtin_bit_cast(bf16x8_t, pf), dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qt[tt][db]),
-                                                          __builtin_bit_cast(bf16x8_t, sf), dk[db], 0, 0, 0);
-        }
-      }
-    }
+    half(st, 0, false);
+    half(st, 1, false);
   }
   // No LDS write may land after the workgroup ends.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -426,7 +457,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
 
 }  // namespace
 
-int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads) { return 2 * heads * tokens + 256; }
+// Stats entries first (16 bytes per (token, head), so they stay 16-byte aligned), then the
+// two fp32 arrays.
+int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads) { return 6 * heads * tokens; }
 
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s) {
   if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
@@ -440,8 +473,9 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.ld_lse = a.ld_lse;
   p.dqkv = static_cast<uint16_t*>(a.dqkv);
   p.ld_dqkv = a.ld_dqkv;
-  p.stats = a.stats;
   p.T = a.batch * a.seq;
+  p.stx = reinterpret_cast<uint16_t*>(a.stats);
+  p.stats = a.stats + 4 * p.T * a.heads;
   p.hd = a.heads * a.head_dim;
   p.seq = int(a.seq);
   p.heads = int(a.heads);

@@ -123,6 +123,29 @@ __device__ __forceinline__ void lgkm_wait_tied(int n, u32x4_t& a, u32x4_t& b) {
   }
 }
 
+// The same wait tying one register group.
+__device__ __forceinline__ void lgkm_wait_tied1(int n, u32x4_t& a) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)); break;
+    case 1: asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(a)); break;
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a)); break;
+    case 3: asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a)); break;
+    case 4: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a)); break;
+    case 5: asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(a)); break;
+    case 6: asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(a)); break;
+    case 7: asm volatile("s_waitcnt lgkmcnt(7)" : "+v"(a)); break;
+    case 8: asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(a)); break;
+    case 9: asm volatile("s_waitcnt lgkmcnt(9)" : "+v"(a)); break;
+    case 10: asm volatile("s_waitcnt lgkmcnt(10)" : "+v"(a)); break;
+    case 11: asm volatile("s_waitcnt lgkmcnt(11)" : "+v"(a)); break;
+    case 12: asm volatile("s_waitcnt lgkmcnt(12)" : "+v"(a)); break;
+    case 13: asm volatile("s_waitcnt lgkmcnt(13)" : "+v"(a)); break;
+    case 14: asm volatile("s_waitcnt lgkmcnt(14)" : "+v"(a)); break;
+    case 15: asm volatile("s_waitcnt lgkmcnt(15)" : "+v"(a)); break;
+    default: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)); break;
+  }
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight and all its
 // LDS operations are done, then barrier. A workgroup fence would wait for every LDS
 // write in flight (vmcnt(0)), which serialises the stage ring, so the wait is explicit.
