@@ -11,6 +11,12 @@ Prints one JSON line: value = rank's fwd+bwd GEMM-chain TFLOP/s (algorithmic FLO
 3 × 2·T·h·(n1 + f_s)), plus a roofline object for the dominant kernel (its average launch
 time measured with HIP events recorded on its own stream by the library) and the CPU
 oracle's throughput on this host.
+
+`--workload gpt3_6p7b_attn_tp8_row` measures the attention block of one rank instead (QKV
+product, causal attention over the rank's heads, out-projection per chunk and its
+reduction; then the backward: dO, the attention backward, dX per chunk and its reduction,
+both weight gradients), with algorithmic FLOPs 3 × (the three products) + 3.5 × the causal
+attention's 4·d·S(S+1)/2 per (sequence, head).
 """
 from __future__ import annotations
 
@@ -22,6 +28,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402  (seeded input generators; no arithmetic of the method)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
@@ -115,6 +123,154 @@ def cpu_baseline(w, inp, reps):
                       f"{reps} reps, {best:.2f} s each"}
 
 
+def attn_flops(w):
+    """Algorithmic FLOPs per step of each timed role of the attention block (one rank)."""
+    T, h, hd = w.tokens, w.hidden, w.heads_shard * w.head_dim
+    att = 4.0 * w.head_dim * w.seq * (w.seq + 1) / 2 * w.heads_shard * w.batch
+    return {
+        "qkv": 2.0 * T * h * 3 * hd, "attn": att, "outproj": 2.0 * T * hd * h,
+        "outproj_dgrad": 2.0 * T * h * hd,
+        # dK/dV kernel: S, dP, dV, dK over the causal pairs; dQ kernel: dQ (it also
+        # computes S and dP again, which is not counted).
+        "attn_bwd_prep": 0.0, "attn_bwd_dkdv": 2.0 * att, "attn_bwd_dq": 0.5 * att,
+        "qkv_dgrad": 2.0 * T * 3 * hd * h, "outproj_wgrad": 2.0 * T * hd * h, "qkv_wgrad": 2.0 * T * h * 3 * hd,
+    }
+
+
+def cpu_baseline_attn(w, inp, reps, n_seq=2):
+    """The oracle (numpy fp64) on this host: one rank's attention forward + backward over the
+    first n_seq sequences of the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = n_seq * w.seq
+    X, Aqkv, Bo, dY = (oracle.to_f64(inp[k]) for k in ("X", "Aqkv", "Bo", "dY"))
+    A0, B0 = oracle.attn_shard_weights(Aqkv, Bo, w.heads_full, w.head_dim, w.n_partials, 0)
+    A0, B0 = np.ascontiguousarray(A0), np.ascontiguousarray(B0)
+    X, dY = np.ascontiguousarray(X[:rows]), np.ascontiguousarray(dY[:rows])
+    sub = synth.AttnWorkload(w.name, batch=n_seq, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard,
+                             head_dim=w.head_dim, dtype=w.dtype, row_chunks=1, n_partials=w.n_partials, seed=w.seed)
+    total = sum(attn_flops(sub).values())
+    best = None
+    for _ in range(max(1, reps)):
+        t0 = time.perf_counter()
+        oracle.attn_shard_forward(X, A0, B0, n_seq, w.seq, w.heads_shard, w.head_dim)
+        oracle.attn_shard_backward(X, A0, B0, dY, n_seq, w.seq, w.heads_shard, w.head_dim)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+        if time.perf_counter() - t0 > 30:
+            break
+    return {"value": total / best / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one rank's attention forward+backward over {n_seq} of the {w.batch} sequences of {w.name} "
+                      f"(fp64 numpy), best of {reps} reps, {best:.2f} s each"}
+
+
+def main_attn(args, w):
+    import torch
+
+    import tensor_transformer_block_domino_amd as D
+    from tensor_transformer_block_domino_amd.tp_sim import AttnGroup
+
+    dev = torch.device("cuda:0")
+    inp = synth.attn_inputs(w)
+    g = AttnGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
+                  row_chunks=w.row_chunks, n_partials=w.n_partials, X=inp["X"], Aqkv=inp["Aqkv"], Bo=inp["Bo"],
+                  dY=inp["dY"], device=dev)
+    g.peer_forward()
+    g.forward()
+    g.peer_backward()
+    torch.cuda.synchronize()
+    compute = torch.cuda.Stream()
+    comm = torch.cuda.Stream()
+
+    def step_domino():
+        g.forward(compute, comm, no_join=1)
+        g.backward(compute, comm)
+
+    def step_unsplit():
+        g.forward(compute, None, rank_alone=True, row_chunks=1)
+        g.backward(compute, None, rank_alone=True, row_chunks=1)
+
+    ms = timed_steps(step_domino, args.steps, args.warmup)
+    print(f"[bench] attention domino step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms_unsplit = timed_steps(step_unsplit, args.steps, 2)
+
+    D.domino_timing_enable(True)
+    for _ in range(args.steps):
+        step_domino()
+    torch.cuda.synchronize()
+    fl = attn_flops(w)
+    roles = list(fl) + ["reduce", "aux"]
+    per = {r: D.domino_timing_read(r) for r in roles}
+    kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
+    D.domino_timing_enable(False)
+    total_flops = sum(fl.values())
+    value = total_flops / (ms * 1e-3) / 1e12
+    by_kernel = {}
+    for r in fl:
+        if fl[r] > 0:
+            by_kernel.setdefault(kernel_of[r], []).append(r)
+    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
+    n_dom = sum(per[r][0] for r in by_kernel[dom])
+    tot_dom = sum(per[r][1] for r in by_kernel[dom])
+    flops_dom = sum(fl[r] for r in by_kernel[dom]) * args.steps
+    achieved = flops_dom / (tot_dom * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "heads_shard": w.heads_shard, "head_dim": w.head_dim, "tp_partials": w.n_partials,
+                   "split": f"rows x{w.row_chunks}", "pass": "fwd+bwd", "attention": "causal"},
+        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "t_domino_ms": round(ms, 4),
+        "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
+        "t_reduce_ms": round(per["reduce"][1] / args.steps, 4),
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
+        "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
+                          for r in fl if fl[r] > 0 and per[r][1] > 0},
+        "kernel_of_role": kernel_of,
+        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(tot_dom / max(1, n_dom) * 1e3, 2), "launches": n_dom,
+                     "flops_per_launch": flops_dom / max(1, n_dom)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_attn(w, inp, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+def timed_steps(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -123,7 +279,6 @@ def main():
         sys.exit(2)
     import torch
 
-    import synth
     import tensor_transformer_block_domino_amd as D
     from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
 
@@ -136,6 +291,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
+    if isinstance(w, synth.AttnWorkload):
+        return main_attn(args, w)
     assert isinstance(w, synth.MlpWorkload) and w.dtype == "bf16"
     dev = torch.device("cuda:0")
     inp = synth.mlp_inputs(w)

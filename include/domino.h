@@ -244,12 +244,14 @@ typedef enum {
   DOMINO_K_ATTN = 8,
   DOMINO_K_OUTPROJ = 9,
   DOMINO_K_AUX = 10,        /* k-split tiles' fixed-order slice sums with their epilogues */
-  DOMINO_K_ATTN_BWD = 11,   /* attention backward: Δ, dK/dV and dQ kernels */
+  DOMINO_K_ATTN_BWD = 11,   /* attention backward: the dK/dV kernel */
   DOMINO_K_OUTPROJ_DGRAD = 12,  /* dY·B_o_sᵀ */
   DOMINO_K_QKV_DGRAD = 13,  /* dQKV·A_qkv_sᵀ */
   DOMINO_K_OUTPROJ_WGRAD = 14,  /* Oᵀ·dY */
   DOMINO_K_QKV_WGRAD = 15,  /* Xᵀ·dQKV */
-  DOMINO_K_COUNT = 16
+  DOMINO_K_ATTN_BWD_DQ = 16,    /* attention backward: the dQ kernel */
+  DOMINO_K_ATTN_BWD_PREP = 17,  /* attention backward: Δ and the per-row statistics */
+  DOMINO_K_COUNT = 18
 } domino_kernel_kind;
 
 domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */

@@ -19,8 +19,8 @@ DOMINO_MAX_PARTIALS = 16
 STATUS_NAMES = {0: "DOMINO_OK", 1: "DOMINO_ERR_INVALID_ARG", 2: "DOMINO_ERR_SHAPE", 3: "DOMINO_ERR_ALIGN",
                 4: "DOMINO_ERR_UNSUPPORTED", 5: "DOMINO_ERR_HIP"}
 KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgrad_a": 4, "wgrad_b": 5,
-                "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10, "attn_bwd": 11, "outproj_dgrad": 12,
-                "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15}
+                "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10, "attn_bwd_dkdv": 11, "outproj_dgrad": 12,
+                "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15, "attn_bwd_dq": 16, "attn_bwd_prep": 17}
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",

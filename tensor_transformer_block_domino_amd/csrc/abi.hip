@@ -713,8 +713,12 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
     ab.scale = scale;
     if (hip_ok(run_gemm(DOMINO_K_OUTPROJ_DGRAD, attn_dout(d, dY, B_o_s, dO), workspace, workspace_bytes, sc.cs), &msg,
                "dO GEMM") ||
-        hip_ok(timed(DOMINO_K_ATTN_BWD, sc.cs, [&] { return launch_attention_bwd(ab, sc.cs); }), &msg,
-               "attention backward"))
+        hip_ok(timed(DOMINO_K_ATTN_BWD_PREP, sc.cs, [&] { return launch_attention_bwd_prep(ab, sc.cs); }), &msg,
+               "attention backward statistics") ||
+        hip_ok(timed(DOMINO_K_ATTN_BWD, sc.cs, [&] { return launch_attention_bwd_dkdv(ab, sc.cs); }), &msg,
+               "attention backward dK/dV") ||
+        hip_ok(timed(DOMINO_K_ATTN_BWD_DQ, sc.cs, [&] { return launch_attention_bwd_dq(ab, sc.cs); }), &msg,
+               "attention backward dQ"))
       return fail(DOMINO_ERR_HIP, msg);
   }
   for (int i = 0; i < d->row_chunks && tok; ++i) {

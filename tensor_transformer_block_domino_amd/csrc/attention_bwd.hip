@@ -461,8 +461,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
 // two fp32 arrays.
 int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads) { return 6 * heads * tokens; }
 
-hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s) {
-  if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
+namespace {
+BwdParams bwd_params(const AttnBwdArgs& a) {
   BwdParams p{};
   p.qkv = static_cast<const uint16_t*>(a.qkv);
   p.ld_qkv = a.ld_qkv;
@@ -482,17 +482,33 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.batch = int(a.batch);
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  const int64_t pairs = p.T * p.heads;
+  return p;
+}
+}  // namespace
+
+hipError_t launch_attention_bwd_prep(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
+  const BwdParams p = bwd_params(a);
   note_kernel("attn_bwd_prep_kernel");
-  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((pairs + 15) / 16)), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((p.T * p.heads + 15) / 16)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
+  const BwdParams p = bwd_params(a);
   const int nkb = int((a.seq + kWG - 1) / kWG);
   note_kernel("attn_bwd_dkdv_kernel");
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd_dq(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
+  const BwdParams p = bwd_params(a);
+  const int nqb = int((a.seq + kWG - 1) / kWG);
   note_kernel("attn_bwd_dq_kernel");
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(nqb * p.heads * p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -83,6 +83,9 @@ struct AttnBwdArgs {
   float scale;
 };
 int64_t attn_bwd_stats_floats(int64_t tokens, int64_t heads);
-hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t s);
+// The three launches in order: Δ and the stats entries; dK, dV; dQ.
+hipError_t launch_attention_bwd_prep(const AttnBwdArgs& a, hipStream_t s);
+hipError_t launch_attention_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s);
+hipError_t launch_attention_bwd_dq(const AttnBwdArgs& a, hipStream_t s);
 
 }  // namespace domino

@@ -142,6 +142,13 @@ def test_attn_rejects(lib):
             D.domino_attn_block_fwd(ad(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
 
 
+def test_every_timing_kind_is_readable(lib):
+    D.domino_timing_enable(False)
+    for kind in D.KERNEL_KINDS:
+        assert D.domino_timing_read(kind) == (0, 0.0)
+    assert max(D.KERNEL_KINDS.values()) == len(D.KERNEL_KINDS) - 1
+
+
 def test_timing_read_rejects_bad_kind(lib):
     with pytest.raises(D.DominoError):
         D.domino_timing_read(99)
