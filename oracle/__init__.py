@@ -20,13 +20,17 @@ Sources (web pages, by title and section):
             (column-parallel and row-parallel linear layers; FFN = column then row).
   [Overlap] "04 · TP/SP 的通信-计算 overlap 与工程优化", §1 "粗粒度：dgrad 通信 ∥ wgrad 计算"
             (grad_input = grad_output·Wᵀ needs the reduce; grad_weight is local).
+  The layer (layer.py) follows [Domino] "前向：多个计算片段轮转重叠 AllReduce" (attention,
+  then the small kernels Dropout, Residual, LayerNorm, then the MLP) and the
+  DominoTransformerLayer excerpt under "μ-batch 流水" (pre-LayerNorm block).
 
 Readings where the pages are silent (each listed with its basis in the design doc):
   GeLU is the tanh form; SwiGLU is silu(gate)*up with A's columns [gate | up];
   shards are contiguous equal column blocks of A and the matching row blocks of B
   (contiguous head blocks for attention); the row split is along batch with
   torch.chunk sizes; attention is causal self-attention with scale 1/sqrt(d) and
-  no bias, dropout or rotary embedding.
+  no bias, dropout or rotary embedding; LayerNorm uses the biased variance and eps 1e-5
+  inside the root; dropout is inverted dropout with a given keep mask.
 
 Every function below is pinned by tests/test_oracle_pins.py (brute-force scalar
 loops, the split and shard-sum identities, finite differences, closed forms and
@@ -43,4 +47,8 @@ from .attention import (  # noqa: F401
     attn_shard_weights, causal_attention, attn_shard_forward, attn_forward_unsharded,
     attn_y_rows, domino_attn_forward, causal_attention_lse, causal_attention_backward,
     attn_lse, attn_shard_backward, attn_backward_unsharded, domino_attn_backward,
+)
+from .layer import (  # noqa: F401
+    LN_EPS, unpack_keep, dropout, layer_norm, layer_norm_backward, resid_group_forward,
+    resid_group_backward, layer_forward, layer_backward, stack_forward, stack_backward,
 )

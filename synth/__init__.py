@@ -12,6 +12,12 @@ Recipe (one CPU generator per workload, seeded; draws in this fixed order):
               (columns [gate | up], gate first), 1 for GeLU.
   attention:  X ~ N(0,1) [T, h];  Aqkv ~ N(0,1)*0.02 [h, 3*H*d] (columns [Q | K | V]);
               Bo ~ N(0,1)*0.02 [H*d, h]
+  group:      resid ~ N(0,1) [T, h];  y ~ N(0,1) [T, h];  bias ~ N(0,1)*0.02 [h];
+              gamma ~ 1 + N(0,1)*0.1 [h];  beta ~ N(0,1)*0.1 [h];  keep: uniform u [T, h],
+              kept where u >= p;  d_ln ~ N(0,1) [T, h];  d_res ~ N(0,1) [T, h]
+  layer:      X ~ N(0,1) [T, h]; then per layer: ln1 gamma, beta; Aqkv; Bo; ln2 gamma, beta;
+              A; B (as above); keep1, keep2; finally dY ~ N(0,1) [T, h]
+Keep masks are bit-packed: element j of a row is bit j % 32 of int32 word j // 32.
 Draws are fp32 (torch.randn on a CPU torch.Generator); bf16 workloads then round
 each tensor to nearest-even bf16, and consumers read those exact values.
 The 0.02 scale is a standard deviation (the plain reading of the N(0, 0.02)
@@ -25,7 +31,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["MlpWorkload", "AttnWorkload", "WORKLOADS", "mlp_inputs", "attn_inputs", "workload"]
+__all__ = ["MlpWorkload", "AttnWorkload", "LayerWorkload", "WORKLOADS", "mlp_inputs", "attn_inputs",
+           "group_inputs", "layer_inputs", "pack_keep", "workload"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -78,6 +85,36 @@ class AttnWorkload:
         return self.n_partials * self.heads_shard
 
 
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    """A stack of pre-LayerNorm transformer layers (attention + MLP) on one rank."""
+    name: str
+    batch: int
+    seq: int
+    hidden: int
+    heads_shard: int
+    head_dim: int
+    ffn_shard: int
+    act: str
+    row_chunks: int         # μ-batches (whole sequences)
+    n_partials: int
+    layers: int
+    p_drop: float
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def heads_full(self) -> int:
+        return self.n_partials * self.heads_shard
+
+    @property
+    def ffn_full(self) -> int:
+        return self.n_partials * self.ffn_shard
+
+
 # The five workloads: a tiny fp32 MLP simulating TP=2, and layers shaped like
 # GPT-3 2.7B / 6.7B and Llama-2 7B / 13B at TP=8.
 WORKLOADS = {
@@ -96,6 +133,11 @@ WORKLOADS = {
     "llama2_13b_swiglu_tp8_2d": MlpWorkload(
         "llama2_13b_swiglu_tp8_2d", batch=8, seq=4096, hidden=5120, ffn_shard=1728, act="swiglu",
         dtype="bf16", row_chunks=2, col_chunks=2, n_partials=8, backward=True, seed=4),
+    # Whole layers of the GPT-3 6.7B shape (the attention workload's shard plus its MLP,
+    # 4·h / 8 FFN columns per rank), two μ-batches, hidden dropout 0.1.
+    "gpt3_6p7b_layer_tp8_row": LayerWorkload(
+        "gpt3_6p7b_layer_tp8_row", batch=8, seq=2048, hidden=4096, heads_shard=4, head_dim=128, ffn_shard=2048,
+        act="gelu_tanh", row_chunks=2, n_partials=8, layers=2, p_drop=0.1, seed=5),
 }
 
 
@@ -142,6 +184,56 @@ def attn_inputs(w: AttnWorkload, *, seed: Optional[int] = None, tokens: Optional
     Bo = torch.randn(Hd, h, generator=g, dtype=torch.float32) * 0.02
     dY = torch.randn(T, h, generator=g, dtype=torch.float32)
     return {k: _cast(v, w.dtype) for k, v in dict(X=X, Aqkv=Aqkv, Bo=Bo, dY=dY).items()}
+
+
+def pack_keep(keep: torch.Tensor) -> torch.Tensor:
+    """Bool [rows, h] -> int32 words [rows, ceil(h/32)]: element j is bit j % 32 of word j // 32."""
+    import numpy as np
+
+    rows, h = keep.shape
+    words = (h + 31) // 32
+    b = np.packbits(keep.numpy().astype(np.uint8), axis=1, bitorder="little")
+    b = np.pad(b, ((0, 0), (0, 4 * words - b.shape[1])))
+    return torch.from_numpy(np.ascontiguousarray(b).view("<i4").copy())
+
+
+def _keep(g: torch.Generator, rows: int, h: int, p: float) -> torch.Tensor:
+    return pack_keep(torch.rand(rows, h, generator=g, dtype=torch.float32) >= p)
+
+
+def group_inputs(rows: int, hidden: int, *, seed: int, p: float = 0.1):
+    """Inputs of the residual/LayerNorm group and of its backward (bf16, keep mask int32)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    out = dict(resid=torch.randn(rows, hidden, generator=g), y=torch.randn(rows, hidden, generator=g),
+               bias=torch.randn(hidden, generator=g) * 0.02,
+               gamma=1.0 + torch.randn(hidden, generator=g) * 0.1, beta=torch.randn(hidden, generator=g) * 0.1)
+    keep = _keep(g, rows, hidden, p)
+    out.update(d_ln=torch.randn(rows, hidden, generator=g), d_res=torch.randn(rows, hidden, generator=g))
+    out = {k: v.to(torch.bfloat16) for k, v in out.items()}
+    out["keep"] = keep
+    return out
+
+
+def layer_inputs(w: LayerWorkload, *, layers: Optional[int] = None):
+    """X, per-layer parameters and keep masks, and dY of a stack (bf16; masks int32)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    T, h, Hd, F = w.tokens, w.hidden, w.heads_full * w.head_dim, w.ffn_full
+    n_a = 2 if w.act == "swiglu" else 1
+    bf = lambda t: t.to(torch.bfloat16)  # noqa: E731
+    X = bf(torch.randn(T, h, generator=g))
+    per = []
+    for _ in range(w.layers if layers is None else layers):
+        prm = dict(ln1_g=bf(1.0 + torch.randn(h, generator=g) * 0.1), ln1_b=bf(torch.randn(h, generator=g) * 0.1),
+                   Aqkv=bf(torch.randn(h, 3 * Hd, generator=g) * 0.02), Bo=bf(torch.randn(Hd, h, generator=g) * 0.02),
+                   ln2_g=bf(1.0 + torch.randn(h, generator=g) * 0.1), ln2_b=bf(torch.randn(h, generator=g) * 0.1),
+                   A=bf(torch.randn(h, n_a * F, generator=g) * 0.02), B=bf(torch.randn(F, h, generator=g) * 0.02))
+        prm["keep1"] = _keep(g, T, h, w.p_drop)
+        prm["keep2"] = _keep(g, T, h, w.p_drop)
+        per.append(prm)
+    dY = bf(torch.randn(T, h, generator=g))
+    return dict(X=X, layers=per, dY=dY)
 
 
 def randn(shape, *, seed: int, dtype: str = "bf16", scale: float = 1.0) -> torch.Tensor:
