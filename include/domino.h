@@ -219,6 +219,53 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* desc, const void* X,
                                     hipStream_t compute, hipStream_t comm);
 size_t domino_attn_block_bwd_workspace_size(const domino_attn_desc* desc);
 
+/*
+ * The small-kernel group between sublayers (deep-dive, "前向：多个计算片段轮转重叠 AllReduce":
+ * the Dropout, Residual and LayerNorm kernels that hide an AllReduce; the layer excerpt
+ * under "μ-batch 流水"), fused into one pass over the rows. bf16, rows × hidden contiguous;
+ * hidden a multiple of 8, at most 8192; 0 <= p_drop < 1; eps > 0.
+ */
+typedef struct {
+  int64_t rows, hidden;
+  float eps;        /* LayerNorm epsilon, inside the root */
+  float p_drop;     /* dropout probability; kept values are scaled by 1/(1 − p_drop) */
+} domino_group_desc;
+
+/*
+ * domino_resid_ln_fwd:
+ *   resid_out = resid + dropout(y + bias)     (y NULL: resid_out = resid; bias NULL: 0;
+ *                                              keep NULL: no dropout)
+ *   ln_out = (resid_out − μ)·rstd·gamma + beta, μ and σ² over the row (biased variance),
+ *   rstd = 1/√(σ² + eps), computed from the stored bf16 resid_out; mean, rstd [rows] fp32
+ *   saved for the backward. gamma NULL: no LayerNorm (ln_out, beta, mean, rstd unused);
+ *   beta NULL: 0.
+ *   keep: bit-packed [rows][ceil(hidden/32)] int32 words, element j of a row kept iff bit
+ *   j % 32 of word j / 32 is set. resid_out may alias resid. Fp32 arithmetic, one rounding
+ *   per output.
+ */
+domino_status domino_resid_ln_fwd(const domino_group_desc* desc, const void* resid, const void* y,
+                                  const void* bias, const int32_t* keep, void* resid_out, const void* gamma,
+                                  const void* beta, void* ln_out, float* mean, float* rstd, hipStream_t stream);
+
+/*
+ * domino_resid_ln_bwd: the backward of domino_resid_ln_fwd.
+ *   d_resid = d_res + LayerNorm'(d_ln)  (d_res NULL: 0; d_ln NULL: no LayerNorm term)
+ *     with g = d_ln·gamma, x̂ = (resid_out − mean)·rstd:
+ *     LayerNorm'(d_ln) = rstd·(g − mean_row(g) − x̂·mean_row(g·x̂))
+ *   d_y = dropout'(d_resid) = keep ? d_resid/(1 − p_drop) : 0   (NULL: not stored)
+ *   d_gamma (+)= Σ_rows d_ln·x̂, d_beta (+)= Σ_rows d_ln, d_bias (+)= Σ_rows d_y   [hidden] fp32,
+ *   each NULL to skip; accumulate != 0 adds to their contents. Column sums are per-block
+ *   partials in the workspace, summed in a fixed order (deterministic).
+ *   resid_out, mean, rstd, gamma: from the forward (needed when d_ln is given).
+ *   d_resid may alias d_res. workspace: at least domino_resid_ln_bwd_workspace_size bytes.
+ */
+domino_status domino_resid_ln_bwd(const domino_group_desc* desc, const void* d_ln, const void* d_res,
+                                  const void* resid_out, const float* mean, const float* rstd, const void* gamma,
+                                  const int32_t* keep, void* d_resid, void* d_y, float* d_gamma, float* d_beta,
+                                  float* d_bias, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+size_t domino_resid_ln_bwd_workspace_size(const domino_group_desc* desc);
+
 /* Human-readable name of a status code (static storage). */
 const char* domino_status_string(domino_status status);
 
@@ -251,7 +298,9 @@ typedef enum {
   DOMINO_K_QKV_WGRAD = 15,  /* Xᵀ·dQKV */
   DOMINO_K_ATTN_BWD_DQ = 16,    /* attention backward: the dQ kernel */
   DOMINO_K_ATTN_BWD_PREP = 17,  /* attention backward: Δ and the per-row statistics */
-  DOMINO_K_COUNT = 18
+  DOMINO_K_GROUP_FWD = 18,      /* dropout + residual + LayerNorm */
+  DOMINO_K_GROUP_BWD = 19,      /* its backward (with the fixed-order column sums) */
+  DOMINO_K_COUNT = 20
 } domino_kernel_kind;
 
 domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */

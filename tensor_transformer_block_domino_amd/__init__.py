@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH, AttnDesc, DominoError, MlpDesc, domino_attn_block_fwd, domino_attn_block_bwd, domino_block_bwd,
     domino_attn_block_fwd_workspace_size, domino_attn_block_bwd_workspace_size, domino_block_bwd_workspace_size,
     domino_block_fwd,
-    domino_block_fwd_workspace_size, domino_status_string, domino_timing_enable,
+    domino_block_fwd_workspace_size, domino_status_string, domino_timing_enable, GroupDesc, domino_resid_ln_fwd,
+    domino_resid_ln_bwd, domino_resid_ln_bwd_workspace_size,
     domino_timing_kernel, domino_timing_read, load, shard_reduce,
 )

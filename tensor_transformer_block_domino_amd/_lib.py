@@ -20,12 +20,14 @@ STATUS_NAMES = {0: "DOMINO_OK", 1: "DOMINO_ERR_INVALID_ARG", 2: "DOMINO_ERR_SHAP
                 4: "DOMINO_ERR_UNSUPPORTED", 5: "DOMINO_ERR_HIP"}
 KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgrad_a": 4, "wgrad_b": 5,
                 "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10, "attn_bwd_dkdv": 11, "outproj_dgrad": 12,
-                "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15, "attn_bwd_dq": 16, "attn_bwd_prep": 17}
+                "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15, "attn_bwd_dq": 16, "attn_bwd_prep": 17,
+                "group_fwd": 18, "group_bwd": 19}
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
             "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
             "domino_attn_block_bwd", "domino_attn_block_bwd_workspace_size",
+            "domino_resid_ln_fwd", "domino_resid_ln_bwd", "domino_resid_ln_bwd_workspace_size",
             "domino_status_string", "domino_last_error", "domino_timing_enable",
             "domino_timing_read", "domino_timing_kernel")
 
@@ -42,6 +44,11 @@ class AttnDesc(ctypes.Structure):
                 ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("row_chunks", ctypes.c_int32), ("n_partials", ctypes.c_int32),
                 ("no_join", ctypes.c_int32)]
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("hidden", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("p_drop", ctypes.c_float)]
 
 
 class DominoError(RuntimeError):
@@ -83,6 +90,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.domino_attn_block_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp,
                                           vp, vp, i32, vp, ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_bwd.restype = i32
+    lib.domino_resid_ln_fwd.argtypes = [ctypes.POINTER(GroupDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.domino_resid_ln_fwd.restype = i32
+    lib.domino_resid_ln_bwd.argtypes = [ctypes.POINTER(GroupDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i32, vp, ctypes.c_size_t, vp]
+    lib.domino_resid_ln_bwd.restype = i32
+    lib.domino_resid_ln_bwd_workspace_size.argtypes = [ctypes.POINTER(GroupDesc)]
+    lib.domino_resid_ln_bwd_workspace_size.restype = ctypes.c_size_t
     lib.domino_status_string.argtypes = [i32]
     lib.domino_status_string.restype = ctypes.c_char_p
     lib.domino_last_error.argtypes = []
@@ -181,6 +195,25 @@ def domino_attn_block_bwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, lse, dY, dO
 
 def domino_attn_block_bwd_workspace_size(desc: AttnDesc) -> int:
     return int(load().domino_attn_block_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def domino_resid_ln_fwd(desc: GroupDesc, resid, y, bias, keep, resid_out, gamma, beta, ln_out, mean, rstd,
+                        stream=None):
+    _check(load().domino_resid_ln_fwd(ctypes.byref(desc), _ptr(resid), _ptr(y), _ptr(bias), _ptr(keep),
+                                      _ptr(resid_out), _ptr(gamma), _ptr(beta), _ptr(ln_out), _ptr(mean), _ptr(rstd),
+                                      _stream(stream)))
+
+
+def domino_resid_ln_bwd(desc: GroupDesc, d_ln, d_res, resid_out, mean, rstd, gamma, keep, d_resid, d_y, d_gamma,
+                        d_beta, d_bias, accumulate: int, workspace, workspace_bytes: int, stream=None):
+    _check(load().domino_resid_ln_bwd(ctypes.byref(desc), _ptr(d_ln), _ptr(d_res), _ptr(resid_out), _ptr(mean),
+                                      _ptr(rstd), _ptr(gamma), _ptr(keep), _ptr(d_resid), _ptr(d_y), _ptr(d_gamma),
+                                      _ptr(d_beta), _ptr(d_bias), int(accumulate), _ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
+
+
+def domino_resid_ln_bwd_workspace_size(desc: GroupDesc) -> int:
+    return int(load().domino_resid_ln_bwd_workspace_size(ctypes.byref(desc)))
 
 
 def domino_status_string(status: int) -> str:

@@ -151,6 +151,21 @@ domino_status check_peers(const void* const* peers, int n_partials, const char* 
   return DOMINO_OK;
 }
 
+domino_status check_group_desc(const domino_group_desc* d) {
+  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
+  if (d->rows < 0 || d->hidden < 0) return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (d->hidden % 8) return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of 8");
+  if (d->hidden > 8192) return fail(DOMINO_ERR_UNSUPPORTED, "hidden above 8192");
+  if (!(d->p_drop >= 0.0f && d->p_drop < 1.0f)) return fail(DOMINO_ERR_INVALID_ARG, "p_drop must be in [0, 1)");
+  if (!(d->eps > 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "eps must be > 0");
+  return DOMINO_OK;
+}
+
+domino_status check_keep(const int32_t* keep) {
+  if (keep && (reinterpret_cast<uintptr_t>(keep) & 3u)) return fail(DOMINO_ERR_ALIGN, "keep is not 4-byte aligned");
+  return DOMINO_OK;
+}
+
 hipError_t hip_ok(hipError_t e, std::string* msg, const char* what) {
   if (e != hipSuccess) *msg = std::string(what) + ": " + hipGetErrorString(e);
   return e;
@@ -737,6 +752,61 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
                                 workspace_bytes, sc.cs), &msg, "dA_qkv GEMM")))
     return fail(DOMINO_ERR_HIP, msg);
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+domino_status domino_resid_ln_fwd(const domino_group_desc* d, const void* resid, const void* y, const void* bias,
+                                  const int32_t* keep, void* resid_out, const void* gamma, const void* beta,
+                                  void* ln_out, float* mean, float* rstd, hipStream_t stream) {
+  domino_status st = check_group_desc(d);
+  if (st != DOMINO_OK) return st;
+  const bool any = d->rows > 0 && d->hidden > 0;
+  if ((st = check_ptr(resid, "resid", any)) || (st = check_ptr(resid_out, "resid_out", any)) ||
+      (st = check_ptr(y, "y", any && y)) || (st = check_ptr(bias, "bias", any && bias)) || (st = check_keep(keep)) ||
+      (st = check_ptr(gamma, "gamma", any && gamma)) || (st = check_ptr(beta, "beta", any && beta)) ||
+      (st = check_ptr(ln_out, "ln_out", any && gamma)) || (st = check_ptr(mean, "mean", any && gamma)) ||
+      (st = check_ptr(rstd, "rstd", any && gamma)))
+    return st;
+  if (!any) return DOMINO_OK;
+  GroupFwdArgs a{resid, y, bias, keep, resid_out, gamma, beta, ln_out, mean, rstd, d->rows, d->hidden, d->eps,
+                 d->p_drop};
+  std::string msg;
+  if (hip_ok(timed(DOMINO_K_GROUP_FWD, stream, [&] { return launch_resid_ln_fwd(a, stream); }), &msg, "group"))
+    return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+size_t domino_resid_ln_bwd_workspace_size(const domino_group_desc* d) {
+  if (!d || d->rows <= 0 || d->hidden <= 0) return 0;
+  return size_t(3 * group_bwd_blocks(d->rows) * d->hidden) * sizeof(float);
+}
+
+domino_status domino_resid_ln_bwd(const domino_group_desc* d, const void* d_ln, const void* d_res,
+                                  const void* resid_out, const float* mean, const float* rstd, const void* gamma,
+                                  const int32_t* keep, void* d_resid, void* d_y, float* d_gamma, float* d_beta,
+                                  float* d_bias, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  domino_status st = check_group_desc(d);
+  if (st != DOMINO_OK) return st;
+  const bool any = d->rows > 0 && d->hidden > 0, ln = d_ln != nullptr;
+  if ((st = check_ptr(d_ln, "d_ln", any && ln)) || (st = check_ptr(d_res, "d_res", any && d_res)) ||
+      (st = check_ptr(resid_out, "resid_out", any && ln)) || (st = check_ptr(mean, "mean", any && ln)) ||
+      (st = check_ptr(rstd, "rstd", any && ln)) || (st = check_ptr(gamma, "gamma", any && ln)) ||
+      (st = check_keep(keep)) || (st = check_ptr(d_resid, "d_resid", any)) ||
+      (st = check_ptr(d_y, "d_y", any && d_y)) || (st = check_ptr(d_gamma, "d_gamma", d->hidden > 0 && d_gamma)) ||
+      (st = check_ptr(d_beta, "d_beta", d->hidden > 0 && d_beta)) ||
+      (st = check_ptr(d_bias, "d_bias", d->hidden > 0 && d_bias)))
+    return st;
+  if (!ln && (d_gamma || d_beta)) return fail(DOMINO_ERR_INVALID_ARG, "d_gamma/d_beta need d_ln");
+  if (!any) return DOMINO_OK;
+  if (!workspace || workspace_bytes < domino_resid_ln_bwd_workspace_size(d))
+    return fail(DOMINO_ERR_INVALID_ARG, "workspace smaller than domino_resid_ln_bwd_workspace_size");
+  if (!aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  GroupBwdArgs a{d_ln, d_res, resid_out, mean, rstd, gamma, keep, d_resid, d_y, d_gamma, d_beta, d_bias,
+                 accumulate ? 1 : 0, static_cast<float*>(workspace), d->rows, d->hidden, d->p_drop};
+  std::string msg;
+  if (hip_ok(timed(DOMINO_K_GROUP_BWD, stream, [&] { return launch_resid_ln_bwd(a, stream); }), &msg, "group backward"))
+    return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
 }
 

@@ -88,4 +88,26 @@ hipError_t launch_attention_bwd_prep(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_attention_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_attention_bwd_dq(const AttnBwdArgs& a, hipStream_t s);
 
+// The dropout + residual + LayerNorm group and its backward (bf16 rows × hidden,
+// contiguous). Null pointers select the variants the ABI documents.
+struct GroupFwdArgs {
+  const void* resid; const void* y; const void* bias; const int32_t* keep;
+  void* r_out; const void* gamma; const void* beta; void* ln; float* mean; float* rstd;
+  int64_t rows, hidden;
+  float eps, p_drop;
+};
+hipError_t launch_resid_ln_fwd(const GroupFwdArgs& a, hipStream_t s);
+
+struct GroupBwdArgs {
+  const void* d_ln; const void* d_res; const void* r_out; const float* mean; const float* rstd;
+  const void* gamma; const int32_t* keep;
+  void* d_resid; void* d_y; float* d_gamma; float* d_beta; float* d_bias;
+  int accumulate;
+  float* workspace;    // 3 · group_bwd_blocks(rows) · hidden floats
+  int64_t rows, hidden;
+  float p_drop;
+};
+int64_t group_bwd_blocks(int64_t rows);
+hipError_t launch_resid_ln_bwd(const GroupBwdArgs& a, hipStream_t s);
+
 }  // namespace domino

@@ -164,3 +164,43 @@ def test_workspace_size_is_zero_for_fp32_and_sized_for_bf16(lib):
     big = mlp_desc(batch=4, seq=2048, hidden=2560, ffn_shard=1280)
     n = D.domino_block_bwd_workspace_size(big)
     assert n % 4 == 0 and n >= 0
+
+
+def group_desc(**kw):
+    base = dict(rows=4, hidden=64, eps=1e-5, p_drop=0.1)
+    base.update(kw)
+    return L.GroupDesc(**base)
+
+
+def test_group_desc_layout():
+    assert ctypes.sizeof(L.GroupDesc) == 24 and L.GroupDesc.p_drop.offset == 20
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(hidden=60), "ALIGN: hidden must be a multiple of 8"),
+    (dict(hidden=8200), "UNSUPPORTED: hidden above 8192"),
+    (dict(p_drop=1.0), "INVALID_ARG: p_drop"),
+    (dict(p_drop=-0.1), "INVALID_ARG: p_drop"),
+    (dict(eps=0.0), "INVALID_ARG: eps"),
+    (dict(rows=-1), "SHAPE"),
+])
+def test_group_rejects_bad_desc(lib, kw, msg):
+    with pytest.raises(D.DominoError, match=msg):
+        D.domino_resid_ln_fwd(group_desc(**kw), FAKE, FAKE, None, None, FAKE, None, None, None, None, None)
+
+
+def test_group_rejects_bad_pointers(lib):
+    with pytest.raises(D.DominoError, match="INVALID_ARG: resid is NULL"):
+        D.domino_resid_ln_fwd(group_desc(), None, FAKE, None, None, FAKE, None, None, None, None, None)
+    with pytest.raises(D.DominoError, match="INVALID_ARG: ln_out is NULL"):
+        D.domino_resid_ln_fwd(group_desc(), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, FAKE)
+    with pytest.raises(D.DominoError, match="ALIGN: keep"):
+        D.domino_resid_ln_fwd(group_desc(), FAKE, FAKE, None, FAKE + 2, FAKE, None, None, None, None, None)
+    with pytest.raises(D.DominoError, match="d_gamma/d_beta need d_ln"):
+        D.domino_resid_ln_bwd(group_desc(), None, FAKE, None, None, None, None, None, FAKE, None, FAKE, None, None,
+                              0, FAKE, 1 << 20)
+    with pytest.raises(D.DominoError, match="workspace smaller"):
+        D.domino_resid_ln_bwd(group_desc(), None, FAKE, None, None, None, None, None, FAKE, None, None, None, None,
+                              0, FAKE, 4)
+    ws = D.domino_resid_ln_bwd_workspace_size(group_desc(rows=4096, hidden=4096))
+    assert ws == 3 * 512 * 4096 * 4
