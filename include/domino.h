@@ -266,6 +266,76 @@ domino_status domino_resid_ln_bwd(const domino_group_desc* desc, const void* d_l
                                   hipStream_t stream);
 size_t domino_resid_ln_bwd_workspace_size(const domino_group_desc* desc);
 
+/*
+ * A stack of Domino transformer layers on one tensor-parallel rank (deep-dive, "前向：多个计算
+ * 片段轮转重叠 AllReduce" and the DominoTransformerLayer excerpt under "μ-batch 流水"). Per
+ * layer, with x the residual stream entering it:
+ *   a = LN1(x);  y_attn = Σ_ranks Attn_s(a);  h = x + dropout(y_attn + b_o);  m = LN2(h);
+ *   y_mlp = Σ_ranks MLP_s(m);  x_next = h + dropout(y_mlp + b_2)
+ * (Attn_s: QKV product, causal attention over the rank's heads, out-projection; MLP_s: GEMM
+ * with the activation epilogue, GEMM; Σ_ranks: the own partial plus the P-1 peer partials,
+ * the AllReduce's sum). The rows are split into row_chunks μ-batches of whole sequences and
+ * issued on `compute` in the order
+ *   for each μ: the closing group of the previous layer fused with LN1 (it waits for that
+ *               layer's MLP reduction of μ), the attention of μ, then its reduction on `comm`;
+ *   for each μ: wait for the attention reduction of μ; dropout + residual + LN2 of μ; the MLP
+ *               of μ, then its reduction on `comm`;
+ * so the reduction of one μ-batch's attention hides behind the next μ-batch's attention and
+ * the small kernels, an MLP reduction behind the next μ-batch's MLP, and a layer's last MLP
+ * reduction behind the next layer's first attention. After the last layer the closing group
+ * writes `out` per μ. comm NULL (or == compute): everything in order on `compute`.
+ */
+typedef struct {
+  int64_t batch, seq, hidden;
+  int64_t heads, head_dim;    /* this rank's heads; head_dim 128 */
+  int64_t ffn_shard;          /* this rank's FFN columns (per half for SwiGLU) */
+  int32_t act;                /* domino_act */
+  float eps;                  /* LayerNorm epsilon (inside the root), > 0 */
+  float p_drop;               /* dropout probability of both residual branches, [0, 1) */
+  float scale;                /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t row_chunks;         /* μ-batches, >= 1, divides batch */
+  int32_t n_partials;         /* P: own partial + P-1 peer partials */
+  int32_t layers;             /* >= 1 */
+  int32_t reserved;           /* 0 */
+} domino_layer_desc;
+
+/* One layer's parameters on this rank (device pointers, bf16; T = batch·seq). */
+typedef struct {
+  const void* ln1_gamma; const void* ln1_beta;    /* [hidden]; beta may be NULL (0) */
+  const void* A_qkv_s;                            /* [hidden, 3·heads·head_dim] = [Q | K | V] */
+  const void* B_o_s;                              /* [heads·head_dim, hidden] */
+  const void* b_o;                                /* [hidden] or NULL */
+  const void* ln2_gamma; const void* ln2_beta;
+  const void* A_s;                                /* [hidden, n1] ([gate | up] for SwiGLU) */
+  const void* B_s;                                /* [ffn_shard, hidden] */
+  const void* b_2;                                /* [hidden] or NULL */
+  const int32_t* keep_attn;                       /* keep masks [T][ceil(hidden/32)] (bit j % 32 of */
+  const int32_t* keep_mlp;                        /* word j / 32) or NULL: no dropout there */
+} domino_layer_params;
+
+/* One layer's activations: written by the forward and kept for the backward. All
+ * [T, hidden] bf16 unless stated. */
+typedef struct {
+  void* x_in;                                     /* the residual stream entering the layer; for layer 0
+                                                     NULL means X itself (else a copy of X is written) */
+  void* ln1; float* mean1; float* rstd1;          /* LN1 output; its row mean and 1/σ [T] fp32 */
+  void* QKV;                                      /* [T, 3·heads·head_dim] */
+  void* O;                                        /* [T, heads·head_dim] */
+  float* lse;                                     /* [T, heads] fp32 or NULL */
+  void* y_attn_own;                               /* this rank's attention partial */
+  const void* const* peer_y_attn;                 /* HOST array of P-1 device pointers */
+  void* y_attn;                                   /* reduced attention output (may be y_attn_own if P = 1) */
+  void* h; void* ln2; float* mean2; float* rstd2; /* mid residual, LN2 output and its statistics */
+  void* Hpre; void* H;                            /* [T, n1], [T, ffn_shard] */
+  void* y_mlp_own; const void* const* peer_y_mlp; void* y_mlp;
+} domino_layer_acts;
+
+/* params and acts: arrays of desc->layers entries. out [T, hidden]: the last layer's output.
+ * workspace: optional device scratch (k-split slices). */
+domino_status domino_stack_fwd(const domino_layer_desc* desc, const void* X, const domino_layer_params* params,
+                               const domino_layer_acts* acts, void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t compute, hipStream_t comm);
+
 /* Human-readable name of a status code (static storage). */
 const char* domino_status_string(domino_status status);
 

@@ -27,7 +27,7 @@ KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgra
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
             "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
             "domino_attn_block_bwd", "domino_attn_block_bwd_workspace_size",
-            "domino_resid_ln_fwd", "domino_resid_ln_bwd", "domino_resid_ln_bwd_workspace_size",
+            "domino_resid_ln_fwd", "domino_resid_ln_bwd", "domino_resid_ln_bwd_workspace_size", "domino_stack_fwd",
             "domino_status_string", "domino_last_error", "domino_timing_enable",
             "domino_timing_read", "domino_timing_kernel")
 
@@ -49,6 +49,29 @@ class AttnDesc(ctypes.Structure):
 class GroupDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("hidden", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("p_drop", ctypes.c_float)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("ffn_shard", ctypes.c_int64),
+                ("act", ctypes.c_int32), ("eps", ctypes.c_float), ("p_drop", ctypes.c_float), ("scale", ctypes.c_float),
+                ("row_chunks", ctypes.c_int32), ("n_partials", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_VP = ctypes.c_void_p
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("ln1_gamma", "ln1_beta", "A_qkv_s", "B_o_s", "b_o", "ln2_gamma", "ln2_beta", "A_s",
+                                   "B_s", "b_2", "keep_attn", "keep_mlp")]
+
+
+class LayerActs(ctypes.Structure):
+    _fields_ = [("x_in", _VP), ("ln1", _VP), ("mean1", _VP), ("rstd1", _VP), ("QKV", _VP), ("O", _VP), ("lse", _VP),
+                ("y_attn_own", _VP), ("peer_y_attn", ctypes.POINTER(_VP)), ("y_attn", _VP), ("h", _VP), ("ln2", _VP),
+                ("mean2", _VP), ("rstd2", _VP), ("Hpre", _VP), ("H", _VP), ("y_mlp_own", _VP),
+                ("peer_y_mlp", ctypes.POINTER(_VP)), ("y_mlp", _VP)]
 
 
 class DominoError(RuntimeError):
@@ -97,6 +120,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.domino_resid_ln_bwd.restype = i32
     lib.domino_resid_ln_bwd_workspace_size.argtypes = [ctypes.POINTER(GroupDesc)]
     lib.domino_resid_ln_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.domino_stack_fwd.argtypes = [ctypes.POINTER(LayerDesc), vp, ctypes.POINTER(LayerParams),
+                                     ctypes.POINTER(LayerActs), vp, vp, ctypes.c_size_t, vp, vp]
+    lib.domino_stack_fwd.restype = i32
     lib.domino_status_string.argtypes = [i32]
     lib.domino_status_string.restype = ctypes.c_char_p
     lib.domino_last_error.argtypes = []
@@ -214,6 +240,31 @@ def domino_resid_ln_bwd(desc: GroupDesc, d_ln, d_res, resid_out, mean, rstd, gam
 
 def domino_resid_ln_bwd_workspace_size(desc: GroupDesc) -> int:
     return int(load().domino_resid_ln_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def _struct_of(cls, fields: dict, keep: list):
+    """A ctypes struct from a dict of tensors / ints / None (HOST pointer arrays for lists)."""
+    st = cls()
+    for name, ftype in cls._fields_:
+        v = fields.get(name)
+        if isinstance(v, (list, tuple)):
+            arr = _ptr_array(v)
+            keep.append(arr)
+            setattr(st, name, ctypes.cast(arr, ftype))
+        else:
+            setattr(st, name, _ptr(v))
+    return st
+
+
+def domino_stack_fwd(desc: LayerDesc, X, params: Sequence[dict], acts: Sequence[dict], out, workspace=None,
+                     workspace_bytes: int = 0, compute=None, comm=None):
+    """params / acts: one dict per layer with the fields of domino_layer_params / domino_layer_acts
+    (tensors, None, or for peer_y_attn / peer_y_mlp a list of tensors)."""
+    keep: list = []
+    pa = (LayerParams * len(params))(*[_struct_of(LayerParams, p, keep) for p in params])
+    aa = (LayerActs * len(acts))(*[_struct_of(LayerActs, a, keep) for a in acts])
+    _check(load().domino_stack_fwd(ctypes.byref(desc), _ptr(X), pa, aa, _ptr(out), _ptr(workspace), workspace_bytes,
+                                   _stream(compute), _stream(comm)))
 
 
 def domino_status_string(status: int) -> str:

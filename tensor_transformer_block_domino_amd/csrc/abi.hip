@@ -47,6 +47,7 @@ struct EventSet {
   bool ready = false;
   hipEvent_t done[kMaxChunks];  // compute: chunk's products finished
   hipEvent_t reduced;           // comm: last reduction finished
+  hipEvent_t sub[2][kMaxChunks];  // comm: a layer's attention (0) or MLP (1) reduction of a μ-batch finished
 };
 constexpr int kMaxDevices = 64;
 thread_local EventSet t_events[kMaxDevices];
@@ -68,6 +69,11 @@ hipError_t events_for_current_device(EventSet** out) {
     }
     e = hipEventCreateWithFlags(&es.reduced, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) return e;
+    for (int k = 0; k < 2; ++k)
+      for (int i = 0; i < kMaxChunks; ++i) {
+        e = hipEventCreateWithFlags(&es.sub[k][i], hipEventDisableTiming | hipEventDisableSystemFence);
+        if (e != hipSuccess) return e;
+      }
     es.ready = true;
   }
   *out = &es;
@@ -163,6 +169,54 @@ domino_status check_group_desc(const domino_group_desc* d) {
 
 domino_status check_keep(const int32_t* keep) {
   if (keep && (reinterpret_cast<uintptr_t>(keep) & 3u)) return fail(DOMINO_ERR_ALIGN, "keep is not 4-byte aligned");
+  return DOMINO_OK;
+}
+
+domino_status check_layer_desc(const domino_layer_desc* d) {
+  if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0 || d->seq < 0 || d->hidden < 0 || d->heads < 0 || d->ffn_shard < 0)
+    return fail(DOMINO_ERR_SHAPE, "negative size");
+  if (d->act != DOMINO_ACT_GELU_TANH && d->act != DOMINO_ACT_SWIGLU) return fail(DOMINO_ERR_INVALID_ARG, "bad act");
+  if (d->head_dim != 128) return fail(DOMINO_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->row_chunks < 1 || d->row_chunks > kMaxChunks) return fail(DOMINO_ERR_SHAPE, "bad row_chunks");
+  if (d->batch % d->row_chunks) return fail(DOMINO_ERR_SHAPE, "batch % row_chunks != 0");
+  if (d->n_partials < 1 || d->n_partials > DOMINO_MAX_PARTIALS) return fail(DOMINO_ERR_INVALID_ARG, "bad n_partials");
+  if (d->layers < 1) return fail(DOMINO_ERR_INVALID_ARG, "layers must be >= 1");
+  if (d->hidden % 8 || d->ffn_shard % 8) return fail(DOMINO_ERR_ALIGN, "hidden and ffn_shard must be multiples of 8");
+  if (d->hidden > 8192) return fail(DOMINO_ERR_UNSUPPORTED, "hidden above 8192");
+  if (!(d->p_drop >= 0.0f && d->p_drop < 1.0f)) return fail(DOMINO_ERR_INVALID_ARG, "p_drop must be in [0, 1)");
+  if (!(d->eps > 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "eps must be > 0");
+  if (d->reserved != 0) return fail(DOMINO_ERR_INVALID_ARG, "reserved must be 0");
+  return DOMINO_OK;
+}
+
+domino_status check_layer_ptrs(const domino_layer_desc* d, const domino_layer_params* prm, const domino_layer_acts* act,
+                               const void* X, const void* out) {
+  if (!prm || !act) return fail(DOMINO_ERR_INVALID_ARG, "params or acts is NULL");
+  domino_status st;
+  if ((st = check_ptr(X, "X", true)) || (st = check_ptr(out, "out", true))) return st;
+  for (int l = 0; l < d->layers; ++l) {
+    const domino_layer_params& p = prm[l];
+    const domino_layer_acts& a = act[l];
+    const std::string L = "layer " + std::to_string(l) + ": ";
+    auto need = [&](const void* q, const char* n, bool req) { return check_ptr(q, (L + n).c_str(), req); };
+    const bool P = d->n_partials > 1;
+    if ((st = need(p.ln1_gamma, "ln1_gamma", true)) || (st = need(p.ln1_beta, "ln1_beta", p.ln1_beta)) ||
+        (st = need(p.A_qkv_s, "A_qkv_s", true)) || (st = need(p.B_o_s, "B_o_s", true)) ||
+        (st = need(p.b_o, "b_o", p.b_o)) || (st = need(p.ln2_gamma, "ln2_gamma", true)) ||
+        (st = need(p.ln2_beta, "ln2_beta", p.ln2_beta)) || (st = need(p.A_s, "A_s", true)) ||
+        (st = need(p.B_s, "B_s", true)) || (st = need(p.b_2, "b_2", p.b_2)) || (st = check_keep(p.keep_attn)) ||
+        (st = check_keep(p.keep_mlp)) || (st = need(a.x_in, "x_in", l > 0)) || (st = need(a.ln1, "ln1", true)) ||
+        (st = need(a.mean1, "mean1", true)) || (st = need(a.rstd1, "rstd1", true)) || (st = need(a.QKV, "QKV", true)) ||
+        (st = need(a.O, "O", true)) || (st = need(a.lse, "lse", a.lse)) ||
+        (st = need(a.y_attn_own, "y_attn_own", true)) || (st = need(a.y_attn, "y_attn", true)) ||
+        (st = check_peers(a.peer_y_attn, d->n_partials, (L + "peer_y_attn").c_str(), P)) ||
+        (st = need(a.h, "h", true)) || (st = need(a.ln2, "ln2", true)) || (st = need(a.mean2, "mean2", true)) ||
+        (st = need(a.rstd2, "rstd2", true)) || (st = need(a.Hpre, "Hpre", true)) || (st = need(a.H, "H", true)) ||
+        (st = need(a.y_mlp_own, "y_mlp_own", true)) || (st = need(a.y_mlp, "y_mlp", true)) ||
+        (st = check_peers(a.peer_y_mlp, d->n_partials, (L + "peer_y_mlp").c_str(), P)))
+      return st;
+  }
   return DOMINO_OK;
 }
 
@@ -807,6 +861,101 @@ domino_status domino_resid_ln_bwd(const domino_group_desc* d, const void* d_ln, 
   std::string msg;
   if (hip_ok(timed(DOMINO_K_GROUP_BWD, stream, [&] { return launch_resid_ln_bwd(a, stream); }), &msg, "group backward"))
     return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
+domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const domino_layer_params* prm,
+                               const domino_layer_acts* act, void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t compute, hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_layer_desc(d);
+  if (st != DOMINO_OK) return st;
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim, f = d->ffn_shard;
+  const int64_t n1 = d->act == DOMINO_ACT_SWIGLU ? 2 * f : f;
+  if (T == 0 || h == 0) return DOMINO_OK;
+  if (d->heads == 0 || f == 0) return fail(DOMINO_ERR_UNSUPPORTED, "a layer needs heads > 0 and ffn_shard > 0");
+  if ((st = check_layer_ptrs(d, prm, act, X, out))) return st;
+  if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+  const int rc = d->row_chunks, P = d->n_partials;
+  const int64_t Tc = (d->batch / rc) * d->seq, kw = (h + 31) / 32;
+  const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
+  // One μ-batch as a problem of its own: batch / row_chunks whole sequences.
+  domino_attn_desc ad{d->batch / rc, d->seq, h, d->heads, d->head_dim, scale, DOMINO_BF16, 1, P, 1};
+  domino_mlp_desc md{d->batch / rc, d->seq, h, f, d->act, DOMINO_BF16, 1, 1, P, 1};
+  std::string msg;
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t r, const char* what) {
+    if (e == hipSuccess && r != hipSuccess) e = hip_ok(r, &msg, what);
+    return e == hipSuccess;
+  };
+  auto group = [&](const void* resid, const void* y, const void* bias, const int32_t* keep, void* r_out,
+                   const void* g, const void* b, void* ln, float* mean, float* rstd, int64_t r0) {
+    GroupFwdArgs ga{at(resid, r0 * h, 2), at(y, r0 * h, 2), bias, keep ? keep + r0 * kw : nullptr, at(r_out, r0 * h, 2),
+                    g, b, at(ln, r0 * h, 2), mean ? mean + r0 : nullptr, rstd ? rstd + r0 : nullptr, Tc, h, d->eps,
+                    d->p_drop};
+    return timed(DOMINO_K_GROUP_FWD, sc.cs, [&] { return launch_resid_ln_fwd(ga, sc.cs); });
+  };
+  // The μ-batch's reduction on the second stream, and an event the compute stream waits on
+  // (nothing when P = 1 and the reduced buffer is the own partial).
+  auto reduce = [&](void* y, const void* own, const void* const* peers, int kind, int mu) {
+    if (!needs_reduce(P, own, y)) return hipSuccess;
+    hipError_t r = sc.reduce(y, own, peers, P, h, mu * Tc * h, Tc, h, DOMINO_BF16);
+    if (r == hipSuccess && sc.overlap) r = hipEventRecord(sc.ev->sub[kind][mu], sc.rs);
+    return r;
+  };
+  auto wait = [&](const void* y, const void* own, int kind, int mu) {
+    return sc.overlap && needs_reduce(P, own, y) ? hipStreamWaitEvent(sc.cs, sc.ev->sub[kind][mu], 0) : hipSuccess;
+  };
+  for (int l = 0; l < d->layers && e == hipSuccess; ++l) {
+    const domino_layer_params& p = prm[l];
+    const domino_layer_acts& a = act[l];
+    const void* x = l == 0 && !a.x_in ? X : a.x_in;
+    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
+      const int64_t r0 = mu * Tc;
+      if (l == 0) {
+        ok(group(X, nullptr, nullptr, nullptr, a.x_in && a.x_in != X ? a.x_in : nullptr, p.ln1_gamma, p.ln1_beta,
+                 a.ln1, a.mean1, a.rstd1, r0), "LN1");
+      } else {
+        const domino_layer_params& q = prm[l - 1];
+        const domino_layer_acts& b = act[l - 1];
+        ok(wait(b.y_mlp, b.y_mlp_own, 1, mu), "wait for the MLP reduction") &&
+            ok(group(b.h, b.y_mlp, q.b_2, q.keep_mlp, a.x_in, p.ln1_gamma, p.ln1_beta, a.ln1, a.mean1, a.rstd1, r0),
+               "closing group + LN1");
+      }
+      AttnArgs aa{};
+      aa.qkv = at(a.QKV, r0 * 3 * hd, 2); aa.ld_qkv = 3 * hd;
+      aa.o = at(a.O, r0 * hd, 2); aa.ld_o = hd;
+      aa.lse = a.lse ? a.lse + r0 * d->heads : nullptr; aa.ld_lse = d->heads;
+      aa.batch = d->batch / rc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
+      aa.scale = scale;
+      ok(run_gemm(DOMINO_K_QKV, attn_qkv(&ad, at(a.ln1, r0 * h, 2), p.A_qkv_s, at(a.QKV, r0 * 3 * hd, 2)), workspace,
+                  workspace_bytes, sc.cs), "QKV GEMM") &&
+          ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), "attention") &&
+          ok(run_gemm(DOMINO_K_OUTPROJ, attn_out(&ad, at(a.O, r0 * hd, 2), p.B_o_s, at(a.y_attn_own, r0 * h, 2), 0),
+                      workspace, workspace_bytes, sc.cs), "out-projection") &&
+          ok(reduce(a.y_attn, a.y_attn_own, a.peer_y_attn, 0, mu), "reduce attention");
+    }
+    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
+      const int64_t r0 = mu * Tc;
+      ok(wait(a.y_attn, a.y_attn_own, 0, mu), "wait for the attention reduction") &&
+          ok(group(x, a.y_attn, p.b_o, p.keep_attn, a.h, p.ln2_gamma, p.ln2_beta, a.ln2, a.mean2, a.rstd2, r0),
+             "middle group") &&
+          ok(run_gemm(DOMINO_K_FWD_GEMM1, mlp_gemm1(&md, at(a.ln2, r0 * h, 2), p.A_s, at(a.Hpre, r0 * n1, 2),
+                                                    at(a.H, r0 * f, 2)), workspace, workspace_bytes, sc.cs), "GEMM1") &&
+          ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(&md, at(a.H, r0 * f, 2), p.B_s, at(a.y_mlp_own, r0 * h, 2), 0, 0),
+                      workspace, workspace_bytes, sc.cs), "GEMM2") &&
+          ok(reduce(a.y_mlp, a.y_mlp_own, a.peer_y_mlp, 1, mu), "reduce MLP");
+    }
+  }
+  const domino_layer_params& q = prm[d->layers - 1];
+  const domino_layer_acts& b = act[d->layers - 1];
+  for (int mu = 0; mu < rc && e == hipSuccess; ++mu)
+    ok(wait(b.y_mlp, b.y_mlp_own, 1, mu), "wait for the MLP reduction") &&
+        ok(group(b.h, b.y_mlp, q.b_2, q.keep_mlp, out, nullptr, nullptr, nullptr, nullptr, nullptr, mu * Tc),
+           "closing group");
+  if (e != hipSuccess) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
 }
 

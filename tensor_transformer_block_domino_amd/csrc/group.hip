@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void resid_ln_fwd_kernel(GroupFwdParams p) {
         for (int e = 0; e < 8; ++e) v[i][e] += (kb[i] >> e) & 1u ? (yv[e] + bv[e]) * sc : 0.f;
       }
       const u32x4_t o = pack8(v[i]);
-      st16(p.r_out + base + 8 * c, o);
+      if (p.r_out) st16(p.r_out + base + 8 * c, o);
       unpack8(o, v[i]);  // the LayerNorm sees the stored value
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[i][e];

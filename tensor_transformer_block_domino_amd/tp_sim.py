@@ -191,3 +191,113 @@ class AttnGroup:
         L.domino_attn_block_bwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
                                 self.lse[0], self.dY, self.dO[0], self.dQKV[0], self.dX_own[0], peers, self.dX,
                                 self.dA, self.dB, accumulate, self.ws, self.ws_bytes, compute, comm)
+
+
+_ACTS = {"gelu_tanh": L.DOMINO_ACT_GELU_TANH, "swiglu": L.DOMINO_ACT_SWIGLU}
+
+
+class LayerGroup:
+    """P ranks of a stack of Domino transformer layers on one device; rank 0 is measured.
+
+    `layers` is a list of per-layer dicts of full (unsharded) CPU tensors: ln1_g, ln1_b, Aqkv,
+    Bo, ln2_g, ln2_b, A, B, keep1, keep2 (and optionally bo, b2). peer_forward() runs the
+    stack once rank by rank with the plain library calls (each rank's attention and MLP
+    partials, their sums, the groups) so every layer's peer partials are those the other GPUs
+    would hold for the true layer inputs; forward() then runs rank 0's Domino schedule.
+    """
+
+    def __init__(self, *, batch, seq, hidden, heads_shard, head_dim, ffn_shard, act, row_chunks, n_partials, p_drop,
+                 X, layers, device="cuda", eps=1e-5):
+        self.batch, self.seq, self.hidden, self.hs, self.d = batch, seq, hidden, heads_shard, head_dim
+        self.f, self.act, self.rc, self.P, self.p, self.eps = ffn_shard, act, row_chunks, n_partials, p_drop, eps
+        self.T = T = batch * seq
+        self.L = len(layers)
+        P, h, hd = n_partials, hidden, heads_shard * head_dim
+        n1 = 2 * ffn_shard if act == "swiglu" else ffn_shard
+        bf = dict(device=device, dtype=torch.bfloat16)
+        f32 = dict(device=device, dtype=torch.float32)
+        self.X = X.to(**bf).contiguous()
+        self.out = torch.empty(T, h, **bf)
+        self.rank_prm = []   # [layer][rank] dict of device tensors
+        self.params = []     # rank 0's domino_layer_params per layer
+        self.acts = []       # rank 0's domino_layer_acts per layer
+        self.peer = []       # [layer] dict of peer partial lists
+        for l, lay in enumerate(layers):
+            ranks = []
+            for r in range(P):
+                Aq, Bo = attn_shard_weights(lay["Aqkv"], lay["Bo"], heads_shard * P, head_dim, P, r)
+                A_s, B_s = mlp_shard_weights(lay["A"], lay["B"], act, P, r)
+                ranks.append(dict(A_qkv_s=Aq.to(**bf), B_o_s=Bo.to(**bf), A_s=A_s.to(**bf), B_s=B_s.to(**bf)))
+            self.rank_prm.append(ranks)
+            dev_or_none = lambda k: None if lay.get(k) is None else lay[k].to(device).contiguous()  # noqa: E731
+            self.params.append(dict(ln1_gamma=dev_or_none("ln1_g"), ln1_beta=dev_or_none("ln1_b"),
+                                    A_qkv_s=ranks[0]["A_qkv_s"], B_o_s=ranks[0]["B_o_s"], b_o=dev_or_none("bo"),
+                                    ln2_gamma=dev_or_none("ln2_g"), ln2_beta=dev_or_none("ln2_b"),
+                                    A_s=ranks[0]["A_s"], B_s=ranks[0]["B_s"], b_2=dev_or_none("b2"),
+                                    keep_attn=dev_or_none("keep1"), keep_mlp=dev_or_none("keep2")))
+            peer = dict(y_attn=[torch.empty(T, h, **bf) for _ in range(P - 1)],
+                        y_mlp=[torch.empty(T, h, **bf) for _ in range(P - 1)])
+            self.peer.append(peer)
+            self.acts.append(dict(
+                x_in=None if l == 0 else torch.empty(T, h, **bf), ln1=torch.empty(T, h, **bf),
+                mean1=torch.empty(T, **f32), rstd1=torch.empty(T, **f32), QKV=torch.empty(T, 3 * hd, **bf),
+                O=torch.empty(T, hd, **bf), lse=torch.empty(T, heads_shard, **f32), y_attn_own=torch.empty(T, h, **bf),
+                peer_y_attn=peer["y_attn"] if P > 1 else None, y_attn=torch.empty(T, h, **bf),
+                h=torch.empty(T, h, **bf), ln2=torch.empty(T, h, **bf), mean2=torch.empty(T, **f32),
+                rstd2=torch.empty(T, **f32), Hpre=torch.empty(T, n1, **bf), H=torch.empty(T, ffn_shard, **bf),
+                y_mlp_own=torch.empty(T, h, **bf), peer_y_mlp=peer["y_mlp"] if P > 1 else None,
+                y_mlp=torch.empty(T, h, **bf)))
+        ws_attn = L.domino_attn_block_fwd_workspace_size(self._attn_desc())
+        ws_mlp = L.domino_block_fwd_workspace_size(self._mlp_desc())
+        self.ws_bytes = max(ws_attn, ws_mlp)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+
+    def desc(self, *, row_chunks=None, rank_alone=False) -> L.LayerDesc:
+        return L.LayerDesc(batch=self.batch, seq=self.seq, hidden=self.hidden, heads=self.hs, head_dim=self.d,
+                           ffn_shard=self.f, act=_ACTS[self.act], eps=self.eps, p_drop=self.p, scale=0.0,
+                           row_chunks=self.rc if row_chunks is None else row_chunks,
+                           n_partials=1 if rank_alone else self.P, layers=self.L, reserved=0)
+
+    def _attn_desc(self):
+        return L.AttnDesc(batch=self.batch, seq=self.seq, hidden=self.hidden, heads=self.hs, head_dim=self.d, scale=0.0,
+                          dtype=L.DOMINO_BF16, row_chunks=1, n_partials=1, no_join=0)
+
+    def _mlp_desc(self):
+        return L.MlpDesc(batch=self.batch, seq=self.seq, hidden=self.hidden, ffn_shard=self.f, act=_ACTS[self.act],
+                         dtype=L.DOMINO_BF16, row_chunks=1, col_chunks=1, n_partials=1, no_join=0)
+
+    def peer_forward(self, stream=None):
+        """Every rank's partials of every layer, from the true layer inputs, by plain calls."""
+        T, h, hd, P = self.T, self.hidden, self.hs * self.d, self.P
+        n1 = 2 * self.f if self.act == "swiglu" else self.f
+        bf = dict(device=self.X.device, dtype=torch.bfloat16)
+        f32 = dict(device=self.X.device, dtype=torch.float32)
+        gd = L.GroupDesc(rows=T, hidden=h, eps=self.eps, p_drop=self.p)
+        x, a, hh, m = self.X, torch.empty(T, h, **bf), torch.empty(T, h, **bf), torch.empty(T, h, **bf)
+        mean, rstd = torch.empty(T, **f32), torch.empty(T, **f32)
+        qkv, o = torch.empty(T, 3 * hd, **bf), torch.empty(T, hd, **bf)
+        hpre, hmid = torch.empty(T, n1, **bf), torch.empty(T, self.f, **bf)
+        own, y = torch.empty(T, h, **bf), torch.empty(T, h, **bf)
+        nxt = [torch.empty(T, h, **bf), torch.empty(T, h, **bf)]
+        ad, md = self._attn_desc(), self._mlp_desc()
+        for l in range(self.L):
+            prm, ranks, peer = self.params[l], self.rank_prm[l], self.peer[l]
+            L.domino_resid_ln_fwd(gd, x, None, None, None, x, prm["ln1_gamma"], prm["ln1_beta"], a, mean, rstd, stream)
+            for r in range(P):
+                dst = own if r == 0 else peer["y_attn"][r - 1]
+                L.domino_attn_block_fwd(ad, a, ranks[r]["A_qkv_s"], ranks[r]["B_o_s"], qkv, o, dst, None, None,
+                                        self.ws, self.ws_bytes, stream, None)
+            L.shard_reduce(y, h, [own] + peer["y_attn"], h, T, h, L.DOMINO_BF16, stream)
+            L.domino_resid_ln_fwd(gd, x, y, prm["b_o"], prm["keep_attn"], hh, prm["ln2_gamma"], prm["ln2_beta"], m,
+                                  mean, rstd, stream)
+            for r in range(P):
+                dst = own if r == 0 else peer["y_mlp"][r - 1]
+                L.domino_block_fwd(md, m, ranks[r]["A_s"], ranks[r]["B_s"], hpre, hmid, dst, None, None, self.ws,
+                                   self.ws_bytes, stream, None)
+            L.shard_reduce(y, h, [own] + peer["y_mlp"], h, T, h, L.DOMINO_BF16, stream)
+            x = nxt[l % 2]
+            L.domino_resid_ln_fwd(gd, hh, y, prm["b_2"], prm["keep_mlp"], x, None, None, None, None, None, stream)
+
+    def forward(self, compute=None, comm=None, **desc_kw):
+        L.domino_stack_fwd(self.desc(**desc_kw), self.X, self.params, self.acts, self.out, self.ws, self.ws_bytes,
+                           compute, comm)
