@@ -336,6 +336,56 @@ domino_status domino_stack_fwd(const domino_layer_desc* desc, const void* X, con
                                const domino_layer_acts* acts, void* out, void* workspace, size_t workspace_bytes,
                                hipStream_t compute, hipStream_t comm);
 
+/*
+ * One layer's gradients and backward scratch on this rank (device pointers). Parameter
+ * gradients are fp32 (NULL skips the bias ones); the rest is bf16 [T, hidden] unless stated.
+ */
+typedef struct {
+  float* d_ln1_gamma; float* d_ln1_beta;          /* [hidden] */
+  float* dA_qkv_s; float* dB_o_s; float* d_b_o;   /* as A_qkv_s, B_o_s; [hidden] or NULL */
+  float* d_ln2_gamma; float* d_ln2_beta;
+  float* dA_s; float* dB_s; float* d_b_2;
+  void* d_x_in;        /* gradient of the residual stream entering the layer (layer 0: NULL, dX is used) */
+  void* d_ym;          /* gradient of y_mlp: the MLP's dY */
+  void* dHpre;         /* [T, n1] */
+  void* dx_mlp_own; const void* const* peer_dx_mlp; void* dx_mlp;     /* MLP input-gradient partials, their sum */
+  void* d_h;           /* gradient of the middle residual h */
+  void* d_ya;          /* gradient of y_attn: the attention's dY */
+  void* dO;            /* [T, heads·head_dim] */
+  void* dQKV;          /* [T, 3·heads·head_dim] */
+  void* dx_attn_own; const void* const* peer_dx_attn; void* dx_attn;  /* attention input-gradient partials, sum */
+} domino_layer_grads;
+
+/*
+ * domino_stack_bwd — the backward of domino_stack_fwd, in reverse order of its steps
+ * (deep-dive, "反向：扩展与权重梯度计算的重叠"; overlap page §1: input gradients need the
+ * reduction, weight gradients are local). Given d_out, the gradient of `out`:
+ *   the last layer's closing group: d_ym = dropout'(d_out);
+ *   per layer, top down:
+ *     for each μ: MLP input gradient (dHpre = act'(Hpre) ⊙ d_ym·B_sᵀ, dx_mlp_own =
+ *                 dHpre·A_sᵀ), then its reduction on `comm`;
+ *     dB_s (+)= Hᵀ·d_ym, dA_s (+)= ln2ᵀ·dHpre                    (hide the last reduction);
+ *     for each μ: wait for the MLP reduction of μ; LN2's backward with the residual
+ *                 gradient (d_h) and dropout'(d_h) = d_ya; attention input gradient (dO,
+ *                 attention backward, dx_attn_own = dQKV·A_qkv_sᵀ), then its reduction;
+ *     dB_o_s (+)= Oᵀ·d_ya, dA_qkv_s (+)= ln1ᵀ·dQKV;
+ *     for each μ: wait for the attention reduction of μ; LN1's backward with the residual
+ *                 gradient gives d_x_in, fused with the layer below's closing group
+ *                 (d_ym of that layer = dropout'(d_x_in)) — issued at the start of the layer
+ *                 below, so a layer's last attention reduction hides behind the next
+ *                 layer's first MLP input gradient;
+ *   layer 0's LN1 backward writes dX.
+ * LayerNorm and bias gradients are sums over rows (fixed order). accumulate != 0 adds every
+ * parameter gradient to its contents. workspace: at least domino_stack_bwd_workspace_size
+ * bytes (required: it holds the attention statistics and the column partial sums).
+ * params and acts: those of the forward; grads: desc->layers entries.
+ */
+domino_status domino_stack_bwd(const domino_layer_desc* desc, const void* X, const domino_layer_params* params,
+                               const domino_layer_acts* acts, const domino_layer_grads* grads, const void* d_out,
+                               void* dX, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                               hipStream_t compute, hipStream_t comm);
+size_t domino_stack_bwd_workspace_size(const domino_layer_desc* desc);
+
 /* Human-readable name of a status code (static storage). */
 const char* domino_status_string(domino_status status);
 

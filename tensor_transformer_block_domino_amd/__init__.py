@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     domino_block_fwd,
     domino_block_fwd_workspace_size, domino_status_string, domino_timing_enable, GroupDesc, domino_resid_ln_fwd,
     domino_resid_ln_bwd, domino_resid_ln_bwd_workspace_size, LayerDesc, LayerParams, LayerActs, domino_stack_fwd,
+    LayerGrads, domino_stack_bwd, domino_stack_bwd_workspace_size,
     domino_timing_kernel, domino_timing_read, load, shard_reduce,
 )

@@ -28,6 +28,7 @@ EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size
             "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
             "domino_attn_block_bwd", "domino_attn_block_bwd_workspace_size",
             "domino_resid_ln_fwd", "domino_resid_ln_bwd", "domino_resid_ln_bwd_workspace_size", "domino_stack_fwd",
+            "domino_stack_bwd", "domino_stack_bwd_workspace_size",
             "domino_status_string", "domino_last_error", "domino_timing_enable",
             "domino_timing_read", "domino_timing_kernel")
 
@@ -72,6 +73,14 @@ class LayerActs(ctypes.Structure):
                 ("y_attn_own", _VP), ("peer_y_attn", ctypes.POINTER(_VP)), ("y_attn", _VP), ("h", _VP), ("ln2", _VP),
                 ("mean2", _VP), ("rstd2", _VP), ("Hpre", _VP), ("H", _VP), ("y_mlp_own", _VP),
                 ("peer_y_mlp", ctypes.POINTER(_VP)), ("y_mlp", _VP)]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("d_ln1_gamma", "d_ln1_beta", "dA_qkv_s", "dB_o_s", "d_b_o", "d_ln2_gamma",
+                                   "d_ln2_beta", "dA_s", "dB_s", "d_b_2", "d_x_in", "d_ym", "dHpre", "dx_mlp_own")] + \
+        [("peer_dx_mlp", ctypes.POINTER(_VP))] + [(n, _VP) for n in ("dx_mlp", "d_h", "d_ya", "dO", "dQKV",
+                                                                    "dx_attn_own")] + \
+        [("peer_dx_attn", ctypes.POINTER(_VP)), ("dx_attn", _VP)]
 
 
 class DominoError(RuntimeError):
@@ -123,6 +132,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.domino_stack_fwd.argtypes = [ctypes.POINTER(LayerDesc), vp, ctypes.POINTER(LayerParams),
                                      ctypes.POINTER(LayerActs), vp, vp, ctypes.c_size_t, vp, vp]
     lib.domino_stack_fwd.restype = i32
+    lib.domino_stack_bwd.argtypes = [ctypes.POINTER(LayerDesc), vp, ctypes.POINTER(LayerParams),
+                                     ctypes.POINTER(LayerActs), ctypes.POINTER(LayerGrads), vp, vp, i32, vp,
+                                     ctypes.c_size_t, vp, vp]
+    lib.domino_stack_bwd.restype = i32
+    lib.domino_stack_bwd_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
+    lib.domino_stack_bwd_workspace_size.restype = ctypes.c_size_t
     lib.domino_status_string.argtypes = [i32]
     lib.domino_status_string.restype = ctypes.c_char_p
     lib.domino_last_error.argtypes = []
@@ -265,6 +280,20 @@ def domino_stack_fwd(desc: LayerDesc, X, params: Sequence[dict], acts: Sequence[
     aa = (LayerActs * len(acts))(*[_struct_of(LayerActs, a, keep) for a in acts])
     _check(load().domino_stack_fwd(ctypes.byref(desc), _ptr(X), pa, aa, _ptr(out), _ptr(workspace), workspace_bytes,
                                    _stream(compute), _stream(comm)))
+
+
+def domino_stack_bwd(desc: LayerDesc, X, params: Sequence[dict], acts: Sequence[dict], grads: Sequence[dict], d_out,
+                     dX, accumulate: int, workspace, workspace_bytes: int, compute=None, comm=None):
+    keep: list = []
+    pa = (LayerParams * len(params))(*[_struct_of(LayerParams, p, keep) for p in params])
+    aa = (LayerActs * len(acts))(*[_struct_of(LayerActs, a, keep) for a in acts])
+    ga = (LayerGrads * len(grads))(*[_struct_of(LayerGrads, g, keep) for g in grads])
+    _check(load().domino_stack_bwd(ctypes.byref(desc), _ptr(X), pa, aa, ga, _ptr(d_out), _ptr(dX), int(accumulate),
+                                   _ptr(workspace), workspace_bytes, _stream(compute), _stream(comm)))
+
+
+def domino_stack_bwd_workspace_size(desc: LayerDesc) -> int:
+    return int(load().domino_stack_bwd_workspace_size(ctypes.byref(desc)))
 
 
 def domino_status_string(status: int) -> str:

@@ -959,6 +959,188 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
   return DOMINO_OK;
 }
 
+// The sub-problems of the layer schedule: one μ-batch (batch / row_chunks sequences) and
+// all rows (for the weight gradients).
+struct LayerShapes {
+  domino_attn_desc ad, ad_all;
+  domino_mlp_desc md, md_all;
+  float scale;
+};
+LayerShapes layer_shapes(const domino_layer_desc* d) {
+  LayerShapes s{};
+  s.scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf(float(d->head_dim));
+  const int64_t b = d->batch / d->row_chunks;
+  s.ad = domino_attn_desc{b, d->seq, d->hidden, d->heads, d->head_dim, s.scale, DOMINO_BF16, 1, d->n_partials, 1};
+  s.ad_all = s.ad;
+  s.ad_all.batch = d->batch;
+  s.md = domino_mlp_desc{b, d->seq, d->hidden, d->ffn_shard, d->act, DOMINO_BF16, 1, 1, d->n_partials, 1};
+  s.md_all = s.md;
+  s.md_all.batch = d->batch;
+  return s;
+}
+
+size_t domino_stack_bwd_workspace_size(const domino_layer_desc* d) {
+  if (check_layer_desc(d) != DOMINO_OK || d->heads == 0 || d->ffn_shard == 0) return 0;
+  const LayerShapes s = layer_shapes(d);
+  const int64_t Tc = s.md.batch * d->seq;
+  if (Tc == 0 || d->hidden == 0) return 0;
+  const size_t stats = size_t(attn_bwd_stats_floats(Tc, d->heads)) * sizeof(float);
+  const size_t part = size_t(3 * group_bwd_blocks(Tc) * d->hidden) * sizeof(float);
+  const size_t gemm = ws_bytes_of({mlp_dgrad_b(&s.md, nullptr, nullptr, nullptr, nullptr),
+                                   mlp_dgrad_a(&s.md, nullptr, nullptr, nullptr, 0, 0),
+                                   mlp_wgrad_b(&s.md_all, nullptr, nullptr, nullptr, 0),
+                                   mlp_wgrad_a(&s.md_all, nullptr, nullptr, nullptr, 0),
+                                   attn_dout(&s.ad, nullptr, nullptr, nullptr), attn_dx(&s.ad, nullptr, nullptr, nullptr, 0),
+                                   attn_wgrad_o(&s.ad_all, nullptr, nullptr, nullptr, 0),
+                                   attn_wgrad_qkv(&s.ad_all, nullptr, nullptr, nullptr, 0)});
+  return std::max(std::max(stats, part), gemm);
+}
+
+domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const domino_layer_params* prm,
+                               const domino_layer_acts* act, const domino_layer_grads* grd, const void* d_out, void* dX,
+                               int32_t accumulate, void* workspace, size_t workspace_bytes, hipStream_t compute,
+                               hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_layer_desc(d);
+  if (st != DOMINO_OK) return st;
+  const int64_t T = d->batch * d->seq, h = d->hidden, hd = d->heads * d->head_dim, f = d->ffn_shard;
+  const int64_t n1 = d->act == DOMINO_ACT_SWIGLU ? 2 * f : f;
+  if (T == 0 || h == 0) return DOMINO_OK;
+  if (d->heads == 0 || f == 0) return fail(DOMINO_ERR_UNSUPPORTED, "a layer needs heads > 0 and ffn_shard > 0");
+  if ((st = check_layer_ptrs(d, prm, act, X, d_out))) return st;
+  if (!grd) return fail(DOMINO_ERR_INVALID_ARG, "grads is NULL");
+  if ((st = check_ptr(dX, "dX", true))) return st;
+  const bool P = d->n_partials > 1;
+  for (int l = 0; l < d->layers; ++l) {
+    const domino_layer_grads& g = grd[l];
+    const std::string L = "layer " + std::to_string(l) + ": ";
+    auto need = [&](const void* q, const char* n, bool req) { return check_ptr(q, (L + n).c_str(), req); };
+    if ((st = need(g.d_ln1_gamma, "d_ln1_gamma", true)) || (st = need(g.d_ln1_beta, "d_ln1_beta", true)) ||
+        (st = need(g.dA_qkv_s, "dA_qkv_s", true)) || (st = need(g.dB_o_s, "dB_o_s", true)) ||
+        (st = need(g.d_b_o, "d_b_o", g.d_b_o)) || (st = need(g.d_ln2_gamma, "d_ln2_gamma", true)) ||
+        (st = need(g.d_ln2_beta, "d_ln2_beta", true)) || (st = need(g.dA_s, "dA_s", true)) ||
+        (st = need(g.dB_s, "dB_s", true)) || (st = need(g.d_b_2, "d_b_2", g.d_b_2)) ||
+        (st = need(g.d_x_in, "d_x_in", l > 0)) || (st = need(g.d_ym, "d_ym", true)) ||
+        (st = need(g.dHpre, "dHpre", true)) || (st = need(g.dx_mlp_own, "dx_mlp_own", true)) ||
+        (st = check_peers(g.peer_dx_mlp, d->n_partials, (L + "peer_dx_mlp").c_str(), P)) ||
+        (st = need(g.dx_mlp, "dx_mlp", true)) || (st = need(g.d_h, "d_h", true)) || (st = need(g.d_ya, "d_ya", true)) ||
+        (st = need(g.dO, "dO", true)) || (st = need(g.dQKV, "dQKV", true)) ||
+        (st = need(g.dx_attn_own, "dx_attn_own", true)) ||
+        (st = check_peers(g.peer_dx_attn, d->n_partials, (L + "peer_dx_attn").c_str(), P)) ||
+        (st = need(g.dx_attn, "dx_attn", true)) || (st = need(act[l].lse, "lse", true)))
+      return st;
+  }
+  if (!workspace || workspace_bytes < domino_stack_bwd_workspace_size(d))
+    return fail(DOMINO_ERR_INVALID_ARG, "workspace smaller than domino_stack_bwd_workspace_size");
+  if (!aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Sched sc;
+  if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
+  const int rc = d->row_chunks, Pn = d->n_partials, Lk = d->layers;
+  const int64_t Tc = (d->batch / rc) * d->seq, kw = (h + 31) / 32;
+  const LayerShapes s = layer_shapes(d);
+  std::string msg;
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t r, const char* what) {
+    if (e == hipSuccess && r != hipSuccess) e = hip_ok(r, &msg, what);
+    return e == hipSuccess;
+  };
+  // Group backward over the rows of μ-batch mu; parameter gradients accumulate over μ-batches.
+  auto group = [&](const void* d_ln, const void* d_res, const void* r_out, const float* mean, const float* rstd,
+                   const void* gamma, const int32_t* keep, void* d_resid, void* d_y, float* dg, float* db, float* dbias,
+                   int mu) {
+    const int64_t r0 = mu * Tc;
+    GroupBwdArgs ga{at(d_ln, r0 * h, 2), at(d_res, r0 * h, 2), at(r_out, r0 * h, 2), mean ? mean + r0 : nullptr,
+                    rstd ? rstd + r0 : nullptr, gamma, keep ? keep + r0 * kw : nullptr, at(d_resid, r0 * h, 2),
+                    at(d_y, r0 * h, 2), dg, db, dbias, (accumulate || mu > 0) ? 1 : 0, static_cast<float*>(workspace),
+                    Tc, h, d->p_drop};
+    return timed(DOMINO_K_GROUP_BWD, sc.cs, [&] { return launch_resid_ln_bwd(ga, sc.cs); });
+  };
+  auto reduce = [&](void* y, const void* own, const void* const* peers, int kind, int mu) {
+    if (!needs_reduce(Pn, own, y)) return hipSuccess;
+    hipError_t r = sc.reduce(y, own, peers, Pn, h, mu * Tc * h, Tc, h, DOMINO_BF16);
+    if (r == hipSuccess && sc.overlap) r = hipEventRecord(sc.ev->sub[kind][mu], sc.rs);
+    return r;
+  };
+  auto wait = [&](const void* y, const void* own, int kind, int mu) {
+    return sc.overlap && needs_reduce(Pn, own, y) ? hipStreamWaitEvent(sc.cs, sc.ev->sub[kind][mu], 0) : hipSuccess;
+  };
+  // The residual stream entering layer l and the gradient that flows out of it.
+  auto x_in = [&](int l) { return l == 0 && !act[0].x_in ? X : static_cast<const void*>(act[l].x_in); };
+  auto d_xin = [&](int l) { return l == 0 ? dX : grd[l].d_x_in; };
+  for (int l = Lk - 1; l >= 0 && e == hipSuccess; --l) {
+    const domino_layer_params& p = prm[l];
+    const domino_layer_acts& a = act[l];
+    const domino_layer_grads& g = grd[l];
+    // Gradient of the layer's output residual: d_out, or what the layer above wrote.
+    const void* d_r = l == Lk - 1 ? d_out : grd[l + 1].d_x_in;
+    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
+      const int64_t r0 = mu * Tc;
+      if (l == Lk - 1) {
+        ok(group(nullptr, d_out, nullptr, nullptr, nullptr, nullptr, p.keep_mlp, nullptr, g.d_ym, nullptr, nullptr,
+                 g.d_b_2, mu), "closing group backward");
+      } else {
+        // LN1 backward of the layer above, fused with this layer's closing dropout.
+        const domino_layer_params& q = prm[l + 1];
+        const domino_layer_acts& b = act[l + 1];
+        const domino_layer_grads& u = grd[l + 1];
+        ok(wait(u.dx_attn, u.dx_attn_own, 0, mu), "wait for the attention reduction") &&
+            ok(group(u.dx_attn, u.d_h, x_in(l + 1), b.mean1, b.rstd1, q.ln1_gamma, p.keep_mlp, u.d_x_in, g.d_ym,
+                     u.d_ln1_gamma, u.d_ln1_beta, g.d_b_2, mu), "LN1 backward + closing group backward");
+      }
+      ok(run_gemm(DOMINO_K_DGRAD_B, mlp_dgrad_b(&s.md, at(g.d_ym, r0 * h, 2), p.B_s, at(g.dHpre, r0 * n1, 2),
+                                                at(a.Hpre, r0 * n1, 2)), workspace, workspace_bytes, sc.cs),
+         "MLP dgrad-B") &&
+          ok(run_gemm(DOMINO_K_DGRAD_A, mlp_dgrad_a(&s.md, at(g.dHpre, r0 * n1, 2), p.A_s, at(g.dx_mlp_own, r0 * h, 2), 0,
+                                                    0), workspace, workspace_bytes, sc.cs), "MLP dgrad-A") &&
+          ok(reduce(g.dx_mlp, g.dx_mlp_own, g.peer_dx_mlp, 1, mu), "reduce MLP dX");
+    }
+    ok(run_gemm(DOMINO_K_WGRAD_B, mlp_wgrad_b(&s.md_all, a.H, g.d_ym, g.dB_s, accumulate), workspace, workspace_bytes,
+                sc.cs), "MLP dB") &&
+        ok(run_gemm(DOMINO_K_WGRAD_A, mlp_wgrad_a(&s.md_all, a.ln2, g.dHpre, g.dA_s, accumulate), workspace,
+                    workspace_bytes, sc.cs), "MLP dA");
+    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
+      const int64_t r0 = mu * Tc;
+      AttnBwdArgs ab{};
+      ab.qkv = at(a.QKV, r0 * 3 * hd, 2); ab.ld_qkv = 3 * hd;
+      ab.o = at(a.O, r0 * hd, 2); ab.dout = at(g.dO, r0 * hd, 2); ab.ld_o = hd;
+      ab.lse = a.lse + r0 * d->heads; ab.ld_lse = d->heads;
+      ab.dqkv = at(g.dQKV, r0 * 3 * hd, 2); ab.ld_dqkv = 3 * hd;
+      ab.stats = static_cast<float*>(workspace);
+      ab.batch = s.ad.batch; ab.seq = d->seq; ab.heads = d->heads; ab.head_dim = d->head_dim;
+      ab.scale = s.scale;
+      ok(wait(g.dx_mlp, g.dx_mlp_own, 1, mu), "wait for the MLP reduction") &&
+          ok(group(g.dx_mlp, d_r, a.h, a.mean2, a.rstd2, p.ln2_gamma, p.keep_attn, g.d_h, g.d_ya, g.d_ln2_gamma,
+                   g.d_ln2_beta, g.d_b_o, mu), "middle group backward") &&
+          ok(run_gemm(DOMINO_K_OUTPROJ_DGRAD, attn_dout(&s.ad, at(g.d_ya, r0 * h, 2), p.B_o_s, at(g.dO, r0 * hd, 2)),
+                      workspace, workspace_bytes, sc.cs), "dO GEMM") &&
+          ok(timed(DOMINO_K_ATTN_BWD_PREP, sc.cs, [&] { return launch_attention_bwd_prep(ab, sc.cs); }),
+             "attention backward statistics") &&
+          ok(timed(DOMINO_K_ATTN_BWD, sc.cs, [&] { return launch_attention_bwd_dkdv(ab, sc.cs); }),
+             "attention backward dK/dV") &&
+          ok(timed(DOMINO_K_ATTN_BWD_DQ, sc.cs, [&] { return launch_attention_bwd_dq(ab, sc.cs); }),
+             "attention backward dQ") &&
+          ok(run_gemm(DOMINO_K_QKV_DGRAD, attn_dx(&s.ad, at(g.dQKV, r0 * 3 * hd, 2), p.A_qkv_s,
+                                                  at(g.dx_attn_own, r0 * h, 2), 0), workspace, workspace_bytes, sc.cs),
+             "QKV dgrad") &&
+          ok(reduce(g.dx_attn, g.dx_attn_own, g.peer_dx_attn, 0, mu), "reduce attention dX");
+    }
+    ok(run_gemm(DOMINO_K_OUTPROJ_WGRAD, attn_wgrad_o(&s.ad_all, a.O, g.d_ya, g.dB_o_s, accumulate), workspace,
+                workspace_bytes, sc.cs), "dB_o GEMM") &&
+        ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(&s.ad_all, a.ln1, g.dQKV, g.dA_qkv_s, accumulate), workspace,
+                    workspace_bytes, sc.cs), "dA_qkv GEMM");
+  }
+  // Layer 0's LN1 backward with its residual gradient: dX.
+  const domino_layer_params& p0 = prm[0];
+  const domino_layer_acts& a0 = act[0];
+  const domino_layer_grads& g0 = grd[0];
+  for (int mu = 0; mu < rc && e == hipSuccess; ++mu)
+    ok(wait(g0.dx_attn, g0.dx_attn_own, 0, mu), "wait for the attention reduction") &&
+        ok(group(g0.dx_attn, g0.d_h, x_in(0), a0.mean1, a0.rstd1, p0.ln1_gamma, nullptr, d_xin(0), nullptr,
+                 g0.d_ln1_gamma, g0.d_ln1_beta, nullptr, mu), "LN1 backward");
+  if (e != hipSuccess) return fail(DOMINO_ERR_HIP, msg);
+  return DOMINO_OK;
+}
+
 domino_status domino_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   for (auto& r : g_timing_recs) {

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void resid_ln_bwd_kernel(GroupBwdParams p) {
           acc_b[i][e] += dl[i][e];
         }
       }
-      st16(p.d_resid + base + 8 * c, pack8(d[i]));
+      if (p.d_resid) st16(p.d_resid + base + 8 * c, pack8(d[i]));
       if (p.want_dy || p.want_bias) {
         const uint32_t kb = p.keep ? p.keep[row * p.keep_row_bytes + c] : 0xffu;
         const float sc = p.keep ? p.scale : 1.0f;

@@ -301,3 +301,123 @@ class LayerGroup:
     def forward(self, compute=None, comm=None, **desc_kw):
         L.domino_stack_fwd(self.desc(**desc_kw), self.X, self.params, self.acts, self.out, self.ws, self.ws_bytes,
                            compute, comm)
+
+    # ------------------------------------------------------------------------------------
+    # Backward
+    # ------------------------------------------------------------------------------------
+    def alloc_backward(self, d_out: torch.Tensor):
+        T, h, hd, P = self.T, self.hidden, self.hs * self.d, self.P
+        n1 = 2 * self.f if self.act == "swiglu" else self.f
+        dev = self.X.device
+        bf = dict(device=dev, dtype=torch.bfloat16)
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.d_out = d_out.to(**bf).contiguous()
+        self.dX = torch.empty(T, h, **bf)
+        self.grads, self.peer_grad = [], []
+        for l in range(self.L):
+            pg = dict(dx_mlp=[torch.empty(T, h, **bf) for _ in range(P - 1)],
+                      dx_attn=[torch.empty(T, h, **bf) for _ in range(P - 1)])
+            self.peer_grad.append(pg)
+            has_bo, has_b2 = self.params[l]["b_o"] is not None, self.params[l]["b_2"] is not None
+            self.grads.append(dict(
+                d_ln1_gamma=torch.zeros(h, **f32), d_ln1_beta=torch.zeros(h, **f32),
+                dA_qkv_s=torch.zeros(h, 3 * hd, **f32), dB_o_s=torch.zeros(hd, h, **f32),
+                d_b_o=torch.zeros(h, **f32) if has_bo else None,
+                d_ln2_gamma=torch.zeros(h, **f32), d_ln2_beta=torch.zeros(h, **f32),
+                dA_s=torch.zeros(h, n1, **f32), dB_s=torch.zeros(self.f, h, **f32),
+                d_b_2=torch.zeros(h, **f32) if has_b2 else None,
+                d_x_in=None if l == 0 else torch.empty(T, h, **bf), d_ym=torch.empty(T, h, **bf),
+                dHpre=torch.empty(T, n1, **bf), dx_mlp_own=torch.empty(T, h, **bf),
+                peer_dx_mlp=pg["dx_mlp"] if P > 1 else None, dx_mlp=torch.empty(T, h, **bf),
+                d_h=torch.empty(T, h, **bf), d_ya=torch.empty(T, h, **bf), dO=torch.empty(T, hd, **bf),
+                dQKV=torch.empty(T, 3 * hd, **bf), dx_attn_own=torch.empty(T, h, **bf),
+                peer_dx_attn=pg["dx_attn"] if P > 1 else None, dx_attn=torch.empty(T, h, **bf)))
+        self.bws_bytes = max(L.domino_stack_bwd_workspace_size(self.desc()),
+                             L.domino_stack_bwd_workspace_size(self.desc(row_chunks=1)),
+                             L.domino_attn_block_bwd_workspace_size(self._attn_desc()),
+                             L.domino_block_bwd_workspace_size(self._mlp_desc()),
+                             L.domino_resid_ln_bwd_workspace_size(L.GroupDesc(rows=T, hidden=h, eps=self.eps,
+                                                                              p_drop=self.p)))
+        self.bws = torch.empty(max(self.bws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def peer_backward(self, stream=None):
+        """Every rank's input-gradient partials of every layer, from the true layer gradients,
+        by plain calls: a reference forward keeps each layer's LayerNorm inputs and outputs,
+        then the backward runs top down, each rank recomputing its own forward activations."""
+        T, h, hd, P, f = self.T, self.hidden, self.hs * self.d, self.P, self.f
+        n1 = 2 * f if self.act == "swiglu" else f
+        bf = dict(device=self.X.device, dtype=torch.bfloat16)
+        f32 = dict(device=self.X.device, dtype=torch.float32)
+        gd = L.GroupDesc(rows=T, hidden=h, eps=self.eps, p_drop=self.p)
+        ad, md = self._attn_desc(), self._mlp_desc()
+        qkv, o, lse = torch.empty(T, 3 * hd, **bf), torch.empty(T, hd, **bf), torch.empty(T, self.hs, **f32)
+        hpre, hmid = torch.empty(T, n1, **bf), torch.empty(T, f, **bf)
+        own, y = torch.empty(T, h, **bf), torch.empty(T, h, **bf)
+        # Reference forward, keeping what the backward needs.
+        ref = []
+        x = self.X
+        for l in range(self.L):
+            prm, ranks = self.params[l], self.rank_prm[l]
+            r = dict(x=x, a=torch.empty(T, h, **bf), m1=torch.empty(T, **f32), s1=torch.empty(T, **f32),
+                     hh=torch.empty(T, h, **bf), m=torch.empty(T, h, **bf), m2=torch.empty(T, **f32),
+                     s2=torch.empty(T, **f32))
+            L.domino_resid_ln_fwd(gd, x, None, None, None, x, prm["ln1_gamma"], prm["ln1_beta"], r["a"], r["m1"],
+                                  r["s1"], stream)
+            parts = []
+            for k in range(P):
+                dst = own if k == 0 else torch.empty(T, h, **bf)
+                L.domino_attn_block_fwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, dst, None, None,
+                                        self.ws, self.ws_bytes, stream, None)
+                parts.append(dst)
+            L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
+            L.domino_resid_ln_fwd(gd, x, y, prm["b_o"], prm["keep_attn"], r["hh"], prm["ln2_gamma"], prm["ln2_beta"],
+                                  r["m"], r["m2"], r["s2"], stream)
+            parts = []
+            for k in range(P):
+                dst = own if k == 0 else torch.empty(T, h, **bf)
+                L.domino_block_fwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, dst, None, None, self.ws,
+                                   self.ws_bytes, stream, None)
+                parts.append(dst)
+            L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
+            x = torch.empty(T, h, **bf)
+            L.domino_resid_ln_fwd(gd, r["hh"], y, prm["b_2"], prm["keep_mlp"], x, None, None, None, None, None,
+                                  stream)
+            ref.append(r)
+        # Reference backward.
+        d_r = self.d_out
+        d_ym, d_h, d_ya, scratch, y_fwd = (torch.empty(T, h, **bf) for _ in range(5))
+        dHpre, dO, dQKV = torch.empty(T, n1, **bf), torch.empty(T, hd, **bf), torch.empty(T, 3 * hd, **bf)
+        dA_m, dB_m = torch.empty(h, n1, **f32), torch.empty(f, h, **f32)
+        dA_a, dB_a = torch.empty(h, 3 * hd, **f32), torch.empty(hd, h, **f32)
+        for l in range(self.L - 1, -1, -1):
+            prm, ranks, pg, r = self.params[l], self.rank_prm[l], self.peer_grad[l], ref[l]
+            L.domino_resid_ln_bwd(gd, None, d_r, None, None, None, None, prm["keep_mlp"], scratch, d_ym, None, None,
+                                  None, 0, self.bws, self.bws_bytes, stream)
+            parts = []
+            for k in range(P):
+                L.domino_block_fwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, y_fwd, None, None,
+                                   self.ws, self.ws_bytes, stream, None)
+                dst = own if k == 0 else pg["dx_mlp"][k - 1]
+                L.domino_block_bwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, d_ym, dHpre, dst, None,
+                                   None, dA_m, dB_m, 0, self.bws, self.bws_bytes, stream, None)
+                parts.append(dst)
+            L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
+            L.domino_resid_ln_bwd(gd, y, d_r, r["hh"], r["m2"], r["s2"], prm["ln2_gamma"], prm["keep_attn"], d_h, d_ya,
+                                  None, None, None, 0, self.bws, self.bws_bytes, stream)
+            parts = []
+            for k in range(P):
+                L.domino_attn_block_fwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, y_fwd, None, None,
+                                        self.ws, self.ws_bytes, stream, None, lse=lse)
+                dst = own if k == 0 else pg["dx_attn"][k - 1]
+                L.domino_attn_block_bwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, lse, d_ya, dO, dQKV,
+                                        dst, None, None, dA_a, dB_a, 0, self.bws, self.bws_bytes, stream, None)
+                parts.append(dst)
+            L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
+            d_x = torch.empty(T, h, **bf)
+            L.domino_resid_ln_bwd(gd, y, d_h, r["x"], r["m1"], r["s1"], prm["ln1_gamma"], None, d_x, None, None, None,
+                                  None, 0, self.bws, self.bws_bytes, stream)
+            d_r = d_x
+
+    def backward(self, compute=None, comm=None, accumulate=0, **desc_kw):
+        L.domino_stack_bwd(self.desc(**desc_kw), self.X, self.params, self.acts, self.grads, self.d_out, self.dX,
+                           accumulate, self.bws, self.bws_bytes, compute, comm)

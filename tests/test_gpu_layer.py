@@ -7,6 +7,7 @@ import pytest
 
 import synth
 from gpu_util import D, np, torch, dev, f64, check, poison, sync, oracle, BF16_TOL
+from gpu_util import check as _check
 from tensor_transformer_block_domino_amd.tp_sim import LayerGroup
 
 pytestmark = pytest.mark.gpu
@@ -121,3 +122,107 @@ def test_stack_forward_one_rank_no_dropout():
     g.forward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
     sync()
     check_stack(g, w, inp)
+
+
+def oracle_stack_backward(w, inp):
+    X = oracle.to_f64(inp["X"])
+    layers, keeps = [], []
+    for lay in inp["layers"]:
+        prm = {k: oracle.to_f64(lay[k]) for k in ("ln1_g", "ln1_b", "Aqkv", "Bo", "ln2_g", "ln2_b", "A", "B")}
+        prm["bo"] = oracle.to_f64(lay["bo"]) if "bo" in lay else None
+        prm["b2"] = oracle.to_f64(lay["b2"]) if "b2" in lay else None
+        layers.append(prm)
+        keeps.append((oracle.unpack_keep(lay["keep1"].numpy(), w.hidden),
+                      oracle.unpack_keep(lay["keep2"].numpy(), w.hidden)))
+    d_out = oracle.to_f64(inp["dY"])
+    dx, per = oracle.stack_backward(X, layers, keeps, w.p_drop, d_out, w.batch, w.seq, w.heads_full, w.head_dim, w.act)
+    return dx, per, layers, keeps
+
+
+def check_stack_backward(g, w, inp, with_bias=False):
+    dx, per, layers, keeps = oracle_stack_backward(w, inp)
+    errors = []
+
+    def check(name, got, ref, tol):  # every tensor's error is printed before the first failure is raised
+        try:
+            _check(name, got, ref, tol)
+        except AssertionError as e:
+            errors.append(str(e))
+
+    check("dX", f64(g.dX), dx, BF16_TOL)
+    _, inputs = oracle.stack_forward(oracle.to_f64(inp["X"]), layers, keeps, w.p_drop, w.batch, w.seq, w.heads_full,
+                                     w.head_dim, w.act)
+    for l in range(w.layers):
+        gr, sv = per[l]
+        G = g.grads[l]
+        for k_gpu, k_ref in (("d_ln1_gamma", "ln1_g"), ("d_ln1_beta", "ln1_b"), ("d_ln2_gamma", "ln2_g"),
+                             ("d_ln2_beta", "ln2_b")):
+            check(f"{k_gpu}[{l}]", f64(G[k_gpu]), gr[k_ref], BF16_TOL)
+        if with_bias:
+            check(f"d_b_o[{l}]", f64(G["d_b_o"]), gr["bo"], BF16_TOL)
+            check(f"d_b_2[{l}]", f64(G["d_b_2"]), gr["b2"], BF16_TOL)
+        check(f"d_ym[{l}]", f64(G["d_ym"]), gr["d_ym"], BF16_TOL)
+        check(f"d_ya[{l}]", f64(G["d_ya"]), gr["d_ya"], BF16_TOL)
+        A0, B0 = oracle.mlp_shard_weights(layers[l]["A"], layers[l]["B"], w.act, w.n_partials, 0)
+        _, _, dA, dB = oracle.mlp_shard_backward(sv["m"], A0, B0, gr["d_ym"], w.act)
+        check(f"dA_s[{l}]", f64(G["dA_s"]), dA, BF16_TOL)
+        check(f"dB_s[{l}]", f64(G["dB_s"]), dB, BF16_TOL)
+        Aq0, Bo0 = oracle.attn_shard_weights(layers[l]["Aqkv"], layers[l]["Bo"], w.heads_full, w.head_dim,
+                                             w.n_partials, 0)
+        _, _, _, dAq, dBo = oracle.attn_shard_backward(sv["a"], Aq0, Bo0, gr["d_ya"], w.batch, w.seq, w.heads_shard,
+                                                       w.head_dim)
+        check(f"dA_qkv_s[{l}]", f64(G["dA_qkv_s"]), dAq, BF16_TOL)
+        check(f"dB_o_s[{l}]", f64(G["dB_o_s"]), dBo, BF16_TOL)
+        if l > 0:
+            d_in = oracle.stack_backward(inputs[l], layers[l:], keeps[l:], w.p_drop, oracle.to_f64(inp["dY"]),
+                                         w.batch, w.seq, w.heads_full, w.head_dim, w.act)[0]
+            check(f"d_x_in[{l}]", f64(G["d_x_in"]), d_in, BF16_TOL)
+    assert not errors, errors
+
+
+def run_backward(w, with_bias=False, comm=True):
+    g, inp = make_group(w, with_bias=with_bias)
+    g.alloc_backward(inp["dY"])
+    g.peer_forward()
+    g.peer_backward()
+    g.forward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
+    poison(g.dX, *[G["d_h"] for G in g.grads])
+    g.backward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream() if comm else None)
+    sync()
+    return g, inp
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_stack_backward_matches_oracle(act):
+    w = small_workload(act)
+    print(f"layer stack bwd act={act} T={w.tokens} layers={w.layers} P={w.n_partials} mu-batches={w.row_chunks}",
+          flush=True)
+    g, inp = run_backward(w)
+    check_stack_backward(g, w, inp)
+
+
+def test_stack_backward_with_biases_three_layers_four_chunks():
+    w = small_workload("gelu_tanh", row_chunks=4, layers=3)
+    print("layer stack bwd with biases, layers=3, mu-batches=4", flush=True)
+    g, inp = run_backward(w, with_bias=True)
+    check_stack_backward(g, w, inp, with_bias=True)
+
+
+def test_stack_backward_schedule_and_accumulate():
+    """The second stream changes no bit; accumulate adds to every parameter gradient."""
+    w = small_workload("gelu_tanh")
+    print("layer stack bwd: two streams vs serial, accumulate", flush=True)
+    g, inp = run_backward(w)
+    first = {k: [G[k].clone() for G in g.grads] for k in ("d_ln1_gamma", "dA_s", "dB_o_s", "d_ln2_beta")}
+    dX = g.dX.clone()
+    g.backward(compute=torch.cuda.current_stream(), comm=None)
+    sync()
+    assert torch.equal(dX, g.dX)
+    for k, v in first.items():
+        for a, G in zip(v, g.grads):
+            assert torch.equal(a, G[k]), k
+    g.backward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream(), accumulate=1)
+    sync()
+    for k, v in first.items():
+        for a, G in zip(v, g.grads):
+            torch.testing.assert_close(G[k], 2 * a, rtol=1e-5, atol=1e-5)
