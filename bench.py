@@ -17,6 +17,10 @@ product, causal attention over the rank's heads, out-projection per chunk and it
 reduction; then the backward: dO, the attention backward, dX per chunk and its reduction,
 both weight gradients), with algorithmic FLOPs 3 × (the three products) + 3.5 × the causal
 attention's 4·d·S(S+1)/2 per (sequence, head).
+
+`--workload gpt3_6p7b_layer_tp8_row` measures a stack of whole layers (LayerNorm, attention,
+dropout + residual, LayerNorm, MLP, dropout + residual) in the μ-batch schedule, forward +
+backward, with the FLOPs of the attention block and of the MLP per layer.
 """
 from __future__ import annotations
 
@@ -258,6 +262,142 @@ def main_attn(args, w):
     print(json.dumps(out), flush=True)
 
 
+def layer_flops(w):
+    """Algorithmic FLOPs per step of each timed role of the layer stack (one rank, all layers)."""
+    T, h, f = w.tokens, w.hidden, w.ffn_shard
+    n1 = 2 * f if w.act == "swiglu" else f
+    fl = {k: v * w.layers for k, v in attn_flops(w).items()}
+    for k, v in {"fwd_gemm1": 2.0 * T * h * n1, "fwd_gemm2": 2.0 * T * f * h, "dgrad_b": 2.0 * T * h * f,
+                 "dgrad_a": 2.0 * T * n1 * h, "wgrad_b": 2.0 * T * f * h, "wgrad_a": 2.0 * T * h * n1}.items():
+        fl[k] = v * w.layers
+    return fl
+
+
+def cpu_baseline_layer(w, inp, n_seq=1):
+    """The oracle on this host: the whole (unsharded) stack's forward + backward over the
+    first n_seq sequences, counted at one rank's share of the FLOPs (÷ P)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = slice(0, n_seq * w.seq)
+    X = oracle.to_f64(inp["X"][rows])
+    dY = oracle.to_f64(inp["dY"][rows])
+    layers, keeps = [], []
+    for lay in inp["layers"]:
+        layers.append({k: oracle.to_f64(lay[k]) for k in ("ln1_g", "ln1_b", "Aqkv", "Bo", "ln2_g", "ln2_b", "A", "B")})
+        keeps.append((oracle.unpack_keep(lay["keep1"][rows].numpy(), w.hidden),
+                      oracle.unpack_keep(lay["keep2"][rows].numpy(), w.hidden)))
+    sub = synth.LayerWorkload(w.name, batch=n_seq, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard,
+                              head_dim=w.head_dim, ffn_shard=w.ffn_shard, act=w.act, row_chunks=1,
+                              n_partials=w.n_partials, layers=w.layers, p_drop=w.p_drop, seed=w.seed)
+    total = sum(layer_flops(sub).values())
+    t0 = time.perf_counter()
+    oracle.stack_backward(X, layers, keeps, w.p_drop, dY, n_seq, w.seq, w.heads_full, w.head_dim, w.act)
+    dt = time.perf_counter() - t0
+    # The oracle computes all P ranks' work (the unsharded layer): count its FLOPs as P shares.
+    return {"value": total * w.n_partials / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the unsharded {w.layers}-layer stack's forward+backward (oracle.stack_backward, which runs the "
+                      f"forward too) over {n_seq} of the {w.batch} sequences of {w.name} (fp64 numpy), one run, "
+                      f"{dt:.1f} s"}
+
+
+def main_layer(args, w):
+    import torch
+
+    import tensor_transformer_block_domino_amd as D
+    from tensor_transformer_block_domino_amd.tp_sim import LayerGroup
+
+    print("[bench] generating the layer inputs", file=sys.stderr, flush=True)
+    inp = synth.layer_inputs(w)
+    g = LayerGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
+                   ffn_shard=w.ffn_shard, act=w.act, row_chunks=w.row_chunks, n_partials=w.n_partials,
+                   p_drop=w.p_drop, X=inp["X"], layers=inp["layers"], device=torch.device("cuda:0"))
+    g.alloc_backward(inp["dY"])
+    print("[bench] peer partials (the other ranks' work, once)", file=sys.stderr, flush=True)
+    g.peer_forward()
+    g.peer_backward()
+    torch.cuda.synchronize()
+    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def step_domino():
+        g.forward(compute, comm)
+        g.backward(compute, comm)
+
+    def step_serial():
+        g.forward(compute, None)
+        g.backward(compute, None)
+
+    def step_unsplit():
+        g.forward(compute, comm, row_chunks=1)
+        g.backward(compute, comm, row_chunks=1)
+
+    ms = timed_steps(step_domino, args.steps, args.warmup)
+    print(f"[bench] layer stack domino step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms_serial = timed_steps(step_serial, args.steps, 2)
+    ms_unsplit = timed_steps(step_unsplit, args.steps, 2)
+    D.domino_timing_enable(True)
+    for _ in range(args.steps):
+        step_domino()
+    torch.cuda.synchronize()
+    fl = layer_flops(w)
+    roles = list(fl) + ["reduce", "aux", "group_fwd", "group_bwd"]
+    per = {r: D.domino_timing_read(r) for r in roles}
+    kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
+    D.domino_timing_enable(False)
+    total_flops = sum(fl.values())
+    value = total_flops / (ms * 1e-3) / 1e12
+    by_kernel = {}
+    for r in fl:
+        if fl[r] > 0 and per[r][0] > 0:
+            by_kernel.setdefault(kernel_of[r], []).append(r)
+    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
+    n_dom = sum(per[r][0] for r in by_kernel[dom])
+    tot_dom = sum(per[r][1] for r in by_kernel[dom])
+    flops_dom = sum(fl[r] for r in by_kernel[dom]) * args.steps
+    achieved = flops_dom / (tot_dom * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "heads_shard": w.heads_shard, "head_dim": w.head_dim, "ffn_shard": w.ffn_shard, "act": w.act,
+                   "layers": w.layers, "p_drop": w.p_drop, "tp_partials": w.n_partials,
+                   "split": f"rows x{w.row_chunks} (mu-batches)", "pass": "fwd+bwd"},
+        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "t_domino_ms": round(ms, 4),
+        "t_serial_ms": round(ms_serial, 4),
+        "t_unsplit_ms": round(ms_unsplit, 4),
+        "t_reduce_ms": round(per["reduce"][1] / args.steps, 4),
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
+        "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
+                          for r in fl if fl[r] > 0 and per[r][1] > 0},
+        "kernel_of_role": kernel_of,
+        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(tot_dom / max(1, n_dom) * 1e3, 2), "launches": n_dom,
+                     "flops_per_launch": flops_dom / max(1, n_dom)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_layer(w, inp)
+    print(json.dumps(out), flush=True)
+
+
 def timed_steps(fn, steps, warmup):
     import torch
 
@@ -293,6 +433,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if isinstance(w, synth.AttnWorkload):
         return main_attn(args, w)
+    if isinstance(w, synth.LayerWorkload):
+        return main_layer(args, w)
     assert isinstance(w, synth.MlpWorkload) and w.dtype == "bf16"
     dev = torch.device("cuda:0")
     inp = synth.mlp_inputs(w)

@@ -149,25 +149,48 @@ __global__ __launch_bounds__(256) void resid_ln_bwd_kernel(GroupBwdParams p) {
     if (p.want_ln && c < nch) unpack8(ld16(p.gamma + 8 * c), gam[i]);
   }
   const float inv_h = 1.0f / float(p.h);
-  int slot = 0;
-  for (int64_t row = r0; row < r1; ++row, slot ^= 1) {
+  // Raw 16-byte chunks of the current row; the next row's are loaded before this row's
+  // reduction, so each workgroup keeps a row of loads in flight.
+  u32x4_t cur_res[CPT], cur_ln[CPT], cur_r[CPT], nxt_res[CPT], nxt_ln[CPT], nxt_r[CPT];
+  float cur_mu = 0.f, cur_rs = 0.f, nxt_mu = 0.f, nxt_rs = 0.f;
+  auto load_row = [&](int64_t row, u32x4_t (&rs_)[CPT], u32x4_t (&ln_)[CPT], u32x4_t (&r_)[CPT], float& mu, float& rsd) {
     const int64_t base = row * p.h;
-    float dl[CPT][8], xh[CPT][8], d[CPT][8];
-    float sg = 0.f, sgx = 0.f;
-    const float mu = p.want_ln ? p.mean[row] : 0.f, rs = p.want_ln ? p.rstd[row] : 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       if (c >= nch) continue;
-      if (p.d_res) unpack8(ld16(p.d_res + base + 8 * c), d[i]);
+      if (p.d_res) rs_[i] = ld16(p.d_res + base + 8 * c);
+      if (p.want_ln) {
+        ln_[i] = ld16(p.d_ln + base + 8 * c);
+        r_[i] = ld16(p.r_out + base + 8 * c);
+      }
+    }
+    if (p.want_ln) {
+      mu = p.mean[row];
+      rsd = p.rstd[row];
+    }
+  };
+  if (r0 < r1) load_row(r0, cur_res, cur_ln, cur_r, cur_mu, cur_rs);
+  int slot = 0;
+  for (int64_t row = r0; row < r1; ++row, slot ^= 1) {
+    if (row + 1 < r1) load_row(row + 1, nxt_res, nxt_ln, nxt_r, nxt_mu, nxt_rs);
+    const int64_t base = row * p.h;
+    float dl[CPT][8], xh[CPT][8], d[CPT][8];
+    float sg = 0.f, sgx = 0.f;
+    const float mu = cur_mu, rs = cur_rs;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c >= nch) continue;
+      if (p.d_res) unpack8(cur_res[i], d[i]);
       else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[i][e] = 0.f;
       }
       if (p.want_ln) {
         float r[8];
-        unpack8(ld16(p.d_ln + base + 8 * c), dl[i]);
-        unpack8(ld16(p.r_out + base + 8 * c), r);
+        unpack8(cur_ln[i], dl[i]);
+        unpack8(cur_r[i], r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xh[i][e] = (r[e] - mu) * rs;
@@ -215,6 +238,14 @@ __global__ __launch_bounds__(256) void resid_ln_bwd_kernel(GroupBwdParams p) {
         if (p.want_dy) st16(p.d_y + base + 8 * c, pack8(dy));
       }
     }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      cur_res[i] = nxt_res[i];
+      cur_ln[i] = nxt_ln[i];
+      cur_r[i] = nxt_r[i];
+    }
+    cur_mu = nxt_mu;
+    cur_rs = nxt_rs;
   }
   const int64_t nb = gridDim.x;
 #pragma unroll
@@ -231,13 +262,43 @@ __global__ __launch_bounds__(256) void resid_ln_bwd_kernel(GroupBwdParams p) {
   }
 }
 
-// out[j] (+)= Σ_b part[b][j], b = 0, 1, … in order.
-__global__ __launch_bounds__(256) void colsum_kernel(const float* part, int nb, int h, float* out, int accumulate) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= h) return;
+// out_q[j] (+)= Σ_b part_q[b][j] for the quantities q = blockIdx.y whose output is non-null.
+// A workgroup owns 32 columns; its 8 thread slices each sum a contiguous eighth of the
+// partial rows (in order, 8 loads in flight), and the 8 slice sums are added in slice order,
+// so the result is the same on every run.
+struct ColsumParams {
+  const float* part;   // [3][nb][h]
+  float* out[3];
+  int nb, h, accumulate;
+};
+__global__ __launch_bounds__(256) void colsum_kernel(ColsumParams p) {
+  __shared__ float red[8][33];
+  float* out = p.out[blockIdx.y];
+  if (!out) return;
+  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int j = blockIdx.x * 32 + c;
+  const float* src = p.part + int64_t(blockIdx.y) * p.nb * p.h + j;
+  const int per = (p.nb + 7) / 8, b0 = sl * per, b1 = b0 + per < p.nb ? b0 + per : p.nb;
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += part[int64_t(b) * h + j];
-  out[j] = accumulate ? out[j] + s : s;
+  if (j < p.h) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[int64_t(b + u) * p.h];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += src[int64_t(b) * p.h];
+  }
+  red[sl][c] = s;
+  __syncthreads();
+  if (sl == 0 && j < p.h) {
+    float t = red[0][c];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) t += red[k][c];
+    out[j] = p.accumulate ? out[j] + t : t;
+  }
 }
 
 constexpr int kBwdBlocks = 512;
@@ -326,13 +387,16 @@ hipError_t launch_resid_ln_bwd(const GroupBwdArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const unsigned cb = unsigned((a.hidden + 255) / 256);
-  const int64_t H = a.hidden;
-  if (a.d_ln && a.d_gamma) hipLaunchKernelGGL(colsum_kernel, dim3(cb), dim3(256), 0, s, a.workspace, blocks, int(H), a.d_gamma, a.accumulate);
-  if (a.d_ln && a.d_beta)
-    hipLaunchKernelGGL(colsum_kernel, dim3(cb), dim3(256), 0, s, a.workspace + int64_t(blocks) * H, blocks, int(H), a.d_beta, a.accumulate);
-  if (a.d_bias)
-    hipLaunchKernelGGL(colsum_kernel, dim3(cb), dim3(256), 0, s, a.workspace + 2 * int64_t(blocks) * H, blocks, int(H), a.d_bias, a.accumulate);
+  ColsumParams cp{};
+  cp.part = a.workspace;
+  cp.out[0] = a.d_ln ? a.d_gamma : nullptr;
+  cp.out[1] = a.d_ln ? a.d_beta : nullptr;
+  cp.out[2] = a.d_bias;
+  cp.nb = blocks;
+  cp.h = int(a.hidden);
+  cp.accumulate = a.accumulate;
+  if (cp.out[0] || cp.out[1] || cp.out[2])
+    hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((a.hidden + 31) / 32), 3), dim3(256), 0, s, cp);
   return hipGetLastError();
 }
 
