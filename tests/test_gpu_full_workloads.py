@@ -111,3 +111,39 @@ def test_full_attention_backward_workload():
         r = slice(b * w.seq, (b + 1) * w.seq)
         ref = oracle.attn_backward_unsharded(X[r], Aqkv, Bo, dY[r], 1, w.seq, w.heads_full, w.head_dim)
         check(f"dX seq {b}", dX[r], ref, BF16_TOL)
+
+
+def test_full_layer_stack_workload():
+    """The two-layer GPT-3 6.7B-shaped stack (8 ranks, two μ-batches, dropout 0.1) forward and
+    backward in the bench's schedule; the output and dX of the first sequence of the second
+    μ-batch against the oracle's unsharded stack run over that sequence alone (a sequence's
+    rows depend on that sequence only)."""
+    from tensor_transformer_block_domino_amd.tp_sim import LayerGroup
+
+    w = synth.WORKLOADS["gpt3_6p7b_layer_tp8_row"]
+    print("full layer stack: generating inputs", flush=True)
+    inp = synth.layer_inputs(w)
+    g = LayerGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
+                   ffn_shard=w.ffn_shard, act=w.act, row_chunks=w.row_chunks, n_partials=w.n_partials,
+                   p_drop=w.p_drop, X=inp["X"], layers=inp["layers"], device=dev())
+    g.alloc_backward(inp["dY"])
+    print("  peer partials, then rank 0's forward and backward on the GPU", flush=True)
+    g.peer_forward()
+    g.peer_backward()
+    g.forward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
+    g.backward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
+    sync()
+    b = w.batch // w.row_chunks
+    rows = slice(b * w.seq, (b + 1) * w.seq)
+    print(f"  oracle: the unsharded stack over sequence {b}", flush=True)
+    X = oracle.to_f64(inp["X"][rows])
+    dY = oracle.to_f64(inp["dY"][rows])
+    layers, keeps = [], []
+    for lay in inp["layers"]:
+        layers.append({k: oracle.to_f64(lay[k]) for k in ("ln1_g", "ln1_b", "Aqkv", "Bo", "ln2_g", "ln2_b", "A", "B")})
+        keeps.append((oracle.unpack_keep(lay["keep1"][rows].numpy(), w.hidden),
+                      oracle.unpack_keep(lay["keep2"][rows].numpy(), w.hidden)))
+    out, _ = oracle.stack_forward(X, layers, keeps, w.p_drop, 1, w.seq, w.heads_full, w.head_dim, w.act)
+    check(f"out (sequence {b})", f64(g.out[rows]), out, BF16_TOL)
+    dx, _ = oracle.stack_backward(X, layers, keeps, w.p_drop, dY, 1, w.seq, w.heads_full, w.head_dim, w.act)
+    check(f"dX (sequence {b})", f64(g.dX[rows]), dx, BF16_TOL)
