@@ -153,3 +153,27 @@ def test_edge_n_partials_one_in_place():
     sync()
     X, A, B = (oracle.to_f64(inp[k]) for k in ("X", "A", "B"))
     check("Y_own", f64(g.Y_own[0]), oracle.mlp_forward_unsharded(X, A, B, "gelu_tanh"), BF16_TOL)
+
+
+MANY_SPLITS = [(4, 1), (1, 4), (3, 1), (2, 4), (4, 4)]
+
+
+@pytest.mark.parametrize("split", MANY_SPLITS)
+def test_mlp_more_than_two_chunks_per_axis(split):
+    """Row, column and 2D splits with 3 or 4 chunks per axis (12 sequences, hidden 320)."""
+    act = "gelu_tanh" if split[0] != 3 else "swiglu"
+    w = small_workload(act, batch=12, seq=40, hidden=320, split=split, seed=23)
+    print(f"mlp many chunks act={act} split={split} T={w.tokens} h={w.hidden}", flush=True)
+    g, inp = run_fwd_bwd(w)
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    P = w.n_partials
+    check("Y", f64(g.Y), oracle.domino_mlp_forward(X, A, B, act, P, w.batch, w.seq, *split), BF16_TOL)
+    dX_ref, dA_ref, dB_ref = oracle.domino_mlp_backward(X, A, B, dY, act, P, 0, w.batch, w.seq, *split)
+    check("dX", f64(g.dX), dX_ref, BF16_TOL)
+    check("dA_s", f64(g.dA), dA_ref, BF16_TOL)
+    check("dB_s", f64(g.dB), dB_ref, BF16_TOL)
+    # Chunks change no dot product: every output equals the unsplit call's, bit for bit.
+    w1 = small_workload(act, batch=12, seq=40, hidden=320, split=(1, 1), seed=23)
+    g1, _ = run_fwd_bwd(w1, inputs=inp)
+    for name in ("Y", "dX", "dA", "dB"):
+        assert torch.equal(getattr(g, name), getattr(g1, name)), name

@@ -155,7 +155,7 @@ def test_act_grads_match_torch_autograd():
 # ------------------------------------------------------------------------------------------
 # Split identities and the shard-sum identity.
 # ------------------------------------------------------------------------------------------
-SPLITS = [(1, 1), (2, 1), (1, 2), (2, 2), (3, 1), (1, 3)]
+SPLITS = [(1, 1), (2, 1), (1, 2), (2, 2), (3, 1), (1, 3), (4, 2), (2, 4)]
 
 
 @pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
