@@ -20,8 +20,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attn_backward_unsharded, attn_forward_unsharded
-from .mlp import mlp_backward_unsharded, mlp_forward_unsharded
+import math
+
+from .attention import _mha, _mha_backward
+from .mlp import act_backward, act_forward
 
 LN_EPS = 1e-5
 
@@ -93,17 +95,48 @@ def resid_group_backward(d_ln, d_res, r_out, keep, p, gamma, eps: float = LN_EPS
 # ----------------------------------------------------------------------------------------
 # The whole pre-LayerNorm layer with full weights (what the Domino schedule over the
 # tensor-parallel shards must equal), and a stack of such layers.
-# Parameters per layer: ln1_g, ln1_b, Aqkv, Bo, bo, ln2_g, ln2_b, A, B, b2 (bo, b2 may be
-# None: no bias); keep masks keep1 (after the attention) and keep2 (after the MLP).
+# Parameters per layer: ln1_g, ln1_b, Aqkv, bqkv, Bo, bo, ln2_g, ln2_b, A, b1, B, b2 (the
+# biases may be absent or None: no bias); keep masks keep1 (after the attention) and keep2
+# (after the MLP). The column-parallel biases (bqkv, b1) are added to the product before
+# the attention / activation; the row-parallel ones (bo, b2) after the sum over ranks.
 # ----------------------------------------------------------------------------------------
+def _bias(b):
+    return 0.0 if b is None else b[None, :]
+
+
+def attention_sublayer(a, Aqkv, bqkv, Bo, batch, seq, heads, head_dim):
+    """Attn(a) = MHA(a·Aqkv + bqkv)·Bo with all heads; returns (y, QKV)."""
+    QKV = a @ Aqkv + _bias(bqkv)
+    return _mha(QKV, batch, seq, heads, head_dim, 1.0 / math.sqrt(head_dim)) @ Bo, QKV
+
+
+def attention_sublayer_backward(a, Aqkv, bqkv, Bo, dy, batch, seq, heads, head_dim):
+    """(da, dbqkv) of attention_sublayer given dy."""
+    _, QKV = attention_sublayer(a, Aqkv, bqkv, Bo, batch, seq, heads, head_dim)
+    dQKV = _mha_backward(QKV, dy @ Bo.T, batch, seq, heads, head_dim, 1.0 / math.sqrt(head_dim))
+    return dQKV @ Aqkv.T, dQKV.sum(axis=0)
+
+
+def mlp_sublayer(m, A, b1, B, act):
+    """MLP(m) = act(m·A + b1)·B."""
+    return act_forward(m @ A + _bias(b1), act) @ B
+
+
+def mlp_sublayer_backward(m, A, b1, B, dy, act):
+    """(dm, db1) of mlp_sublayer given dy."""
+    Hpre = m @ A + _bias(b1)
+    dHpre = act_backward(Hpre, dy @ B.T, act)
+    return dHpre @ A.T, dHpre.sum(axis=0)
+
+
 def layer_forward(x, prm, keep1, keep2, p, batch, seq, heads_full, head_dim, act, eps: float = LN_EPS):
     """Returns (out, saved): out = h + dropout(MLP(LN2(h)) + b2) with
     h = x + dropout(Attn(LN1(x)) + bo); saved holds a = LN1(x), h, m = LN2(h), the
     sublayer outputs ya, ym and the LayerNorm statistics."""
     a, mu1, rs1 = layer_norm(x, prm["ln1_g"], prm["ln1_b"], eps)
-    ya = attn_forward_unsharded(a, prm["Aqkv"], prm["Bo"], batch, seq, heads_full, head_dim)
+    ya = attention_sublayer(a, prm["Aqkv"], prm.get("bqkv"), prm["Bo"], batch, seq, heads_full, head_dim)[0]
     h, m, mu2, rs2 = resid_group_forward(x, ya, prm.get("bo"), keep1, p, prm["ln2_g"], prm["ln2_b"], eps)
-    ym = mlp_forward_unsharded(m, prm["A"], prm["B"], act)
+    ym = mlp_sublayer(m, prm["A"], prm.get("b1"), prm["B"], act)
     out = resid_group_forward(h, ym, prm.get("b2"), keep2, p, None, None)[0]
     return out, dict(a=a, ya=ya, h=h, m=m, ym=ym, mean1=mu1, rstd1=rs1, mean2=mu2, rstd2=rs2)
 
@@ -116,11 +149,13 @@ def layer_backward(x, prm, keep1, keep2, p, d_out, batch, seq, heads_full, head_
     the attention, from which each rank's weight gradients follow)."""
     _, s = layer_forward(x, prm, keep1, keep2, p, batch, seq, heads_full, head_dim, act, eps)
     d_h, d_ym, _, _, db2 = resid_group_backward(None, d_out, s["h"], keep2, p, None, eps)
-    dm = mlp_backward_unsharded(s["m"], prm["A"], prm["B"], d_ym, act)
+    dm, db1 = mlp_sublayer_backward(s["m"], prm["A"], prm.get("b1"), prm["B"], d_ym, act)
     d_h, d_ya, dg2, dbt2, dbo = resid_group_backward(dm, d_h, s["h"], keep1, p, prm["ln2_g"], eps)
-    da = attn_backward_unsharded(s["a"], prm["Aqkv"], prm["Bo"], d_ya, batch, seq, heads_full, head_dim)
+    da, dbqkv = attention_sublayer_backward(s["a"], prm["Aqkv"], prm.get("bqkv"), prm["Bo"], d_ya, batch, seq,
+                                            heads_full, head_dim)
     dx, _, dg1, dbt1, _ = resid_group_backward(da, d_h, x, None, p, prm["ln1_g"], eps)
-    grads = dict(ln1_g=dg1, ln1_b=dbt1, ln2_g=dg2, ln2_b=dbt2, bo=dbo, b2=db2, d_ym=d_ym, d_ya=d_ya, dm=dm, da=da)
+    grads = dict(ln1_g=dg1, ln1_b=dbt1, ln2_g=dg2, ln2_b=dbt2, bo=dbo, b2=db2, bqkv=dbqkv, b1=db1, d_ym=d_ym,
+                 d_ya=d_ya, dm=dm, da=da)
     return dx, grads, s
 
 

@@ -143,7 +143,7 @@ def _params(h, heads, d, f, act):
 def _torch_layer(x, prm, k1, k2, p, batch, seq, heads, d, act):
     h = x.shape[1]
     a = F.layer_norm(x, (h,), prm["ln1_g"], prm["ln1_b"], eps=1e-5)
-    qkv = a @ prm["Aqkv"]
+    qkv = a @ prm["Aqkv"] + (prm["bqkv"] if "bqkv" in prm else 0.0)
     hd = heads * d
 
     def split(t):
@@ -152,15 +152,16 @@ def _torch_layer(x, prm, k1, k2, p, batch, seq, heads, d, act):
     q, k, v = split(qkv[:, :hd]), split(qkv[:, hd:2 * hd]), split(qkv[:, 2 * hd:])
     o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
     ya = o.permute(0, 2, 1, 3).reshape(batch * seq, hd) @ prm["Bo"]
+    ya = ya + (prm["bo"] if "bo" in prm else 0.0)
     hh = x + torch.where(t64(k1).bool(), ya / (1 - p), torch.zeros_like(ya))
     m = F.layer_norm(hh, (h,), prm["ln2_g"], prm["ln2_b"], eps=1e-5)
-    hp = m @ prm["A"]
+    hp = m @ prm["A"] + (prm["b1"] if "b1" in prm else 0.0)
     if act == "swiglu":
         f = hp.shape[1] // 2
         hmid = F.silu(hp[:, :f]) * hp[:, f:]
     else:
         hmid = F.gelu(hp, approximate="tanh")
-    ym = hmid @ prm["B"]
+    ym = hmid @ prm["B"] + (prm["b2"] if "b2" in prm else 0.0)
     return hh + torch.where(t64(k2).bool(), ym / (1 - p), torch.zeros_like(ym))
 
 
@@ -180,6 +181,26 @@ def test_layer_matches_torch_autograd(act):
     dx, grads, _ = oracle.layer_backward(x, prm, k1, k2, p, dy, batch, seq, heads, d, act)
     assert rel(dx, xt.grad.numpy()) < 1e-11
     for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
+        assert rel(grads[k], tp[k].grad.numpy()) < 1e-11, k
+
+
+def test_layer_with_biases_matches_torch_autograd():
+    batch, seq, heads, d, h, f, p, act = 2, 4, 2, 4, 16, 10, 0.2, "swiglu"
+    T = batch * seq
+    x, dy = rnd(T, h), rnd(T, h)
+    prm = _params(h, heads, d, f, act)
+    prm.update(bqkv=rnd(3 * heads * d, scale=0.3), bo=rnd(h, scale=0.3), b1=rnd(2 * f, scale=0.3),
+               b2=rnd(h, scale=0.3))
+    k1, k2 = rand_keep(T, h, p), rand_keep(T, h, p)
+    out, _ = oracle.layer_forward(x, prm, k1, k2, p, batch, seq, heads, d, act)
+    tp = {k: t64(v).requires_grad_() for k, v in prm.items()}
+    xt = t64(x).requires_grad_()
+    ref = _torch_layer(xt, tp, k1, k2, p, batch, seq, heads, d, act)
+    assert rel(out, ref.detach().numpy()) < 1e-12
+    ref.backward(t64(dy))
+    dx, grads, _ = oracle.layer_backward(x, prm, k1, k2, p, dy, batch, seq, heads, d, act)
+    assert rel(dx, xt.grad.numpy()) < 1e-11
+    for k in ("bqkv", "bo", "b1", "b2", "ln1_g", "ln2_b"):
         assert rel(grads[k], tp[k].grad.numpy()) < 1e-11, k
 
 
@@ -257,6 +278,7 @@ def _layer_pins():
     return [test_layer_norm_matches_torch, test_layer_norm_closed_forms, test_layer_norm_backward_matches_torch_autograd,
             test_dropout_special_cases, test_group_forward_backward_match_torch_autograd,
             test_group_backward_finite_differences, lambda: test_layer_matches_torch_autograd("gelu_tanh"),
+            test_layer_with_biases_matches_torch_autograd,
             test_stack_matches_torch_autograd]
 
 
