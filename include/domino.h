@@ -127,6 +127,9 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
  * H[R_i]·B_s[:, C_j], and the chunk's reduction Y[R_i, C_j] = Y_own + Σ peer_Y runs on
  * `comm` while the next chunk's GEMM runs on `compute`.
  *   X [T, hidden]; A_s [hidden, n1]; B_s [ffn_shard, hidden]            (inputs)
+ *   b1_s [n1] or NULL                  the column-parallel bias (deep-dive, "如何尝试
+ *                                      DeepSpeed-Domino": add_bias_linear), added before the
+ *                                      activation: Hpre = X·A_s + b1_s (bf16 only)
  *   Hpre [T, n1], H [T, ffn_shard]     saved for the backward           (outputs)
  *   Y_own [T, hidden]                  this rank's partial              (output)
  *   peer_Y  HOST array of n_partials-1 device pointers [T, hidden]      (inputs; NULL if P==1)
@@ -135,7 +138,7 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
  *   workspace, workspace_bytes         optional device scratch (see Workspace above)
  */
 domino_status domino_block_fwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
-                               void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
+                               const void* b1_s, void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t compute, hipStream_t comm);
 
@@ -158,13 +161,15 @@ size_t domino_block_bwd_workspace_size(const domino_mlp_desc* desc);
  *   dX_own, dX [T, hidden]; peer_dX HOST array of n_partials-1 device pointers; dX NULL or
  *                                       dX_own reduces in place into dX_own
  *   dA_s [hidden, n1], dB_s [ffn_shard, hidden]  fp32
+ *   d_b1_s [n1] fp32 or NULL            (+)= Σ_rows dHpre, the bias gradient (bf16 only; needs
+ *                                       the workspace)
  *   workspace, workspace_bytes          optional device scratch (see Workspace above)
  * Weight gradients are deterministic; the reduction order is fixed.
  */
 domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
                                const void* Hpre, const void* H, const void* dY, void* dHpre,
                                void* dX_own, const void* const* peer_dX, void* dX,
-                               float* dA_s, float* dB_s, int32_t accumulate,
+                               float* dA_s, float* dB_s, float* d_b1_s, int32_t accumulate,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t compute, hipStream_t comm);
 
@@ -176,6 +181,7 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
  * launch over all sequences; then per chunk: Y_own = O·B_o_s; Y = Y_own + Σ peer_Y on `comm`.
  *   X [T, hidden]; A_qkv_s [hidden, 3·heads·head_dim] = [Q | K | V] blocks, head j at
  *   columns j·head_dim within each block; B_o_s [heads·head_dim, hidden]   (inputs)
+ *   b_qkv_s [3·heads·head_dim] or NULL  column-parallel bias: QKV = X·A_qkv_s + b_qkv_s
  *   QKV [T, 3·heads·head_dim], O [T, heads·head_dim]   saved activations   (outputs)
  *   lse [T, heads] fp32 or NULL: per query row and head, ln Σ_{k ≤ q} exp(scale·q·k), the
  *                                       statistic the backward needs (output)
@@ -184,7 +190,7 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
  * head_dim must be 128; bf16 only.
  */
 domino_status domino_attn_block_fwd(const domino_attn_desc* desc, const void* X, const void* A_qkv_s,
-                                    const void* B_o_s, void* QKV, void* O, float* lse, void* Y_own,
+                                    const void* B_o_s, const void* b_qkv_s, void* QKV, void* O, float* lse, void* Y_own,
                                     const void* const* peer_Y, void* Y, void* workspace, size_t workspace_bytes,
                                     hipStream_t compute, hipStream_t comm);
 size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* desc);
@@ -206,6 +212,7 @@ size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* desc);
  *   dO [T, heads·head_dim], dQKV [T, 3·heads·head_dim]   caller-provided scratch/outputs
  *   dX_own, dX [T, hidden]; peer_dX HOST array of n_partials-1 device pointers
  *   dA_qkv_s [hidden, 3·heads·head_dim], dB_o_s [heads·head_dim, hidden]   fp32
+ *   d_b_qkv_s [3·heads·head_dim] fp32 or NULL  (+)= Σ_rows dQKV, the bias gradient
  *   workspace, workspace_bytes          device scratch of at least
  *                                       domino_attn_block_bwd_workspace_size bytes (required:
  *                                       it also holds the attention statistics)
@@ -215,7 +222,7 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* desc, const void* X,
                                     const void* B_o_s, const void* QKV, const void* O, const float* lse,
                                     const void* dY, void* dO, void* dQKV, void* dX_own,
                                     const void* const* peer_dX, void* dX, float* dA_qkv_s, float* dB_o_s,
-                                    int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                    float* d_b_qkv_s, int32_t accumulate, void* workspace, size_t workspace_bytes,
                                     hipStream_t compute, hipStream_t comm);
 size_t domino_attn_block_bwd_workspace_size(const domino_attn_desc* desc);
 
@@ -311,6 +318,8 @@ typedef struct {
   const void* b_2;                                /* [hidden] or NULL */
   const int32_t* keep_attn;                       /* keep masks [T][ceil(hidden/32)] (bit j % 32 of */
   const int32_t* keep_mlp;                        /* word j / 32) or NULL: no dropout there */
+  const void* b_qkv;                              /* [3·heads·head_dim] column-parallel bias or NULL */
+  const void* b_1;                                /* [n1] column-parallel bias or NULL */
 } domino_layer_params;
 
 /* One layer's activations: written by the forward and kept for the backward. All
@@ -354,6 +363,7 @@ typedef struct {
   void* dO;            /* [T, heads·head_dim] */
   void* dQKV;          /* [T, 3·heads·head_dim] */
   void* dx_attn_own; const void* const* peer_dx_attn; void* dx_attn;  /* attention input-gradient partials, sum */
+  float* d_b_qkv; float* d_b_1;                                       /* [3·heads·head_dim], [n1] or NULL */
 } domino_layer_grads;
 
 /*
@@ -420,7 +430,8 @@ typedef enum {
   DOMINO_K_ATTN_BWD_PREP = 17,  /* attention backward: Δ and the per-row statistics */
   DOMINO_K_GROUP_FWD = 18,      /* dropout + residual + LayerNorm */
   DOMINO_K_GROUP_BWD = 19,      /* its backward (with the fixed-order column sums) */
-  DOMINO_K_COUNT = 20
+  DOMINO_K_BIAS_GRAD = 20,      /* column sums of dHpre or dQKV (column-parallel bias gradients) */
+  DOMINO_K_COUNT = 21
 } domino_kernel_kind;
 
 domino_status domino_timing_enable(int32_t enable);   /* enabling also resets */

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "DOMINO_OK", 1: "DOMINO_ERR_INVALID_ARG", 2: "DOMINO_ERR_SHAP
 KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgrad_a": 4, "wgrad_b": 5,
                 "wgrad_a": 6, "qkv": 7, "attn": 8, "outproj": 9, "aux": 10, "attn_bwd_dkdv": 11, "outproj_dgrad": 12,
                 "qkv_dgrad": 13, "outproj_wgrad": 14, "qkv_wgrad": 15, "attn_bwd_dq": 16, "attn_bwd_prep": 17,
-                "group_fwd": 18, "group_bwd": 19}
+                "group_fwd": 18, "group_bwd": 19,
+                "bias_grad": 20}
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
@@ -65,7 +66,7 @@ _VP = ctypes.c_void_p
 
 class LayerParams(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("ln1_gamma", "ln1_beta", "A_qkv_s", "B_o_s", "b_o", "ln2_gamma", "ln2_beta", "A_s",
-                                   "B_s", "b_2", "keep_attn", "keep_mlp")]
+                                   "B_s", "b_2", "keep_attn", "keep_mlp", "b_qkv", "b_1")]
 
 
 class LayerActs(ctypes.Structure):
@@ -80,7 +81,7 @@ class LayerGrads(ctypes.Structure):
                                    "d_ln2_beta", "dA_s", "dB_s", "d_b_2", "d_x_in", "d_ym", "dHpre", "dx_mlp_own")] + \
         [("peer_dx_mlp", ctypes.POINTER(_VP))] + [(n, _VP) for n in ("dx_mlp", "d_h", "d_ya", "dO", "dQKV",
                                                                     "dx_attn_own")] + \
-        [("peer_dx_attn", ctypes.POINTER(_VP)), ("dx_attn", _VP)]
+        [("peer_dx_attn", ctypes.POINTER(_VP)), ("dx_attn", _VP), ("d_b_qkv", _VP), ("d_b_1", _VP)]
 
 
 class DominoError(RuntimeError):
@@ -105,22 +106,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     pp = ctypes.POINTER(ctypes.c_void_p)
     lib.shard_reduce.argtypes = [vp, i64, pp, i32, i64, i64, i64, i32, vp]
     lib.shard_reduce.restype = i32
-    lib.domino_block_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, pp, vp, vp, ctypes.c_size_t,
-                                     vp, vp]
+    lib.domino_block_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, pp, vp, vp,
+                                     ctypes.c_size_t, vp, vp]
     lib.domino_block_fwd.restype = i32
     for name, desc in (("domino_block_fwd_workspace_size", MlpDesc), ("domino_block_bwd_workspace_size", MlpDesc),
                        ("domino_attn_block_fwd_workspace_size", AttnDesc),
                        ("domino_attn_block_bwd_workspace_size", AttnDesc)):
         getattr(lib, name).argtypes = [ctypes.POINTER(desc)]
         getattr(lib, name).restype = ctypes.c_size_t
-    lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32,
-                                     vp, ctypes.c_size_t, vp, vp]
+    lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp,
+                                     i32, vp, ctypes.c_size_t, vp, vp]
     lib.domino_block_bwd.restype = i32
-    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, pp, vp, vp,
+    lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp,
                                           ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_fwd.restype = i32
     lib.domino_attn_block_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp,
-                                          vp, vp, i32, vp, ctypes.c_size_t, vp, vp]
+                                          vp, vp, vp, i32, vp, ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_bwd.restype = i32
     lib.domino_resid_ln_fwd.argtypes = [ctypes.POINTER(GroupDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.domino_resid_ln_fwd.restype = i32
@@ -191,8 +192,8 @@ def shard_reduce(out, ld_out: int, partials: Sequence, ld_in: int, rows: int, co
 
 
 def domino_block_fwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, Y_own, peer_Y, Y, workspace=None, workspace_bytes: int = 0,
-                     compute=None, comm=None):
-    _check(load().domino_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H),
+                     compute=None, comm=None, b1_s=None):
+    _check(load().domino_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(b1_s), _ptr(Hpre), _ptr(H),
                                    _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace), int(workspace_bytes),
                                    _stream(compute), _stream(comm)))
 
@@ -210,27 +211,29 @@ def domino_attn_block_fwd_workspace_size(desc: AttnDesc) -> int:
 
 
 def domino_block_bwd(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, peer_dX, dX, dA_s, dB_s,
-                     accumulate: int = 0, workspace=None, workspace_bytes: int = 0, compute=None, comm=None):
+                     accumulate: int = 0, workspace=None, workspace_bytes: int = 0, compute=None, comm=None,
+                     d_b1_s=None):
     _check(load().domino_block_bwd(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H), _ptr(dY),
                                    _ptr(dHpre), _ptr(dX_own), _ptr_array(peer_dX), _ptr(dX), _ptr(dA_s), _ptr(dB_s),
-                                   int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
+                                   _ptr(d_b1_s), int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
                                    _stream(comm)))
 
 
 def domino_attn_block_fwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, Y_own, peer_Y, Y, workspace=None,
-                          workspace_bytes: int = 0, compute=None, comm=None, lse=None):
-    _check(load().domino_attn_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
+                          workspace_bytes: int = 0, compute=None, comm=None, lse=None, b_qkv_s=None):
+    _check(load().domino_attn_block_fwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(b_qkv_s),
+                                        _ptr(QKV), _ptr(O),
                                         _ptr(lse), _ptr(Y_own), _ptr_array(peer_Y), _ptr(Y), _ptr(workspace),
                                         int(workspace_bytes), _stream(compute), _stream(comm)))
 
 
 def domino_attn_block_bwd(desc: AttnDesc, X, A_qkv_s, B_o_s, QKV, O, lse, dY, dO, dQKV, dX_own, peer_dX, dX,
                           dA_qkv_s, dB_o_s, accumulate: int = 0, workspace=None, workspace_bytes: int = 0,
-                          compute=None, comm=None):
+                          compute=None, comm=None, d_b_qkv_s=None):
     _check(load().domino_attn_block_bwd(ctypes.byref(desc), _ptr(X), _ptr(A_qkv_s), _ptr(B_o_s), _ptr(QKV), _ptr(O),
                                         _ptr(lse), _ptr(dY), _ptr(dO), _ptr(dQKV), _ptr(dX_own),
                                         _ptr_array(peer_dX), _ptr(dX), _ptr(dA_qkv_s), _ptr(dB_o_s),
-                                        int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
+                                        _ptr(d_b_qkv_s), int(accumulate), _ptr(workspace), int(workspace_bytes), _stream(compute),
                                         _stream(comm)))
 
 

@@ -206,6 +206,7 @@ domino_status check_layer_ptrs(const domino_layer_desc* d, const domino_layer_pa
         (st = need(p.b_o, "b_o", p.b_o)) || (st = need(p.ln2_gamma, "ln2_gamma", true)) ||
         (st = need(p.ln2_beta, "ln2_beta", p.ln2_beta)) || (st = need(p.A_s, "A_s", true)) ||
         (st = need(p.B_s, "B_s", true)) || (st = need(p.b_2, "b_2", p.b_2)) || (st = check_keep(p.keep_attn)) ||
+        (st = need(p.b_qkv, "b_qkv", p.b_qkv)) || (st = need(p.b_1, "b_1", p.b_1)) ||
         (st = check_keep(p.keep_mlp)) || (st = need(a.x_in, "x_in", l > 0)) || (st = need(a.ln1, "ln1", true)) ||
         (st = need(a.mean1, "mean1", true)) || (st = need(a.rstd1, "rstd1", true)) || (st = need(a.QKV, "QKV", true)) ||
         (st = need(a.O, "O", true)) || (st = need(a.lse, "lse", a.lse)) ||
@@ -576,9 +577,9 @@ size_t domino_block_fwd_workspace_size(const domino_mlp_desc* d) {
   return ws_bytes_of({mlp_gemm1(d, nullptr, nullptr, nullptr, nullptr), mlp_gemm2(d, nullptr, nullptr, nullptr, 0, 0)});
 }
 
-domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s, void* Hpre,
-                               void* H, void* Y_own, const void* const* peer_Y, void* Y, void* workspace,
-                               size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
+domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
+                               const void* b1_s, void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
+                               void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_mlp_desc(d);
   if (st != DOMINO_OK) return st;
@@ -586,20 +587,23 @@ domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const vo
   if (T == 0 || h == 0) return DOMINO_OK;
   const bool red = needs_reduce(d->n_partials, Y_own, Y);
   if ((st = check_ptr(X, "X", true)) || (st = check_ptr(A_s, "A_s", f > 0)) || (st = check_ptr(B_s, "B_s", f > 0)) ||
+      (st = check_ptr(b1_s, "b1_s", f > 0 && b1_s)) ||
       (st = check_ptr(Hpre, "Hpre", f > 0)) || (st = check_ptr(H, "H", f > 0)) || (st = check_ptr(Y_own, "Y_own", true)) ||
       (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) || (st = check_ptr(Y ? Y : Y_own, "Y", red)))
     return st;
+  if (b1_s && d->dtype != DOMINO_BF16) return fail(DOMINO_ERR_UNSUPPORTED, "b1_s needs bf16");
   if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
   Sched sc;
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
 
   const int64_t Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
+  GemmArgs g1 = mlp_gemm1(d, X, A_s, Hpre, H);
+  g1.bias = b1_s;
   std::string msg;
   // The first product (column-parallel, activation fused) feeds no reduction, so it runs
   // once over all rows: chunking it would only narrow the GEMM. The second product is
   // launched per Domino chunk, and each chunk's reduction starts as soon as it ends.
-  if (f > 0 && hip_ok(run_gemm(DOMINO_K_FWD_GEMM1, mlp_gemm1(d, X, A_s, Hpre, H), workspace, workspace_bytes, sc.cs),
-                      &msg, "GEMM1"))
+  if (f > 0 && hip_ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, workspace, workspace_bytes, sc.cs), &msg, "GEMM1"))
     return fail(DOMINO_ERR_HIP, msg);
   for (int i = 0; i < d->row_chunks; ++i) {
     for (int j = 0; j < d->col_chunks; ++j) {
@@ -617,14 +621,19 @@ domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const vo
 
 size_t domino_block_bwd_workspace_size(const domino_mlp_desc* d) {
   if (check_mlp_desc(d) != DOMINO_OK) return 0;
-  return ws_bytes_of({mlp_dgrad_b(d, nullptr, nullptr, nullptr, nullptr), mlp_dgrad_a(d, nullptr, nullptr, nullptr, 0, 0),
-                      mlp_wgrad_b(d, nullptr, nullptr, nullptr, 0), mlp_wgrad_a(d, nullptr, nullptr, nullptr, 0)});
+  const size_t bias =  // the bias gradient (bf16 only)
+      d->dtype == DOMINO_BF16 ? size_t(bias_grad_ws_floats(d->batch * d->seq, mlp_n1(d))) * sizeof(float) : 0;
+  return std::max(bias, ws_bytes_of({mlp_dgrad_b(d, nullptr, nullptr, nullptr, nullptr),
+                                     mlp_dgrad_a(d, nullptr, nullptr, nullptr, 0, 0),
+                                     mlp_wgrad_b(d, nullptr, nullptr, nullptr, 0),
+                                     mlp_wgrad_a(d, nullptr, nullptr, nullptr, 0)}));
 }
 
 domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
                                const void* Hpre, const void* H, const void* dY, void* dHpre, void* dX_own,
-                               const void* const* peer_dX, void* dX, float* dA_s, float* dB_s, int32_t accumulate,
-                               void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
+                               const void* const* peer_dX, void* dX, float* dA_s, float* dB_s, float* d_b1_s,
+                               int32_t accumulate, void* workspace, size_t workspace_bytes, hipStream_t compute,
+                               hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_mlp_desc(d);
   if (st != DOMINO_OK) return st;
@@ -637,9 +646,15 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
       (st = check_ptr(H, "H", tok && ffn)) || (st = check_ptr(dY, "dY", tok && ffn)) ||
       (st = check_ptr(dHpre, "dHpre", tok && ffn)) || (st = check_ptr(dX_own, "dX_own", tok)) ||
       (st = check_peers(peer_dX, d->n_partials, "peer_dX", red)) || (st = check_ptr(dX ? dX : dX_own, "dX", red)) ||
-      (st = check_ptr(dA_s, "dA_s", ffn)) || (st = check_ptr(dB_s, "dB_s", ffn)))
+      (st = check_ptr(dA_s, "dA_s", ffn)) || (st = check_ptr(dB_s, "dB_s", ffn)) ||
+      (st = check_ptr(d_b1_s, "d_b1_s", ffn && d_b1_s)))
     return st;
   if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (d_b1_s && ffn) {
+    if (d->dtype != DOMINO_BF16) return fail(DOMINO_ERR_UNSUPPORTED, "d_b1_s needs bf16");
+    if (!workspace || workspace_bytes < size_t(bias_grad_ws_floats(T, mlp_n1(d))) * sizeof(float))
+      return fail(DOMINO_ERR_INVALID_ARG, "d_b1_s needs a workspace of domino_block_bwd_workspace_size bytes");
+  }
   Sched sc;
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
 
@@ -671,6 +686,11 @@ domino_status domino_block_bwd(const domino_mlp_desc* d, const void* X, const vo
         hip_ok(run_gemm(DOMINO_K_WGRAD_A, mlp_wgrad_a(d, X, dHpre, dA_s, accumulate), workspace, workspace_bytes, sc.cs),
                &msg, "wgrad A"))
       return fail(DOMINO_ERR_HIP, msg);
+    if (d_b1_s && hip_ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
+                           return launch_bias_grad(dHpre, T, mlp_n1(d), mlp_n1(d), d_b1_s, accumulate,
+                                                   static_cast<float*>(workspace), sc.cs);
+                         }), &msg, "bias gradient"))
+      return fail(DOMINO_ERR_HIP, msg);
   }
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
@@ -682,7 +702,7 @@ size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* d) {
 }
 
 domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
-                                    void* QKV, void* O, float* lse, void* Y_own, const void* const* peer_Y, void* Y,
+                                    const void* b_qkv_s, void* QKV, void* O, float* lse, void* Y_own, const void* const* peer_Y, void* Y,
                                     void* workspace, size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_attn_desc(d);
@@ -693,7 +713,7 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
   const bool heads = d->heads > 0;
   if ((st = check_ptr(X, "X", heads)) || (st = check_ptr(A_qkv_s, "A_qkv_s", heads)) ||
       (st = check_ptr(B_o_s, "B_o_s", heads)) || (st = check_ptr(QKV, "QKV", heads)) || (st = check_ptr(O, "O", heads)) ||
-      (st = check_ptr(lse, "lse", heads && lse)) ||
+      (st = check_ptr(lse, "lse", heads && lse)) || (st = check_ptr(b_qkv_s, "b_qkv_s", heads && b_qkv_s)) ||
       (st = check_ptr(Y_own, "Y_own", true)) || (st = check_peers(peer_Y, d->n_partials, "peer_Y", red)) ||
       (st = check_ptr(Y ? Y : Y_own, "Y", red)))
     return st;
@@ -713,8 +733,9 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
     aa.lse = lse; aa.ld_lse = d->heads;
     aa.batch = d->batch; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
     aa.scale = scale;
-    if (hip_ok(run_gemm(DOMINO_K_QKV, attn_qkv(d, X, A_qkv_s, QKV), workspace, workspace_bytes, sc.cs), &msg,
-               "QKV GEMM") ||
+    GemmArgs gq = attn_qkv(d, X, A_qkv_s, QKV);
+    gq.bias = b_qkv_s;
+    if (hip_ok(run_gemm(DOMINO_K_QKV, gq, workspace, workspace_bytes, sc.cs), &msg, "QKV GEMM") ||
         hip_ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), &msg, "attention"))
       return fail(DOMINO_ERR_HIP, msg);
   }
@@ -733,16 +754,18 @@ domino_status domino_attn_block_fwd(const domino_attn_desc* d, const void* X, co
 size_t domino_attn_block_bwd_workspace_size(const domino_attn_desc* d) {
   if (check_attn_desc(d) != DOMINO_OK) return 0;
   const size_t stats = size_t(attn_bwd_stats_floats(d->batch * d->seq, d->heads)) * sizeof(float);
-  return std::max(stats, ws_bytes_of({attn_dout(d, nullptr, nullptr, nullptr), attn_dx(d, nullptr, nullptr, nullptr, 0),
-                                      attn_wgrad_o(d, nullptr, nullptr, nullptr, 0),
-                                      attn_wgrad_qkv(d, nullptr, nullptr, nullptr, 0)}));
+  const size_t bias = size_t(bias_grad_ws_floats(d->batch * d->seq, 3 * d->heads * d->head_dim)) * sizeof(float);
+  return std::max(std::max(stats, bias),
+                  ws_bytes_of({attn_dout(d, nullptr, nullptr, nullptr), attn_dx(d, nullptr, nullptr, nullptr, 0),
+                               attn_wgrad_o(d, nullptr, nullptr, nullptr, 0),
+                               attn_wgrad_qkv(d, nullptr, nullptr, nullptr, 0)}));
 }
 
 domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, const void* A_qkv_s, const void* B_o_s,
                                     const void* QKV, const void* O, const float* lse, const void* dY, void* dO,
                                     void* dQKV, void* dX_own, const void* const* peer_dX, void* dX, float* dA_qkv_s,
-                                    float* dB_o_s, int32_t accumulate, void* workspace, size_t workspace_bytes,
-                                    hipStream_t compute, hipStream_t comm) {
+                                    float* dB_o_s, float* d_b_qkv_s, int32_t accumulate, void* workspace,
+                                    size_t workspace_bytes, hipStream_t compute, hipStream_t comm) {
   t_last_error.clear();
   domino_status st = check_attn_desc(d);
   if (st != DOMINO_OK) return st;
@@ -756,10 +779,12 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
       (st = check_ptr(dY, "dY", tok && heads)) || (st = check_ptr(dO, "dO", tok && heads)) ||
       (st = check_ptr(dQKV, "dQKV", tok && heads)) || (st = check_ptr(dX_own, "dX_own", tok)) ||
       (st = check_peers(peer_dX, d->n_partials, "peer_dX", red)) || (st = check_ptr(dX ? dX : dX_own, "dX", red)) ||
-      (st = check_ptr(dA_qkv_s, "dA_qkv_s", heads)) || (st = check_ptr(dB_o_s, "dB_o_s", heads)))
+      (st = check_ptr(dA_qkv_s, "dA_qkv_s", heads)) || (st = check_ptr(dB_o_s, "dB_o_s", heads)) ||
+      (st = check_ptr(d_b_qkv_s, "d_b_qkv_s", heads && d_b_qkv_s)))
     return st;
-  const size_t stats_bytes = size_t(attn_bwd_stats_floats(T, d->heads)) * sizeof(float);
-  if (tok && heads && (!workspace || workspace_bytes < stats_bytes))
+  const size_t stats_bytes = std::max(size_t(attn_bwd_stats_floats(T, d->heads)),
+                                      d_b_qkv_s ? size_t(bias_grad_ws_floats(T, 3 * hd)) : size_t(0)) * sizeof(float);
+  if (((tok && heads) || d_b_qkv_s) && (!workspace || workspace_bytes < stats_bytes))
     return fail(DOMINO_ERR_INVALID_ARG, "workspace smaller than domino_attn_block_bwd_workspace_size");
   if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
   Sched sc;
@@ -804,6 +829,11 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
                                 workspace_bytes, sc.cs), &msg, "dB_o GEMM") ||
                 hip_ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(d, X, dQKV, dA_qkv_s, accumulate), workspace,
                                 workspace_bytes, sc.cs), &msg, "dA_qkv GEMM")))
+    return fail(DOMINO_ERR_HIP, msg);
+  if (heads && d_b_qkv_s && hip_ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
+                                     return launch_bias_grad(dQKV, T, 3 * hd, 3 * hd, d_b_qkv_s, accumulate,
+                                                             static_cast<float*>(workspace), sc.cs);
+                                   }), &msg, "bias gradient"))
     return fail(DOMINO_ERR_HIP, msg);
   if (!d->no_join && hip_ok(sc.join(), &msg, "join")) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
@@ -930,8 +960,9 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
       aa.lse = a.lse ? a.lse + r0 * d->heads : nullptr; aa.ld_lse = d->heads;
       aa.batch = d->batch / rc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
       aa.scale = scale;
-      ok(run_gemm(DOMINO_K_QKV, attn_qkv(&ad, at(a.ln1, r0 * h, 2), p.A_qkv_s, at(a.QKV, r0 * 3 * hd, 2)), workspace,
-                  workspace_bytes, sc.cs), "QKV GEMM") &&
+      GemmArgs gq = attn_qkv(&ad, at(a.ln1, r0 * h, 2), p.A_qkv_s, at(a.QKV, r0 * 3 * hd, 2));
+      gq.bias = p.b_qkv;
+      ok(run_gemm(DOMINO_K_QKV, gq, workspace, workspace_bytes, sc.cs), "QKV GEMM") &&
           ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), "attention") &&
           ok(run_gemm(DOMINO_K_OUTPROJ, attn_out(&ad, at(a.O, r0 * hd, 2), p.B_o_s, at(a.y_attn_own, r0 * h, 2), 0),
                       workspace, workspace_bytes, sc.cs), "out-projection") &&
@@ -939,11 +970,12 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
     }
     for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
       const int64_t r0 = mu * Tc;
+      GemmArgs g1 = mlp_gemm1(&md, at(a.ln2, r0 * h, 2), p.A_s, at(a.Hpre, r0 * n1, 2), at(a.H, r0 * f, 2));
+      g1.bias = p.b_1;
       ok(wait(a.y_attn, a.y_attn_own, 0, mu), "wait for the attention reduction") &&
           ok(group(x, a.y_attn, p.b_o, p.keep_attn, a.h, p.ln2_gamma, p.ln2_beta, a.ln2, a.mean2, a.rstd2, r0),
              "middle group") &&
-          ok(run_gemm(DOMINO_K_FWD_GEMM1, mlp_gemm1(&md, at(a.ln2, r0 * h, 2), p.A_s, at(a.Hpre, r0 * n1, 2),
-                                                    at(a.H, r0 * f, 2)), workspace, workspace_bytes, sc.cs), "GEMM1") &&
+          ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, workspace, workspace_bytes, sc.cs), "GEMM1") &&
           ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(&md, at(a.H, r0 * f, 2), p.B_s, at(a.y_mlp_own, r0 * h, 2), 0, 0),
                       workspace, workspace_bytes, sc.cs), "GEMM2") &&
           ok(reduce(a.y_mlp, a.y_mlp_own, a.peer_y_mlp, 1, mu), "reduce MLP");
@@ -985,7 +1017,11 @@ size_t domino_stack_bwd_workspace_size(const domino_layer_desc* d) {
   const int64_t Tc = s.md.batch * d->seq;
   if (Tc == 0 || d->hidden == 0) return 0;
   const size_t stats = size_t(attn_bwd_stats_floats(Tc, d->heads)) * sizeof(float);
-  const size_t part = size_t(3 * group_bwd_blocks(Tc) * d->hidden) * sizeof(float);
+  const size_t part = std::max(size_t(3 * group_bwd_blocks(Tc) * d->hidden),
+                               size_t(bias_grad_ws_floats(d->batch * d->seq,
+                                                          std::max(3 * d->heads * d->head_dim,
+                                                                   (d->act == DOMINO_ACT_SWIGLU ? 2 : 1) * d->ffn_shard)))) *
+                      sizeof(float);
   const size_t gemm = ws_bytes_of({mlp_dgrad_b(&s.md, nullptr, nullptr, nullptr, nullptr),
                                    mlp_dgrad_a(&s.md, nullptr, nullptr, nullptr, 0, 0),
                                    mlp_wgrad_b(&s.md_all, nullptr, nullptr, nullptr, 0),
@@ -1027,7 +1063,8 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
         (st = need(g.dO, "dO", true)) || (st = need(g.dQKV, "dQKV", true)) ||
         (st = need(g.dx_attn_own, "dx_attn_own", true)) ||
         (st = check_peers(g.peer_dx_attn, d->n_partials, (L + "peer_dx_attn").c_str(), P)) ||
-        (st = need(g.dx_attn, "dx_attn", true)) || (st = need(act[l].lse, "lse", true)))
+        (st = need(g.dx_attn, "dx_attn", true)) || (st = need(act[l].lse, "lse", true)) ||
+        (st = need(g.d_b_qkv, "d_b_qkv", g.d_b_qkv)) || (st = need(g.d_b_1, "d_b_1", g.d_b_1)))
       return st;
   }
   if (!workspace || workspace_bytes < domino_stack_bwd_workspace_size(d))
@@ -1098,6 +1135,10 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
                 sc.cs), "MLP dB") &&
         ok(run_gemm(DOMINO_K_WGRAD_A, mlp_wgrad_a(&s.md_all, a.ln2, g.dHpre, g.dA_s, accumulate), workspace,
                     workspace_bytes, sc.cs), "MLP dA");
+    if (g.d_b_1)
+      ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
+           return launch_bias_grad(g.dHpre, T, n1, n1, g.d_b_1, accumulate, static_cast<float*>(workspace), sc.cs);
+         }), "MLP bias gradient");
     for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
       const int64_t r0 = mu * Tc;
       AttnBwdArgs ab{};
@@ -1128,6 +1169,11 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
                 workspace_bytes, sc.cs), "dB_o GEMM") &&
         ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(&s.ad_all, a.ln1, g.dQKV, g.dA_qkv_s, accumulate), workspace,
                     workspace_bytes, sc.cs), "dA_qkv GEMM");
+    if (g.d_b_qkv)
+      ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
+           return launch_bias_grad(g.dQKV, T, 3 * hd, 3 * hd, g.d_b_qkv, accumulate, static_cast<float*>(workspace),
+                                   sc.cs);
+         }), "QKV bias gradient");
   }
   // Layer 0's LN1 backward with its residual gradient: dX.
   const domino_layer_params& p0 = prm[0];

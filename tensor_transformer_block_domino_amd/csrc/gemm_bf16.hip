@@ -179,6 +179,7 @@ struct KParams {
   void* C; int64_t ldc;
   uint16_t* C2; int64_t ldc2;
   const uint16_t* aux; int64_t ldaux;
+  const uint16_t* bias;  // column bias added before the forward epilogues, or null
   float* ws;             // k-split tiles' fp32 slices: [tile − dp_tiles][split][BM][BN]
   int64_t M, N, K, f_s;
   int tiles_m, tiles_n;
@@ -219,10 +220,23 @@ __device__ __forceinline__ AuxQuad load_aux4(const KParams& p, int64_t m, int64_
   return a;
 }
 
+// The column bias of outputs n..n+3 (a wave-uniform branch; no bias, no load).
+__device__ __forceinline__ f32x4_t add_bias4(const KParams& p, int64_t n, f32x4_t v) {
+  if (p.bias) {
+    const u32x2_t b = *reinterpret_cast<const u32x2_t*>(p.bias + n);
+    v.x += bf16_lo(b.x);
+    v.y += bf16_hi(b.x);
+    v.z += bf16_lo(b.y);
+    v.w += bf16_hi(b.y);
+  }
+  return v;
+}
+
 // Epilogue for 4 consecutive output columns n..n+3 of row m (n < N, all four in range).
 template <Epi kEpi>
 __device__ __forceinline__ void epilogue4(const KParams& p, int64_t m, int64_t n, f32x4_t v,
                                           const AuxQuad& ax) {
+  if constexpr (kEpi == Epi::kStore || kEpi == Epi::kGelu) v = add_bias4(p, n, v);
   if constexpr (kEpi == Epi::kStore) {
     store_bf16x4(static_cast<uint16_t*>(p.C) + m * p.ldc + n, v.x, v.y, v.z, v.w);
   } else if constexpr (kEpi == Epi::kGelu) {
@@ -256,6 +270,8 @@ __device__ __forceinline__ void epilogue4(const KParams& p, int64_t m, int64_t n
 
 // SwiGLU epilogue for FFN columns j..j+3 of row m: gate g and up u from the same lane.
 __device__ __forceinline__ void epilogue_swiglu4(const KParams& p, int64_t m, int64_t j, f32x4_t g, f32x4_t u) {
+  g = add_bias4(p, j, g);
+  u = add_bias4(p, p.f_s + j, u);
   uint16_t* hp = static_cast<uint16_t*>(p.C) + m * p.ldc;
   store_bf16x4(hp + j, g.x, g.y, g.z, g.w);
   store_bf16x4(hp + p.f_s + j, u.x, u.y, u.z, u.w);
@@ -791,6 +807,7 @@ KParams make_params(const GemmArgs& g, const Plan& pl) {
   kp.C = g.C; kp.ldc = g.ldc;
   kp.C2 = static_cast<uint16_t*>(g.C2); kp.ldc2 = g.ldc2;
   kp.aux = static_cast<const uint16_t*>(g.aux); kp.ldaux = g.ldaux;
+  kp.bias = static_cast<const uint16_t*>(g.bias);
   kp.ws = g.ws;
   kp.M = g.M; kp.N = g.N; kp.K = g.K; kp.f_s = g.f_s;
   kp.tiles_m = pl.tiles_m; kp.tiles_n = pl.tiles_n;

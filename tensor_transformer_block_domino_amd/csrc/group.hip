@@ -301,6 +301,27 @@ __global__ __launch_bounds__(256) void colsum_kernel(ColsumParams p) {
   }
 }
 
+// Stage one of a bias gradient: workgroup (column block, row block) sums 64 rows of 2048
+// columns (8 per thread, 16-byte loads) into part[row block][col].
+constexpr int kBiasRows = 64;
+__global__ __launch_bounds__(256) void colpart_bf16_kernel(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                                           float* part) {
+  const int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (c >= cols) return;
+  const int64_t r0 = int64_t(blockIdx.y) * kBiasRows;
+  const int64_t r1 = r0 + kBiasRows < rows ? r0 + kBiasRows : rows;
+  float s[8] = {};
+  for (int64_t r = r0; r < r1; ++r) {
+    float v[8];
+    unpack8(ld16(x + r * ld + c), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += v[e];
+  }
+  float* dst = part + int64_t(blockIdx.y) * cols + c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = s[e];
+}
+
 constexpr int kBwdBlocks = 512;
 
 template <int CPL>
@@ -315,6 +336,36 @@ hipError_t launch_bwd(const GroupBwdParams& p, int blocks, hipStream_t s) {
 }
 
 }  // namespace
+
+int64_t bias_grad_ws_floats(int64_t rows, int64_t cols) { return ((rows + kBiasRows - 1) / kBiasRows) * cols; }
+
+hipError_t launch_bias_grad(const void* x, int64_t rows, int64_t cols, int64_t ld, float* out, int accumulate,
+                            float* ws, hipStream_t s) {
+  if (cols == 0) return hipSuccess;
+  if (rows == 0) {
+    if (accumulate) return hipSuccess;
+    ColsumParams cp{};  // nb = 0: writes zeros
+    cp.part = ws;
+    cp.out[0] = out;
+    cp.h = int(cols);
+    hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
+    return hipGetLastError();
+  }
+  const unsigned rb = unsigned((rows + kBiasRows - 1) / kBiasRows);
+  note_kernel("colpart_bf16_kernel");
+  hipLaunchKernelGGL(colpart_bf16_kernel, dim3(unsigned((cols / 8 + 255) / 256), rb), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), rows, cols, ld, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ColsumParams cp{};
+  cp.part = ws;
+  cp.out[0] = out;
+  cp.nb = int(rb);
+  cp.h = int(cols);
+  cp.accumulate = accumulate;
+  hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
+  return hipGetLastError();
+}
 
 int64_t group_bwd_blocks(int64_t rows) {
   const int64_t b = (rows + 7) / 8;

@@ -48,6 +48,8 @@ struct GemmArgs {
   float* ws;                  // fp32 slices of k-split tiles; null: every tile runs whole
   int64_t ws_elems;           // capacity of ws in floats
   bool bf16;                  // operand dtype: bf16 (MFMA path) or fp32 (vector-ALU path)
+  const void* bias = nullptr; // bf16 [N] (kSwiglu: [gate | up], 2·f_s) added before the epilogue's
+                              // activation (kStore, kGelu, kSwiglu; bf16 path only)
 };
 
 // Set by launch_gemm when the product left k-split tiles for launch_gemm_fixup, which the
@@ -108,6 +110,12 @@ struct GroupBwdArgs {
   float p_drop;
 };
 int64_t group_bwd_blocks(int64_t rows);
+
+// Column sums of a bf16 [rows, cols] matrix (leading dimension ld), out (+)= Σ_rows, in a
+// fixed order; ws holds bias_grad_ws_floats(rows, cols) floats.
+int64_t bias_grad_ws_floats(int64_t rows, int64_t cols);
+hipError_t launch_bias_grad(const void* x, int64_t rows, int64_t cols, int64_t ld, float* out, int accumulate,
+                            float* ws, hipStream_t s);
 hipError_t launch_resid_ln_bwd(const GroupBwdArgs& a, hipStream_t s);
 
 }  // namespace domino

@@ -47,6 +47,22 @@ def attn_shard_weights(Aqkv: torch.Tensor, Bo: torch.Tensor, heads_full: int, he
     return A_s.contiguous(), Bo[c0:c1, :].contiguous()
 
 
+def mlp_shard_bias(b1: torch.Tensor, act: str, P: int, r: int):
+    """Rank r's slice of the first MLP product's bias ([gate | up] for SwiGLU)."""
+    F = b1.numel() // (2 if act == "swiglu" else 1)
+    f = F // P
+    if act == "swiglu":
+        return torch.cat([b1[r * f:(r + 1) * f], b1[F + r * f:F + (r + 1) * f]]).contiguous()
+    return b1[r * f:(r + 1) * f].contiguous()
+
+
+def attn_shard_bias(bqkv: torch.Tensor, heads_full: int, head_dim: int, P: int, r: int):
+    """Rank r's slice of the QKV bias: its heads' columns of each of Q, K, V."""
+    Hd = heads_full * head_dim
+    c0, c1 = r * (Hd // P), (r + 1) * (Hd // P)
+    return torch.cat([bqkv[k * Hd + c0:k * Hd + c1] for k in range(3)]).contiguous()
+
+
 class MlpGroup:
     """P ranks of an MLP layer on one device; rank 0 is the measured rank."""
 
@@ -227,14 +243,21 @@ class LayerGroup:
             for r in range(P):
                 Aq, Bo = attn_shard_weights(lay["Aqkv"], lay["Bo"], heads_shard * P, head_dim, P, r)
                 A_s, B_s = mlp_shard_weights(lay["A"], lay["B"], act, P, r)
-                ranks.append(dict(A_qkv_s=Aq.to(**bf), B_o_s=Bo.to(**bf), A_s=A_s.to(**bf), B_s=B_s.to(**bf)))
+                rk = dict(A_qkv_s=Aq.to(**bf), B_o_s=Bo.to(**bf), A_s=A_s.to(**bf), B_s=B_s.to(**bf), b_qkv_s=None,
+                          b_1_s=None)
+                if lay.get("bqkv") is not None:
+                    rk["b_qkv_s"] = attn_shard_bias(lay["bqkv"], heads_shard * P, head_dim, P, r).to(**bf)
+                if lay.get("b1") is not None:
+                    rk["b_1_s"] = mlp_shard_bias(lay["b1"], act, P, r).to(**bf)
+                ranks.append(rk)
             self.rank_prm.append(ranks)
             dev_or_none = lambda k: None if lay.get(k) is None else lay[k].to(device).contiguous()  # noqa: E731
             self.params.append(dict(ln1_gamma=dev_or_none("ln1_g"), ln1_beta=dev_or_none("ln1_b"),
                                     A_qkv_s=ranks[0]["A_qkv_s"], B_o_s=ranks[0]["B_o_s"], b_o=dev_or_none("bo"),
                                     ln2_gamma=dev_or_none("ln2_g"), ln2_beta=dev_or_none("ln2_b"),
                                     A_s=ranks[0]["A_s"], B_s=ranks[0]["B_s"], b_2=dev_or_none("b2"),
-                                    keep_attn=dev_or_none("keep1"), keep_mlp=dev_or_none("keep2")))
+                                    keep_attn=dev_or_none("keep1"), keep_mlp=dev_or_none("keep2"),
+                                    b_qkv=ranks[0]["b_qkv_s"], b_1=ranks[0]["b_1_s"]))
             peer = dict(y_attn=[torch.empty(T, h, **bf) for _ in range(P - 1)],
                         y_mlp=[torch.empty(T, h, **bf) for _ in range(P - 1)])
             self.peer.append(peer)
@@ -286,14 +309,14 @@ class LayerGroup:
             for r in range(P):
                 dst = own if r == 0 else peer["y_attn"][r - 1]
                 L.domino_attn_block_fwd(ad, a, ranks[r]["A_qkv_s"], ranks[r]["B_o_s"], qkv, o, dst, None, None,
-                                        self.ws, self.ws_bytes, stream, None)
+                                        self.ws, self.ws_bytes, stream, None, b_qkv_s=ranks[r]["b_qkv_s"])
             L.shard_reduce(y, h, [own] + peer["y_attn"], h, T, h, L.DOMINO_BF16, stream)
             L.domino_resid_ln_fwd(gd, x, y, prm["b_o"], prm["keep_attn"], hh, prm["ln2_gamma"], prm["ln2_beta"], m,
                                   mean, rstd, stream)
             for r in range(P):
                 dst = own if r == 0 else peer["y_mlp"][r - 1]
                 L.domino_block_fwd(md, m, ranks[r]["A_s"], ranks[r]["B_s"], hpre, hmid, dst, None, None, self.ws,
-                                   self.ws_bytes, stream, None)
+                                   self.ws_bytes, stream, None, b1_s=ranks[r]["b_1_s"])
             L.shard_reduce(y, h, [own] + peer["y_mlp"], h, T, h, L.DOMINO_BF16, stream)
             x = nxt[l % 2]
             L.domino_resid_ln_fwd(gd, hh, y, prm["b_2"], prm["keep_mlp"], x, None, None, None, None, None, stream)
@@ -331,7 +354,9 @@ class LayerGroup:
                 peer_dx_mlp=pg["dx_mlp"] if P > 1 else None, dx_mlp=torch.empty(T, h, **bf),
                 d_h=torch.empty(T, h, **bf), d_ya=torch.empty(T, h, **bf), dO=torch.empty(T, hd, **bf),
                 dQKV=torch.empty(T, 3 * hd, **bf), dx_attn_own=torch.empty(T, h, **bf),
-                peer_dx_attn=pg["dx_attn"] if P > 1 else None, dx_attn=torch.empty(T, h, **bf)))
+                peer_dx_attn=pg["dx_attn"] if P > 1 else None, dx_attn=torch.empty(T, h, **bf),
+                d_b_qkv=torch.zeros(3 * hd, **f32) if self.params[l]["b_qkv"] is not None else None,
+                d_b_1=torch.zeros(n1, **f32) if self.params[l]["b_1"] is not None else None))
         self.bws_bytes = max(L.domino_stack_bwd_workspace_size(self.desc()),
                              L.domino_stack_bwd_workspace_size(self.desc(row_chunks=1)),
                              L.domino_attn_block_bwd_workspace_size(self._attn_desc()),
@@ -367,7 +392,7 @@ class LayerGroup:
             for k in range(P):
                 dst = own if k == 0 else torch.empty(T, h, **bf)
                 L.domino_attn_block_fwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, dst, None, None,
-                                        self.ws, self.ws_bytes, stream, None)
+                                        self.ws, self.ws_bytes, stream, None, b_qkv_s=ranks[k]["b_qkv_s"])
                 parts.append(dst)
             L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
             L.domino_resid_ln_fwd(gd, x, y, prm["b_o"], prm["keep_attn"], r["hh"], prm["ln2_gamma"], prm["ln2_beta"],
@@ -376,7 +401,7 @@ class LayerGroup:
             for k in range(P):
                 dst = own if k == 0 else torch.empty(T, h, **bf)
                 L.domino_block_fwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, dst, None, None, self.ws,
-                                   self.ws_bytes, stream, None)
+                                   self.ws_bytes, stream, None, b1_s=ranks[k]["b_1_s"])
                 parts.append(dst)
             L.shard_reduce(y, h, parts, h, T, h, L.DOMINO_BF16, stream)
             x = torch.empty(T, h, **bf)
@@ -396,7 +421,7 @@ class LayerGroup:
             parts = []
             for k in range(P):
                 L.domino_block_fwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, y_fwd, None, None,
-                                   self.ws, self.ws_bytes, stream, None)
+                                   self.ws, self.ws_bytes, stream, None, b1_s=ranks[k]["b_1_s"])
                 dst = own if k == 0 else pg["dx_mlp"][k - 1]
                 L.domino_block_bwd(md, r["m"], ranks[k]["A_s"], ranks[k]["B_s"], hpre, hmid, d_ym, dHpre, dst, None,
                                    None, dA_m, dB_m, 0, self.bws, self.bws_bytes, stream, None)
@@ -407,7 +432,7 @@ class LayerGroup:
             parts = []
             for k in range(P):
                 L.domino_attn_block_fwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, y_fwd, None, None,
-                                        self.ws, self.ws_bytes, stream, None, lse=lse)
+                                        self.ws, self.ws_bytes, stream, None, lse=lse, b_qkv_s=ranks[k]["b_qkv_s"])
                 dst = own if k == 0 else pg["dx_attn"][k - 1]
                 L.domino_attn_block_bwd(ad, r["a"], ranks[k]["A_qkv_s"], ranks[k]["B_o_s"], qkv, o, lse, d_ya, dO, dQKV,
                                         dst, None, None, dA_a, dB_a, 0, self.bws, self.bws_bytes, stream, None)

@@ -226,3 +226,55 @@ def test_stack_backward_schedule_and_accumulate():
     for k, v in first.items():
         for a, G in zip(v, g.grads):
             torch.testing.assert_close(G[k], 2 * a, rtol=1e-5, atol=1e-5)
+
+
+def add_column_biases(inp, w, seed=7):
+    gen = torch.Generator().manual_seed(seed)
+    n_a = 2 if w.act == "swiglu" else 1
+    for lay in inp["layers"]:
+        lay["bqkv"] = (torch.randn(3 * w.heads_full * w.head_dim, generator=gen) * 0.1).to(torch.bfloat16)
+        lay["b1"] = (torch.randn(n_a * w.ffn_full, generator=gen) * 0.1).to(torch.bfloat16)
+        lay["bo"] = (torch.randn(w.hidden, generator=gen) * 0.1).to(torch.bfloat16)
+        lay["b2"] = (torch.randn(w.hidden, generator=gen) * 0.1).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_stack_with_all_biases(act):
+    """The column-parallel biases (QKV, first MLP product: in the GEMM epilogue, before the
+    attention / activation) and the row-parallel ones (after the sum); every bias gradient."""
+    from tensor_transformer_block_domino_amd.tp_sim import attn_shard_bias, mlp_shard_bias
+
+    w = small_workload(act)
+    print(f"layer stack with all biases act={act}", flush=True)
+    inp = synth.layer_inputs(w)
+    add_column_biases(inp, w)
+    g = LayerGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
+                   ffn_shard=w.ffn_shard, act=w.act, row_chunks=w.row_chunks, n_partials=w.n_partials,
+                   p_drop=w.p_drop, X=inp["X"], layers=inp["layers"], device=dev())
+    g.alloc_backward(inp["dY"])
+    g.peer_forward()
+    g.peer_backward()
+    g.forward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
+    g.backward(compute=torch.cuda.current_stream(), comm=torch.cuda.Stream())
+    sync()
+    X = oracle.to_f64(inp["X"])
+    layers, keeps = [], []
+    for lay in inp["layers"]:
+        layers.append({k: oracle.to_f64(lay[k]) for k in ("ln1_g", "ln1_b", "Aqkv", "bqkv", "Bo", "bo", "ln2_g",
+                                                          "ln2_b", "A", "b1", "B", "b2")})
+        keeps.append((oracle.unpack_keep(lay["keep1"].numpy(), w.hidden),
+                      oracle.unpack_keep(lay["keep2"].numpy(), w.hidden)))
+    out, _ = oracle.stack_forward(X, layers, keeps, w.p_drop, w.batch, w.seq, w.heads_full, w.head_dim, w.act)
+    check("out", f64(g.out), out, BF16_TOL)
+    dx, per = oracle.stack_backward(X, layers, keeps, w.p_drop, oracle.to_f64(inp["dY"]), w.batch, w.seq,
+                                    w.heads_full, w.head_dim, w.act)
+    check("dX", f64(g.dX), dx, BF16_TOL)
+    for l in range(w.layers):
+        gr = per[l][0]
+        G = g.grads[l]
+        ref_bqkv = attn_shard_bias(torch.from_numpy(gr["bqkv"]), w.heads_full, w.head_dim, w.n_partials, 0).numpy()
+        ref_b1 = mlp_shard_bias(torch.from_numpy(gr["b1"]), w.act, w.n_partials, 0).numpy()
+        check(f"d_b_qkv[{l}]", f64(G["d_b_qkv"]), ref_bqkv, BF16_TOL)
+        check(f"d_b_1[{l}]", f64(G["d_b_1"]), ref_b1, BF16_TOL)
+        check(f"d_b_o[{l}]", f64(G["d_b_o"]), gr["bo"], BF16_TOL)
+        check(f"d_b_2[{l}]", f64(G["d_b_2"]), gr["b2"], BF16_TOL)

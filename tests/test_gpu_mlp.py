@@ -177,3 +177,37 @@ def test_mlp_more_than_two_chunks_per_axis(split):
     g1, _ = run_fwd_bwd(w1, inputs=inp)
     for name in ("Y", "dX", "dA", "dB"):
         assert torch.equal(getattr(g, name), getattr(g1, name)), name
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_mlp_block_with_bias(act):
+    """b1_s in GEMM1's epilogue (before the activation) and d_b1_s = Σ_rows dHpre."""
+    from oracle import layer as olayer
+    from tensor_transformer_block_domino_amd.tp_sim import mlp_shard_bias
+
+    w = small_workload(act, split=(2, 1), seed=31)
+    inp = synth.mlp_inputs(w)
+    n_a = 2 if act == "swiglu" else 1
+    b1 = (torch.randn(n_a * w.ffn_full, generator=torch.Generator().manual_seed(5)) * 0.1).to(torch.bfloat16)
+    print(f"mlp with bias act={act} T={w.tokens}", flush=True)
+    g = make_group(w, inp)
+    d = dev()
+    shards = [mlp_shard_bias(b1, act, w.n_partials, r).to(d) for r in range(w.n_partials)]
+    for r in range(1, w.n_partials):
+        D.domino_block_fwd(g.desc(rank_alone=True, row_chunks=1, col_chunks=1), g.X, g.A_s[r], g.B_s[r], g.Hpre[r],
+                           g.H[r], g.Y_own[r], None, None, g.ws, g.ws_bytes, b1_s=shards[r])
+    peers = [g.Y_own[r] for r in range(1, w.n_partials)]
+    D.domino_block_fwd(g.desc(), g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], peers, g.Y, g.ws, g.ws_bytes,
+                       None, torch.cuda.Stream(), b1_s=shards[0])
+    dB1 = torch.empty(n_a * w.ffn_shard, device=d)
+    D.domino_block_bwd(g.desc(rank_alone=True), g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.dY, g.dHpre[0],
+                       g.dX_own[0], None, None, g.dA, g.dB, 0, g.ws, g.ws_bytes, d_b1_s=dB1)
+    sync()
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    b1f = oracle.to_f64(b1)
+    check("Y", f64(g.Y), olayer.mlp_sublayer(X, A, b1f, B, act), BF16_TOL)
+    A0, B0 = oracle.mlp_shard_weights(A, B, act, w.n_partials, 0)
+    b10 = oracle.to_f64(shards[0].cpu())
+    dHpre0 = oracle.act_backward(X @ A0 + b10, dY @ B0.T, act)
+    check("dHpre", f64(g.dHpre[0]), dHpre0, BF16_TOL)
+    check("d_b1_s", f64(dB1), dHpre0.sum(axis=0), BF16_TOL)
