@@ -321,9 +321,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 }
 
 // dQ of 128 queries of one (sequence, head).
+//
+// Each wave owns 32 queries (Q, dO fragments, LSE and Δ in registers); blocks of 64 keys
+// stream through LDS. Per block: S and dP for the two 32-key halves with one query per lane
+// (K and V fragments read four k-steps ahead), dS = P·(dP − Δ), then dQᵀ += Kᵀ·dSᵀ with K
+// read transposed. Key blocks that end before the workgroup's first query are whole for
+// every wave (main loop, no mask); the last two blocks hold the diagonals and are peeled.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kBlk * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kBlk * kD];
+  agpr_accumulators();
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,71 +381,88 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   };
 
   const float c = p.scale_log2;
-  issue(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int st = kb & 1;
-    wait_vm_barrier<0>();
-    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
-    const int k0 = kb * kBlk;
-    if (k0 > qw + 31 || qw >= p.seq) continue;  // every key of the block is in this wave's future
-
-    // S[key][query] and dP[key][query] for keys 32nb + 8j + 4h + r: X = the tile's rows.
-    u32x4_t kr[8][2], vr[8][2];
+  // One block of 64 keys from stage st. lim: the lane's query sees key k0 + 4h + off
+  // (off = 32nb + 8j + r) iff off ≤ lim; masked only on the blocks that reach the diagonal.
+  auto block = [&](int st, bool masked, int lim) {
+    // Pin the dQ accumulators to AGPRs across blocks (else the allocator moves them through
+    // VGPRs at every loop boundary).
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(dq[i]));
+    // K and V fragments in the order (s, nb), four pairs ahead; pair i = 2s + nb.
+    u32x4_t kr[16], vr[16];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        lds_read_b128(kr[s][nb], &sK[st][t_off(nb * 32 + l32, 2 * s + h)]);
-        lds_read_b128(vr[s][nb], &sV[st][t_off(nb * 32 + l32, 2 * s + h)]);
+    for (int i = 0; i < 4; ++i) {
+      lds_read_b128(kr[i], &sK[st][t_off((i & 1) * 32 + l32, 2 * (i >> 1) + h)]);
+      lds_read_b128(vr[i], &sV[st][t_off((i & 1) * 32 + l32, 2 * (i >> 1) + h)]);
+    }
+    const f32x16_t zero = {};
+    f32x16_t sacc[2] = {zero, zero}, pacc[2] = {zero, zero};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = i >> 1, nb = i & 1;
+      // Issued so far: pairs 0 .. min(i, 12) + 3; pair i is reads 2i, 2i + 1.
+      lgkm_wait_tied(2 * ((i < 12 ? i : 12) + 4) - 2 * i - 2, kr[i], vr[i]);
+      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[i]),
+                                                        __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
+      pacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vr[i]),
+                                                        __builtin_bit_cast(bf16x8_t, df[s]), pacc[nb], 0, 0, 0);
+      if (i + 4 < 16) {
+        const int j = i + 4;
+        lds_read_b128(kr[j], &sK[st][t_off((j & 1) * 32 + l32, 2 * (j >> 1) + h)]);
+        lds_read_b128(vr[j], &sV[st][t_off((j & 1) * 32 + l32, 2 * (j >> 1) + h)]);
       }
-    f32x16_t sacc[2], pacc[2];
+    }
+    // dS, packed to the bf16 B operands of the four 16-key steps.
+    u32x4_t sf[4];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[nb][r] = pacc[nb][r] = 0.f;
-    lds_wait_all();
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        tie(kr[s][nb]);
-        tie(vr[s][nb]);
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s][nb]),
-                                                          __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
-        pacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vr[s][nb]),
-                                                          __builtin_bit_cast(bf16x8_t, df[s]), pacc[nb], 0, 0, 0);
-      }
-    // Transposed K for dQᵀ += Kᵀ·dSᵀ, four 16-key steps.
-    u32x4_t kt[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) read_tr_frag(kt[t][db], sK[st], t, db, lane);
-    // dS; key k0 + 4h + off (off = 32nb + 8j + r) is visible iff off ≤ lim.
-    const bool edge = k0 + kBlk - 1 > qw || k0 + kBlk > p.seq;  // wave-uniform
-    const int lim = min(q, p.seq - 1) - k0 - 4 * h;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      f32x16_t ds;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int off = nb * 32 + 8 * (e >> 2) + (e & 3);
         float pe = __builtin_amdgcn_exp2f(fmaf(sacc[nb][e], c, -l2));
-        if (edge) pe = off <= lim ? pe : 0.f;
-        sacc[nb][e] = pe * (pacc[nb][e] - dl);
+        if (masked) pe = off <= lim ? pe : 0.f;
+        ds[e] = pe * (pacc[nb][e] - dl);
       }
-    lds_wait_all();
+      sf[2 * nb] = pack_step(ds, 0);
+      sf[2 * nb + 1] = pack_step(ds, 1);
+    }
+    // dQᵀ += Kᵀ·dSᵀ: K read transposed, one 16-key step ahead (8 reads per step).
+    u32x4_t kt[2][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) tie(kt[t][db]);
+    for (int db = 0; db < 4; ++db) read_tr_frag(kt[0][db], sK[st], 0, db, lane);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const u32x4_t sf = pack_step(sacc[t >> 1], t & 1);
+      if (t + 1 < 4) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kt[t][db]),
-                                                        __builtin_bit_cast(bf16x8_t, sf), dq[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) read_tr_frag(kt[(t + 1) & 1][db], sK[st], t + 1, db, lane);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        lgkm_wait_tied1((t + 1 < 4 ? 8 : 0) + 2 * (3 - db), kt[t & 1][db]);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kt[t & 1][db]),
+                                                        __builtin_bit_cast(bf16x8_t, sf[t]), dq[db], 0, 0, 0);
+      }
     }
+  };
+
+  // Blocks before the workgroup's first query: whole for every wave.
+  const int kfull = min(q0 / kBlk, nkb);
+  issue(0, 0);
+  for (int kb = 0; kb < kfull; ++kb) {
+    const int st = kb & 1;
+    wait_vm_barrier<0>();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    block(st, false, 0);
+  }
+  // The last (at most two) blocks: each wave's diagonal, masked; blocks wholly after a
+  // wave's queries are skipped by it.
+  for (int kb = kfull; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    wait_vm_barrier<0>();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const int k0 = kb * kBlk;
+    if (k0 <= qw + 31 && qw < p.seq) block(st, true, min(q, p.seq - 1) - k0 - 4 * h);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
