@@ -33,6 +33,11 @@ struct GroupBwdParams {
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// Rows that are read once: non-temporal loads (measured 3.9 -> 4.4 TB/s for both kernels at
+// 8192 x 4096, against 5.1 TB/s for a 1 GiB device copy).
+__device__ __forceinline__ u32x4_t ld16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 __device__ __forceinline__ void st16(uint16_t* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 __device__ __forceinline__ void unpack8(u32x4_t w, float (&f)[8]) {
@@ -68,9 +73,9 @@ __global__ __launch_bounds__(256) void resid_ln_fwd_kernel(GroupFwdParams p) {
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
-      rw[i] = ld16(p.resid + base + 8 * c);
+      rw[i] = ld16_stream(p.resid + base + 8 * c);
       if (p.y) {
-        yw[i] = ld16(p.y + base + 8 * c);
+        yw[i] = ld16_stream(p.y + base + 8 * c);
         bw[i] = p.bias ? ld16(p.bias + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
         kb[i] = p.keep ? p.keep[row * p.keep_row_bytes + c] : 0xffu;
       }
@@ -159,9 +164,9 @@ __global__ __launch_bounds__(256) void resid_ln_bwd_kernel(GroupBwdParams p) {
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       if (c >= nch) continue;
-      if (p.d_res) rs_[i] = ld16(p.d_res + base + 8 * c);
+      if (p.d_res) rs_[i] = ld16_stream(p.d_res + base + 8 * c);
       if (p.want_ln) {
-        ln_[i] = ld16(p.d_ln + base + 8 * c);
+        ln_[i] = ld16_stream(p.d_ln + base + 8 * c);
         r_[i] = ld16(p.r_out + base + 8 * c);
       }
     }
