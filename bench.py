@@ -340,6 +340,7 @@ def main_layer(args, w):
     print(f"[bench] layer stack domino step {ms:.3f} ms", file=sys.stderr, flush=True)
     ms_serial = timed_steps(step_serial, args.steps, 2)
     ms_unsplit = timed_steps(step_unsplit, args.steps, 2)
+    ms_graph = graph_steps(step_domino, compute, args.steps)
     D.domino_timing_enable(True)
     for _ in range(args.steps):
         step_domino()
@@ -381,6 +382,7 @@ def main_layer(args, w):
         "t_domino_ms": round(ms, 4),
         "t_serial_ms": round(ms_serial, 4),
         "t_unsplit_ms": round(ms_unsplit, 4),
+        "t_graph_ms": round(ms_graph, 4),
         "t_reduce_ms": round(per["reduce"][1] / args.steps, 4),
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
         "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
@@ -396,6 +398,19 @@ def main_layer(args, w):
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_layer(w, inp)
     print(json.dumps(out), flush=True)
+
+
+def graph_steps(fn, stream, steps):
+    """The step captured once into a HIP graph on `stream` and replayed: ms per replay."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return timed_steps(graph.replay, steps, 2)
 
 
 def timed_steps(fn, steps, warmup):
@@ -478,6 +493,7 @@ def main():
     print(f"[bench] domino step {ms:.3f} ms", file=sys.stderr, flush=True)
     ms_serial = timed(step_serial, args.steps, 2)
     ms_unsplit = timed(step_unsplit, args.steps, 2)
+    ms_graph = graph_steps(step_domino, compute, args.steps)
     print(f"[bench] serial {ms_serial:.3f} ms, unsplit without reduce {ms_unsplit:.3f} ms", file=sys.stderr,
           flush=True)
 
@@ -549,6 +565,7 @@ def main():
         "t_domino_ms": round(ms, 4),
         "t_serial_ms": round(ms_serial, 4),
         "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
+        "t_graph_ms": round(ms_graph, 4),
         "t_reduce_ms": round(red_ms_step, 4),
         "hidden_fraction": None if hidden_frac is None else round(hidden_frac, 3),
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
