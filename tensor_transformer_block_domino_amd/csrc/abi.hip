@@ -782,9 +782,7 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
       (st = check_ptr(dA_qkv_s, "dA_qkv_s", heads)) || (st = check_ptr(dB_o_s, "dB_o_s", heads)) ||
       (st = check_ptr(d_b_qkv_s, "d_b_qkv_s", heads && d_b_qkv_s)))
     return st;
-  const size_t stats_bytes = std::max(size_t(attn_bwd_stats_floats(T, d->heads)),
-                                      d_b_qkv_s ? size_t(bias_grad_ws_floats(T, 3 * hd)) : size_t(0)) * sizeof(float);
-  if (((tok && heads) || d_b_qkv_s) && (!workspace || workspace_bytes < stats_bytes))
+  if (((tok && heads) || d_b_qkv_s) && (!workspace || workspace_bytes < domino_attn_block_bwd_workspace_size(d)))
     return fail(DOMINO_ERR_INVALID_ARG, "workspace smaller than domino_attn_block_bwd_workspace_size");
   if (workspace && !aligned16(workspace)) return fail(DOMINO_ERR_ALIGN, "workspace is not 16-byte aligned");
   Sched sc;

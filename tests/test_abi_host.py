@@ -204,3 +204,165 @@ def test_group_rejects_bad_pointers(lib):
                               0, FAKE, 4)
     ws = D.domino_resid_ln_bwd_workspace_size(group_desc(rows=4096, hidden=4096))
     assert ws == 3 * 512 * 4096 * 4
+
+
+def layer_desc(**kw):
+    base = dict(batch=2, seq=64, hidden=256, heads=2, head_dim=128, ffn_shard=128, act=0, eps=1e-5, p_drop=0.1,
+                scale=0.0, row_chunks=2, n_partials=1, layers=1, reserved=0)
+    base.update(kw)
+    return L.LayerDesc(**base)
+
+
+def layer_ptrs(layers=1, n_partials=1, **over):
+    """Every field of the per-layer parameter, activation and gradient structs set to a valid
+    (never dereferenced) address; `over` replaces fields as "params.name" / "acts.name" /
+    "grads.name" = value for layer 0, or "L<l>.<struct>.name" for layer l."""
+    peers = [FAKE] * (n_partials - 1)
+    out = []
+    for l in range(layers):
+        p = {n: FAKE for n, _ in L.LayerParams._fields_}
+        a = {n: FAKE for n, _ in L.LayerActs._fields_}
+        g = {n: FAKE for n, _ in L.LayerGrads._fields_}
+        for s in (a, g):
+            for n, t in L.LayerActs._fields_ + L.LayerGrads._fields_:
+                if n in s and t is not L._VP:
+                    s[n] = list(peers)
+        out.append({"params": p, "acts": a, "grads": g})
+    for key, v in over.items():
+        parts = key.split(".")
+        l = int(parts[0][1:]) if parts[0].startswith("L") else 0
+        struct, name = parts[-2], parts[-1]
+        out[l][struct][name] = v
+    return ([o["params"] for o in out], [o["acts"] for o in out], [o["grads"] for o in out])
+
+
+def test_layer_desc_layout():
+    assert ctypes.sizeof(L.LayerDesc) == 80 and L.LayerDesc.reserved.offset == 76
+    assert ctypes.sizeof(L.LayerParams) == 14 * 8 and ctypes.sizeof(L.LayerActs) == 19 * 8
+    assert ctypes.sizeof(L.LayerGrads) == 25 * 8
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(head_dim=64), "UNSUPPORTED: head_dim must be 128"),
+    (dict(batch=3), "SHAPE: batch % row_chunks"),
+    (dict(row_chunks=0), "SHAPE: bad row_chunks"),
+    (dict(n_partials=0), "INVALID_ARG: bad n_partials"),
+    (dict(n_partials=17), "INVALID_ARG: bad n_partials"),
+    (dict(layers=0), "INVALID_ARG: layers must be >= 1"),
+    (dict(hidden=260), "ALIGN: hidden and ffn_shard"),
+    (dict(ffn_shard=100), "ALIGN: hidden and ffn_shard"),
+    (dict(hidden=8200), "UNSUPPORTED: hidden above 8192"),
+    (dict(act=7), "INVALID_ARG: bad act"),
+    (dict(p_drop=1.0), "INVALID_ARG: p_drop"),
+    (dict(eps=0.0), "INVALID_ARG: eps"),
+    (dict(reserved=1), "INVALID_ARG: reserved must be 0"),
+    (dict(seq=-1), "SHAPE: negative size"),
+    (dict(heads=0), "UNSUPPORTED: a layer needs heads > 0"),
+    (dict(ffn_shard=0), "UNSUPPORTED: a layer needs heads > 0"),
+])
+def test_stack_rejects_bad_desc(lib, kw, msg):
+    prm, act, grd = layer_ptrs()
+    with pytest.raises(D.DominoError, match=msg):
+        D.domino_stack_fwd(layer_desc(**kw), FAKE, prm, act, FAKE)
+    with pytest.raises(D.DominoError, match=msg):
+        D.domino_stack_bwd(layer_desc(**kw), FAKE, prm, act, grd, FAKE, FAKE, 0, FAKE, 1 << 40)
+    if not msg.startswith("UNSUPPORTED: a layer"):
+        assert D.domino_stack_bwd_workspace_size(layer_desc(**kw)) == 0
+
+
+@pytest.mark.parametrize("over,msg", [
+    ({"params.A_qkv_s": None}, "INVALID_ARG: layer 0: A_qkv_s is NULL"),
+    ({"params.B_s": FAKE + 2}, "ALIGN: layer 0: B_s is not 16-byte aligned"),
+    ({"params.ln1_beta": FAKE + 8}, "ALIGN: layer 0: ln1_beta"),
+    ({"params.keep_attn": FAKE + 2}, "ALIGN: keep is not 4-byte aligned"),
+    ({"acts.ln2": None}, "INVALID_ARG: layer 0: ln2 is NULL"),
+    ({"acts.y_mlp": None}, "INVALID_ARG: layer 0: y_mlp is NULL"),
+    ({"L1.acts.x_in": None}, "INVALID_ARG: layer 1: x_in is NULL"),
+    ({"L1.params.A_s": None}, "INVALID_ARG: layer 1: A_s is NULL"),
+    ({"acts.peer_y_attn": [FAKE, None]}, r"INVALID_ARG: layer 0: peer_y_attn\[1\] is NULL"),
+    ({"L1.acts.peer_y_mlp": [FAKE + 4, FAKE]}, r"ALIGN: layer 1: peer_y_mlp\[0\]"),
+])
+def test_stack_fwd_rejects_bad_pointers(lib, over, msg):
+    prm, act, _ = layer_ptrs(layers=2, n_partials=3, **over)
+    with pytest.raises(D.DominoError, match=msg):
+        D.domino_stack_fwd(layer_desc(layers=2, n_partials=3), FAKE, prm, act, FAKE)
+
+
+def test_stack_fwd_rejects_missing_input_and_output(lib):
+    prm, act, _ = layer_ptrs()
+    with pytest.raises(D.DominoError, match="INVALID_ARG: X is NULL"):
+        D.domino_stack_fwd(layer_desc(), None, prm, act, FAKE)
+    with pytest.raises(D.DominoError, match="INVALID_ARG: out is NULL"):
+        D.domino_stack_fwd(layer_desc(), FAKE, prm, act, None)
+    with pytest.raises(D.DominoError, match="ALIGN: workspace"):
+        D.domino_stack_fwd(layer_desc(), FAKE, prm, act, FAKE, FAKE + 4, 1 << 20)
+    # Zero tokens: nothing to do and no pointer is read.
+    D.domino_stack_fwd(layer_desc(batch=0), None, [{}], [{}], None)
+
+
+@pytest.mark.parametrize("over,msg", [
+    ({"grads.dA_s": None}, "INVALID_ARG: layer 0: dA_s is NULL"),
+    ({"grads.d_b_o": FAKE + 2}, "ALIGN: layer 0: d_b_o"),
+    ({"acts.lse": None}, "INVALID_ARG: layer 0: lse is NULL"),
+    ({"L1.grads.d_x_in": None}, "INVALID_ARG: layer 1: d_x_in is NULL"),
+    ({"grads.peer_dx_attn": [None, FAKE]}, r"INVALID_ARG: layer 0: peer_dx_attn\[0\] is NULL"),
+    ({"L1.grads.peer_dx_mlp": [FAKE, FAKE + 2]}, r"ALIGN: layer 1: peer_dx_mlp\[1\]"),
+])
+def test_stack_bwd_rejects_bad_pointers(lib, over, msg):
+    d = layer_desc(layers=2, n_partials=3)
+    prm, act, grd = layer_ptrs(layers=2, n_partials=3, **over)
+    with pytest.raises(D.DominoError, match=msg):
+        D.domino_stack_bwd(d, FAKE, prm, act, grd, FAKE, FAKE, 0, FAKE, 1 << 40)
+
+
+def test_stack_bwd_workspace_checks(lib):
+    d = layer_desc(layers=2, n_partials=3)
+    prm, act, grd = layer_ptrs(layers=2, n_partials=3)
+    ws = D.domino_stack_bwd_workspace_size(d)
+    assert ws > 0 and ws % 16 == 0
+    with pytest.raises(D.DominoError, match="workspace smaller than domino_stack_bwd_workspace_size"):
+        D.domino_stack_bwd(d, FAKE, prm, act, grd, FAKE, FAKE, 0, FAKE, ws - 16)
+    with pytest.raises(D.DominoError, match="workspace smaller"):
+        D.domino_stack_bwd(d, FAKE, prm, act, grd, FAKE, FAKE, 0, None, ws)
+    with pytest.raises(D.DominoError, match="ALIGN: workspace"):
+        D.domino_stack_bwd(d, FAKE, prm, act, grd, FAKE, FAKE, 0, FAKE + 8, ws)
+    with pytest.raises(D.DominoError, match="INVALID_ARG: dX is NULL"):
+        D.domino_stack_bwd(d, FAKE, prm, act, grd, FAKE, None, 0, FAKE, ws)
+
+
+def test_attn_bwd_rejects(lib):
+    def ad(**kw):
+        base = dict(batch=2, seq=16, hidden=64, heads=2, head_dim=128, scale=0.0, dtype=1, row_chunks=1,
+                    n_partials=1, no_join=0)
+        base.update(kw)
+        return L.AttnDesc(**base)
+
+    args = [FAKE] * 10 + [None] + [FAKE] * 3  # X .. dX_own, peer_dX, dX, dA_qkv_s, dB_o_s
+
+    def call(desc, *, ws=FAKE, ws_bytes=1 << 30, **over):
+        a = list(args)
+        names = ["X", "A_qkv_s", "B_o_s", "QKV", "O", "lse", "dY", "dO", "dQKV", "dX_own", "peer_dX", "dX",
+                 "dA_qkv_s", "dB_o_s"]
+        d_b = over.pop("d_b_qkv_s", None)
+        for k, v in over.items():
+            a[names.index(k)] = v
+        D.domino_attn_block_bwd(desc, *a, accumulate=0, workspace=ws, workspace_bytes=ws_bytes, d_b_qkv_s=d_b)
+
+    for kw, pat in [(dict(head_dim=64), "UNSUPPORTED"), (dict(dtype=0), "UNSUPPORTED"),
+                    (dict(batch=3, row_chunks=2), "SHAPE"), (dict(hidden=60), "ALIGN")]:
+        with pytest.raises(D.DominoError, match=pat):
+            call(ad(**kw))
+    with pytest.raises(D.DominoError, match="INVALID_ARG: lse is NULL"):
+        call(ad(), lse=None)
+    with pytest.raises(D.DominoError, match="ALIGN: dO"):
+        call(ad(), dO=FAKE + 2)
+    with pytest.raises(D.DominoError, match=r"INVALID_ARG: peer_dX\[1\] is NULL"):
+        call(ad(n_partials=3), peer_dX=[FAKE, None])
+    with pytest.raises(D.DominoError, match="ALIGN: d_b_qkv_s"):
+        call(ad(), d_b_qkv_s=FAKE + 4)
+    ws = D.domino_attn_block_bwd_workspace_size(ad())
+    assert ws > 0
+    with pytest.raises(D.DominoError, match="workspace smaller than domino_attn_block_bwd_workspace_size"):
+        call(ad(), ws_bytes=ws - 4)
+    with pytest.raises(D.DominoError, match="ALIGN: workspace"):
+        call(ad(), ws=FAKE + 4, ws_bytes=ws)
