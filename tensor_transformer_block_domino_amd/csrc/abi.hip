@@ -97,6 +97,15 @@ int64_t g_timing_n[DOMINO_K_COUNT];
 std::string g_timing_kernel[DOMINO_K_COUNT];
 thread_local std::string t_kernel;  // the kernel the calling thread's launcher last noted
 
+}  // namespace
+
+LaunchEvents& domino::launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+
+namespace {
+
 hipEvent_t timing_event() {
   if (!g_timing_free.empty()) {
     hipEvent_t e = g_timing_free.back();
@@ -124,9 +133,17 @@ hipError_t timed(int kind, hipStream_t s, F&& f) {
   }
   if (!a || !b) return hipErrorOutOfMemory;
   t_kernel.clear();
-  hipError_t e = hipEventRecord(a, s);
-  if (e == hipSuccess) e = f();
-  if (e == hipSuccess) e = hipEventRecord(b, s);
+  // The launches inside f record a at the first kernel's start and b at the last one's end.
+  LaunchEvents& ev = launch_events();
+  ev.start = a;
+  ev.stop = b;
+  hipError_t e = f();
+  const bool launched = ev.start == nullptr;
+  ev.start = ev.stop = nullptr;
+  if (e == hipSuccess && !launched) {  // nothing launched: an empty interval
+    e = hipEventRecord(a, s);
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+  }
   if (e == hipSuccess) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_recs.push_back({kind, a, b, t_kernel});

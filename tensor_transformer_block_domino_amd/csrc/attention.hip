@@ -273,7 +273,7 @@ hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   const int blocks = p.nqb * p.heads * p.batch;
   note_kernel("attn_fwd_kernel");
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(blocks), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(attn_fwd_kernel, dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -514,7 +514,7 @@ hipError_t launch_attention_bwd_prep(const AttnBwdArgs& a, hipStream_t s) {
   if (a.batch == 0 || a.seq == 0 || a.heads == 0) return hipSuccess;
   const BwdParams p = bwd_params(a);
   note_kernel("attn_bwd_prep_kernel");
-  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((p.T * p.heads + 15) / 16)), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(attn_bwd_prep_kernel, dim3(unsigned((p.T * p.heads + 15) / 16)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -523,7 +523,7 @@ hipError_t launch_attention_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s) {
   const BwdParams p = bwd_params(a);
   const int nkb = int((a.seq + kWG - 1) / kWG);
   note_kernel("attn_bwd_dkdv_kernel");
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(attn_bwd_dkdv_kernel, dim3(nkb * p.heads * p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -532,7 +532,7 @@ hipError_t launch_attention_bwd_dq(const AttnBwdArgs& a, hipStream_t s) {
   const BwdParams p = bwd_params(a);
   const int nqb = int((a.seq + kWG - 1) / kWG);
   note_kernel("attn_bwd_dq_kernel");
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(nqb * p.heads * p.batch), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(attn_bwd_dq_kernel, dim3(nqb * p.heads * p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

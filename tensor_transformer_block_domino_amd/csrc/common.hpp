@@ -1,6 +1,7 @@
 // Device-side helpers shared by the HIP kernels of the Domino shard library (gfx950).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -156,3 +157,16 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 }  // namespace domino
+
+// Every kernel launch of the library: a plain launch, or while a call is timed the extended
+// launch that records that call's events with the kernel's own start and end.
+#define DOMINO_LAUNCH(kernel, grid, block, lds, stream, ...)                                        \
+  do {                                                                                              \
+    ::domino::LaunchEvents& ev_ = ::domino::launch_events();                                        \
+    if (ev_.stop) {                                                                                 \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev_.start, ev_.stop, 0, __VA_ARGS__); \
+      ev_.start = nullptr;                                                                          \
+    } else {                                                                                        \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                            \
+    }                                                                                               \
+  } while (0)

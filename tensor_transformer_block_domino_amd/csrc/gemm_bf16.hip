@@ -343,7 +343,12 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
   struct Frag {
     u32x4_t a[TM], b[TN];
   };
-  Frag f0, f1;
+  // Fragments are read kAhead sub-steps before their MFMAs: two with one workgroup per CU
+  // (its four waves are the only ones to hide the LDS latency), else one. NF fragment sets
+  // rotate with the sub-step.
+  constexpr int kAhead = kOcc == 1 && NS >= 3 && NSUB % 4 == 0 ? 2 : 1;
+  constexpr int NF = kAhead == 2 ? 4 : 2;
+  Frag f[NF];
   // Fragment reads are inline assembly, so their order against the MFMAs is the order
   // written here and the compiler adds no waits of its own: through the builtins, each
   // transposed read would wait for every global→LDS copy in flight (the compiler cannot
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
     for (int q = 0; q < NQ; ++q) {
       const int i = q / TN, j = q % TN;
       const int before = q == 0 ? 0 : issued_after(q - 1);
-      lgkm_wait_tied(min(15, kReads - 1 - need(i, j) + before), cur.a[i], cur.b[j]);
+      lgkm_wait_tied(min(15, kReads - 1 - need(i, j) + (kAhead - 1) * kReads + before), cur.a[i], cur.b[j]);
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.b[j]),
                                                          __builtin_bit_cast(bf16x8_t, cur.a[i]), acc[i][j], 0, 0, 0);
 #pragma unroll
@@ -465,34 +470,42 @@ __global__ __launch_bounds__(kThreads, kOcc) void gemm_bf16_kernel(KParams p) {
     for (int st = 0; st < NS; ++st) issue(kt_begin + st, st);
     wait_vm_barrier<(NS - 1) * kLPS>();
 #pragma unroll
-    for (int r = 0; r < kReads; ++r) read_op(f0, 0, 0, r);
+    for (int r = 0; r < kReads; ++r) read_op(f[0], 0, 0, r);
+    if constexpr (kAhead == 2) {
+#pragma unroll
+      for (int r = 0; r < kReads; ++r) read_op(f[1], 0, 1, r);
+    }
     int slot = 0;
     for (int kt = kt_begin; kt < kt_end; ++kt) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        Frag& cur = (s & 1) ? f1 : f0;
-        Frag& nxt = (s & 1) ? f0 : f1;
-        if (s + 1 < NSUB) {
-          step(cur, nxt, slot, s + 1, s + 1, kSpreadCopies && kt > kt_begin);
+        Frag& cur = f[s % NF];
+        Frag& nxt = f[(s + kAhead) % NF];
+        constexpr int sb = NSUB - kAhead;  // the sub-step that starts with the stage barrier
+        if (s < sb) {
+          step(cur, nxt, slot, s + kAhead, s + kAhead, kSpreadCopies && kt > kt_begin);
         } else {
-          // Every wave has read all of this stage (its last fragments are in registers):
-          // wait for the next stage, start refilling this slot NS stages ahead, and read the
-          // next stage's first fragments during this sub-step.
-          wait_vm_barrier<(NS - 2) * kLPS>();
-          if constexpr (kSpreadCopies) {
-            dkt = __builtin_amdgcn_readfirstlane(kt + NS);
-            dslot = __builtin_amdgcn_readfirstlane(slot);
-          } else {
-            issue(kt + NS, slot);
+          if (s == sb) {
+            // Every wave has issued all reads of this stage (the barrier waits for them):
+            // wait for the next stage, start refilling this slot NS stages ahead, and read
+            // the next stage's first fragments from this sub-step on.
+            wait_vm_barrier<(NS - 2) * kLPS>();
+            if constexpr (kSpreadCopies) {
+              dkt = __builtin_amdgcn_readfirstlane(kt + NS);
+              dslot = __builtin_amdgcn_readfirstlane(slot);
+            } else {
+              issue(kt + NS, slot);
+            }
+            slot = slot + 1 == NS ? 0 : slot + 1;
           }
-          slot = slot + 1 == NS ? 0 : slot + 1;
-          step(cur, nxt, slot, 0, 0, kSpreadCopies);
+          step(cur, nxt, slot, s + kAhead - NSUB, s - sb, kSpreadCopies);
         }
       }
     }
     // The reads of the sub-step after the last are never used; they must land before their
     // registers are reused, and no LDS write may land after the workgroup ends.
-    wait_frags(f0);
+#pragma unroll
+    for (int q = 0; q < NF; ++q) wait_frags(f[q]);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
@@ -613,7 +626,7 @@ constexpr TileCfg kTiles[] = {
 
 template <int BM, int BN, int BK, int NS, int kOcc, bool kAK, bool kBKc, Epi kEpi>
 void launch_tile(const KParams& kp, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, kOcc, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
+  DOMINO_LAUNCH((gemm_bf16_kernel<BM, BN, BK, NS, kOcc, kAK, kBKc, kEpi>), dim3(blocks), dim3(kThreads), 0, s, kp);
 }
 
 // Each operand layout is built only with the tiles make_plan can choose for it.
@@ -668,7 +681,7 @@ template <int BM, int BN, Epi kEpi>
 void launch_fixup(const KParams& kp, int rest, hipStream_t s) {
   constexpr int kCols = kEpi == Epi::kSwiglu ? BN / 2 : BN;
   const int64_t items = int64_t(rest) * BM * (kCols / 4);
-  hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, kEpi>), dim3(unsigned((items + 255) / 256)), dim3(256), 0, s, kp);
+  DOMINO_LAUNCH((gemm_fixup_kernel<BM, BN, kEpi>), dim3(unsigned((items + 255) / 256)), dim3(256), 0, s, kp);
 }
 
 // k-split tiles occur for input gradients (tiles kT128, kT256) and weight gradients (any

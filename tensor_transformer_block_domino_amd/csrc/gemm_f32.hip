@@ -78,10 +78,10 @@ hipError_t gemm_f32(const float* A, int64_t lda, bool ak, const float* B, int64_
   F32Params p{A, lda, B, ldb, C, ldc, M, N, K, accumulate};
   dim3 grid(unsigned((N + kTile - 1) / kTile), unsigned((M + kTile - 1) / kTile));
   note_kernel("gemm_f32_kernel");
-  if (ak && bk) hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, dim3(256), 0, s, p);
-  else if (ak && !bk) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, dim3(256), 0, s, p);
-  else if (!ak && bk) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, dim3(256), 0, s, p);
+  if (ak && bk) DOMINO_LAUNCH((gemm_f32_kernel<true, true>), grid, dim3(256), 0, s, p);
+  else if (ak && !bk) DOMINO_LAUNCH((gemm_f32_kernel<true, false>), grid, dim3(256), 0, s, p);
+  else if (!ak && bk) DOMINO_LAUNCH((gemm_f32_kernel<false, true>), grid, dim3(256), 0, s, p);
+  else DOMINO_LAUNCH((gemm_f32_kernel<false, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -143,10 +143,10 @@ hipError_t launch_gemm_f32_path(const GemmArgs& g, hipStream_t s, int* launches)
       const int64_t f = sw ? g.f_s : g.N;
       note_kernel("gemm_f32_kernel + act_fwd_f32_kernel");
       if (sw)
-        hipLaunchKernelGGL((act_fwd_f32_kernel<true>), dim3(grid_for(g.M * f)), dim3(256), 0, s, C, g.ldc,
+        DOMINO_LAUNCH((act_fwd_f32_kernel<true>), dim3(grid_for(g.M * f)), dim3(256), 0, s, C, g.ldc,
                            static_cast<float*>(g.C2), g.ldc2, g.M, f);
       else
-        hipLaunchKernelGGL((act_fwd_f32_kernel<false>), dim3(grid_for(g.M * f)), dim3(256), 0, s, C, g.ldc,
+        DOMINO_LAUNCH((act_fwd_f32_kernel<false>), dim3(grid_for(g.M * f)), dim3(256), 0, s, C, g.ldc,
                            static_cast<float*>(g.C2), g.ldc2, g.M, f);
       *launches = 2;
       return hipGetLastError();
@@ -158,10 +158,10 @@ hipError_t launch_gemm_f32_path(const GemmArgs& g, hipStream_t s, int* launches)
       const float* hp = static_cast<const float*>(g.aux);
       note_kernel("gemm_f32_kernel + act_bwd_f32_kernel");
       if (g.epi == Epi::kDSwiglu)
-        hipLaunchKernelGGL((act_bwd_f32_kernel<true>), dim3(grid_for(g.M * g.N)), dim3(256), 0, s, hp, g.ldaux, C,
+        DOMINO_LAUNCH((act_bwd_f32_kernel<true>), dim3(grid_for(g.M * g.N)), dim3(256), 0, s, hp, g.ldaux, C,
                            g.ldc, g.M, g.N);
       else
-        hipLaunchKernelGGL((act_bwd_f32_kernel<false>), dim3(grid_for(g.M * g.N)), dim3(256), 0, s, hp, g.ldaux, C,
+        DOMINO_LAUNCH((act_bwd_f32_kernel<false>), dim3(grid_for(g.M * g.N)), dim3(256), 0, s, hp, g.ldaux, C,
                            g.ldc, g.M, g.N);
       *launches = 2;
       return hipGetLastError();
@@ -183,7 +183,7 @@ __global__ void fill_zero_f32_kernel(float* out, int64_t ld, int64_t rows, int64
 hipError_t launch_fill_zero_f32(float* out, int64_t ld, int64_t rows, int64_t cols, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   note_kernel("fill_zero_f32_kernel");
-  hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(grid_for(rows * cols)), dim3(256), 0, s, out, ld, rows, cols);
+  DOMINO_LAUNCH(fill_zero_f32_kernel, dim3(grid_for(rows * cols)), dim3(256), 0, s, out, ld, rows, cols);
   return hipGetLastError();
 }
 

@@ -331,12 +331,12 @@ constexpr int kBwdBlocks = 512;
 
 template <int CPL>
 hipError_t launch_fwd(const GroupFwdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(resid_ln_fwd_kernel<CPL>, dim3(unsigned((p.rows + 3) / 4)), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(resid_ln_fwd_kernel<CPL>, dim3(unsigned((p.rows + 3) / 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 template <int CPT>
 hipError_t launch_bwd(const GroupBwdParams& p, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL(resid_ln_bwd_kernel<CPT>, dim3(blocks), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(resid_ln_bwd_kernel<CPT>, dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -353,12 +353,12 @@ hipError_t launch_bias_grad(const void* x, int64_t rows, int64_t cols, int64_t l
     cp.part = ws;
     cp.out[0] = out;
     cp.h = int(cols);
-    hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
+    DOMINO_LAUNCH(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
     return hipGetLastError();
   }
   const unsigned rb = unsigned((rows + kBiasRows - 1) / kBiasRows);
   note_kernel("colpart_bf16_kernel");
-  hipLaunchKernelGGL(colpart_bf16_kernel, dim3(unsigned((cols / 8 + 255) / 256), rb), dim3(256), 0, s,
+  DOMINO_LAUNCH(colpart_bf16_kernel, dim3(unsigned((cols / 8 + 255) / 256), rb), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), rows, cols, ld, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -368,7 +368,7 @@ hipError_t launch_bias_grad(const void* x, int64_t rows, int64_t cols, int64_t l
   cp.nb = int(rb);
   cp.h = int(cols);
   cp.accumulate = accumulate;
-  hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
+  DOMINO_LAUNCH(colsum_kernel, dim3(unsigned((cols + 31) / 32), 1), dim3(256), 0, s, cp);
   return hipGetLastError();
 }
 
@@ -452,7 +452,7 @@ hipError_t launch_resid_ln_bwd(const GroupBwdArgs& a, hipStream_t s) {
   cp.h = int(a.hidden);
   cp.accumulate = a.accumulate;
   if (cp.out[0] || cp.out[1] || cp.out[2])
-    hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((a.hidden + 31) / 32), 3), dim3(256), 0, s, cp);
+    DOMINO_LAUNCH(colsum_kernel, dim3(unsigned((a.hidden + 31) / 32), 3), dim3(256), 0, s, cp);
   return hipGetLastError();
 }
 

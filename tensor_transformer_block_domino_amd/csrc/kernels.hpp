@@ -7,6 +7,15 @@
 
 namespace domino {
 
+// Events of a timed call. While the library's kernel timing is on, its timing wrapper hands
+// the launches of the call it times (on the calling thread) a start and a stop event, which
+// the dispatch itself records: the start at the first kernel's start, the stop at the end of
+// every kernel, so that it ends up at the last one's end. Null otherwise.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
 constexpr int kMaxPartials = 16;
 
 // Records the kernel (symbol and template arguments) a launcher is about to launch on the

@@ -92,7 +92,7 @@ static hipError_t launch_reduce_p(const ReduceArgs& a, hipStream_t s) {
   char name[64];
   snprintf(name, sizeof name, "shard_reduce_kernel<%s, %d>", sizeof(T) == 2 ? "bf16" : "f32", P);
   note_kernel(name);
-  hipLaunchKernelGGL((shard_reduce_kernel<T, P>), dim3(blocks), dim3(256), 0, s, a.out, a.ld_out, parts,
+  DOMINO_LAUNCH((shard_reduce_kernel<T, P>), dim3(blocks), dim3(256), 0, s, a.out, a.ld_out, parts,
                      a.ld_in, uint32_t(a.rows), groups_per_row, total);
   return hipGetLastError();
 }
