@@ -77,6 +77,8 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (valida
     (dict(act=7), L.STATUS_NAMES[1]),
     (dict(dtype=9), L.STATUS_NAMES[1]),
     (dict(batch=-1), L.STATUS_NAMES[2]),
+    (dict(batch=65, row_chunks=65), L.STATUS_NAMES[4]),                    # 65 chunks: above the 64 the scheduler holds
+    (dict(batch=16, row_chunks=16, hidden=640, col_chunks=5), L.STATUS_NAMES[4]),
 ])
 def test_block_fwd_rejects_bad_desc(lib, kw, status):
     with pytest.raises(D.DominoError) as ei:

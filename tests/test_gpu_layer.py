@@ -278,3 +278,13 @@ def test_stack_with_all_biases(act):
         check(f"d_b_1[{l}]", f64(G["d_b_1"]), ref_b1, BF16_TOL)
         check(f"d_b_o[{l}]", f64(G["d_b_o"]), gr["bo"], BF16_TOL)
         check(f"d_b_2[{l}]", f64(G["d_b_2"]), gr["b2"], BF16_TOL)
+
+
+def test_stack_many_mu_batches_most_partials():
+    """Sixteen μ-batches of one sequence each and the largest group (16 partials): every
+    μ-batch's events and reductions in both directions, forward and backward."""
+    w = small_workload("swiglu", row_chunks=16, P=16, layers=2, batch=16, seq=40)
+    print(f"layer stack mu-batches=16 P=16 T={w.tokens}", flush=True)
+    g, inp = run_backward(w)
+    check_stack(g, w, inp)
+    check_stack_backward(g, w, inp)

@@ -211,3 +211,20 @@ def test_mlp_block_with_bias(act):
     dHpre0 = oracle.act_backward(X @ A0 + b10, dY @ B0.T, act)
     check("dHpre", f64(g.dHpre[0]), dHpre0, BF16_TOL)
     check("d_b1_s", f64(dB1), dHpre0.sum(axis=0), BF16_TOL)
+
+
+@pytest.mark.parametrize("split,batch,seq", [((8, 8), 16, 24), ((64, 1), 64, 6)])
+def test_mlp_maximum_chunks_and_partials(split, batch, seq):
+    """The largest Domino splits the scheduler takes (64 chunks: 8 × 8, or 64 row chunks of one
+    sequence each) with the largest number of partials (16): every chunk's event, reduction
+    and output slice, forward and backward."""
+    act = "gelu_tanh" if split[1] > 1 else "swiglu"
+    w = small_workload(act, batch=batch, seq=seq, hidden=128, ffn_shard=48, P=16, split=split, seed=29)
+    print(f"mlp max chunks act={act} split={split} T={w.tokens} P=16", flush=True)
+    g, inp = run_fwd_bwd(w)
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    check("Y", f64(g.Y), oracle.domino_mlp_forward(X, A, B, act, 16, w.batch, w.seq, *split), BF16_TOL)
+    dX_ref, dA_ref, dB_ref = oracle.domino_mlp_backward(X, A, B, dY, act, 16, 0, w.batch, w.seq, *split)
+    check("dX", f64(g.dX), dX_ref, BF16_TOL)
+    check("dA_s", f64(g.dA), dA_ref, BF16_TOL)
+    check("dB_s", f64(g.dB), dB_ref, BF16_TOL)
