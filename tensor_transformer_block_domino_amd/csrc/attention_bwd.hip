@@ -18,9 +18,10 @@
 //  * dQ: one workgroup per (sequence, head, 128 queries), as in the forward: blocks of 64
 //    keys stream through LDS, S and dP come out with one query per lane, and
 //    dQᵀ += Kᵀ·dSᵀ reads K transposed.
-// Every LDS tile is [row][d] with the 16-byte chunk c of row r at c ^ (r & 15): row reads
-// (16 rows × one chunk) and transposed reads (4 rows × 32 bytes per 16 lanes) both spread
-// over the banks. LDS reads are inline assembly with explicit waits (through the builtins
+// Every LDS tile is [row][d] with the 16-byte chunk c of row r at c ^ sw(r), sw(r) the low
+// four bits of r with their two halves swapped: a row read (16 consecutive rows × one chunk)
+// and a transposed read (4 consecutive rows × 4 consecutive chunks per 32 lanes) both hit
+// every bank once. (With c ^ (r & 15) the transposed reads hit half the banks twice.) LDS reads are inline assembly with explicit waits (through the builtins
 // the compiler would make them wait for the global→LDS copies of the next block).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -33,7 +34,8 @@ constexpr int kWG = 128;   // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kBlk = 64;   // queries (dK/dV) or keys (dQ) per streamed block
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int t_off(int row, int chunk) { return row * kD + ((chunk ^ (row & 15)) << 3); }
+__device__ __forceinline__ int sw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int t_off(int row, int chunk) { return row * kD + ((chunk ^ sw(row)) << 3); }
 
 struct BwdParams {
   const uint16_t* qkv; int64_t ld_qkv;
@@ -52,7 +54,7 @@ __device__ __forceinline__ u32x4_t ld_frag(const uint16_t* g) { return *reinterp
 
 // Copy offsets (bytes) of a [64][128] tile in the swizzled layout: wave w fills 1 KB pieces
 // w, w+4, w+8, w+12; lane byte 16·(64·piece + lane) holds row (64·piece + lane)/16 and
-// logical chunk (lane & 15) ^ (row & 15).
+// logical chunk (lane & 15) ^ sw(row).
 struct TileCopy {
   int32_t off[4];
   int row[4];
@@ -61,7 +63,7 @@ struct TileCopy {
     for (int i = 0; i < 4; ++i) {
       const int pos = (w + 4 * i) * 64 + lane, r = pos >> 4, c16 = pos & 15;
       row[i] = r;
-      off[i] = int32_t((int64_t(r) * ld + ((c16 ^ (r & 15)) << 3)) * 2);
+      off[i] = int32_t((int64_t(r) * ld + ((c16 ^ sw(r)) << 3)) * 2);
     }
   }
   // Rows at or beyond `valid` load zeros.
