@@ -431,8 +431,8 @@ def timed_steps(fn, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported in this build "
-              f"(the reduction of tensor-parallel partials runs on one GPU)", file=sys.stderr)
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported: the library sums the "
+              f"tensor-parallel partials on one GPU, with no collective between GPUs", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -71,7 +71,7 @@ typedef enum {
   DOMINO_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, n_partials out of range */
   DOMINO_ERR_SHAPE = 2,        /* sizes inconsistent or not divisible as required */
   DOMINO_ERR_ALIGN = 3,        /* pointer not 16-byte aligned or width / ld not a multiple of 8 */
-  DOMINO_ERR_UNSUPPORTED = 4,  /* a valid combination this build does not implement */
+  DOMINO_ERR_UNSUPPORTED = 4,  /* a valid combination the library does not implement */
   DOMINO_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
 } domino_status;
 

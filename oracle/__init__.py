@@ -24,7 +24,7 @@ Sources (web pages, by title and section):
   then the small kernels Dropout, Residual, LayerNorm, then the MLP) and the
   DominoTransformerLayer excerpt under "μ-batch 流水" (pre-LayerNorm block).
 
-Readings where the pages are silent (each listed with its basis in the design doc):
+Readings where the pages are silent (the plainest reading the rest of the pages supports):
   GeLU is the tanh form; SwiGLU is silu(gate)*up with A's columns [gate | up];
   shards are contiguous equal column blocks of A and the matching row blocks of B
   (contiguous head blocks for attention); the row split is along batch with
@@ -32,7 +32,7 @@ Readings where the pages are silent (each listed with its basis in the design doc):
   no bias, dropout or rotary embedding; LayerNorm uses the biased variance and eps 1e-5
   inside the root; dropout is inverted dropout with a given keep mask.
 
-Every function below is pinned by tests/test_oracle_pins.py (brute-force scalar
+Every function below is pinned by tests/test_oracle_pins.py and tests/test_oracle_layer_pins.py (brute-force scalar
 loops, the split and shard-sum identities, finite differences, closed forms and
 library cross-checks); none is "parity unpinned".
 """
