@@ -15,9 +15,10 @@
 //  * K advances through a ring of NS LDS stages of BK k each. Stages are filled by
 //    buffer loads that write LDS directly (no staging registers), NS−1 stages ahead of
 //    the one being consumed; one barrier per stage.
-//  * Within a stage, k advances 16 at a time; the fragments of sub-step s+1 are read
-//    from LDS while sub-step s runs on the matrix cores, one read between consecutive
-//    MFMAs (MFMA issue blocks the wave, so the reads must not form a run).
+//  * Within a stage, k advances 16 at a time; the fragments of sub-step s+1 (s+2 with one
+//    workgroup per CU) are read from LDS while sub-step s runs on the matrix cores, one
+//    read between consecutive MFMAs (MFMA issue blocks the wave, so the reads must not
+//    form a run).
 //  * An operand contiguous along k is staged [row][k] with an XOR chunk swizzle, and
 //    each MFMA fragment (8 consecutive k of one row) is one 16-byte LDS read. An
 //    operand contiguous along m (or n) — the [in, out] weights of the forward and both
