@@ -403,11 +403,13 @@ const char* domino_status_string(domino_status status);
 const char* domino_last_error(void);
 
 /*
- * Kernel timing for measurement: while enabled, every kernel the library launches is
- * bracketed by a pair of hipEvents recorded on the stream it runs on. domino_timing_read
- * waits for those events and returns, for kernel class `kind`, the number of launches
- * and their summed duration in milliseconds since the last reset. Timing adds two event
- * records per launch; keep it off outside measurement.
+ * Kernel timing for measurement: while enabled, each timed launch (one kernel, or a kernel
+ * and its small companion such as a column sum) is dispatched with a pair of hipEvents
+ * that the dispatch itself records at the first kernel's start and the last kernel's end
+ * (hipExtLaunchKernel), on the stream it runs on. domino_timing_read waits for those events
+ * and returns, for kernel class `kind`, the number of launches and their summed duration
+ * in milliseconds since the last reset. Keep timing off outside measurement and graph
+ * capture.
  */
 typedef enum {
   DOMINO_K_REDUCE = 0,
