@@ -52,6 +52,11 @@
  *   Errors     Every argument is checked before anything is enqueued; on an error
  *              nothing runs and the status says why. A failed HIP launch returns
  *              DOMINO_ERR_HIP (work enqueued before it may have run).
+ *   Limits     (DOMINO_ERR_UNSUPPORTED beyond them; the kernels index with 32-bit
+ *              offsets) every leading dimension of a product operand — hidden, n1,
+ *              ffn_shard, 3·heads·head_dim — at most 2^22 elements; at most 2^31 tokens;
+ *              a reduced region (shard_reduce, or T × hidden of a block call) at most
+ *              2^32 − 2^21 groups of 8 bf16 (4 fp32) elements.
  *   Threads    Calls may come from any host thread; calls that share output buffers
  *              must be ordered by the caller.
  */

@@ -303,6 +303,8 @@ domino_status make_sched(hipStream_t compute, hipStream_t comm, Sched* s) {
   return DOMINO_OK;
 }
 
+int64_t mlp_n1(const domino_mlp_desc* d) { return d->act == DOMINO_ACT_SWIGLU ? 2 * d->ffn_shard : d->ffn_shard; }
+
 domino_status check_mlp_desc(const domino_mlp_desc* d) {
   if (!d) return fail(DOMINO_ERR_INVALID_ARG, "desc is NULL");
   if (d->act != DOMINO_ACT_GELU_TANH && d->act != DOMINO_ACT_SWIGLU) return fail(DOMINO_ERR_INVALID_ARG, "bad act");
@@ -319,8 +321,14 @@ domino_status check_mlp_desc(const domino_mlp_desc* d) {
     return fail(DOMINO_ERR_ALIGN, "hidden must be a multiple of col_chunks * (8 for bf16, 4 for fp32)");
   if (d->ffn_shard % al) return fail(DOMINO_ERR_ALIGN, "ffn_shard must be a multiple of 8 (bf16) or 4 (fp32)");
   const int64_t T = d->batch * d->seq;
-  if (T > (int64_t(1) << 31) || d->hidden > (int64_t(1) << 31) || d->ffn_shard > (int64_t(1) << 30))
-    return fail(DOMINO_ERR_UNSUPPORTED, "size beyond 32-bit tile indexing");
+  if (T > (int64_t(1) << 31)) return fail(DOMINO_ERR_UNSUPPORTED, "more than 2^31 tokens");
+  if (d->hidden > kMaxLd || mlp_n1(d) > kMaxLd)
+    return fail(DOMINO_ERR_UNSUPPORTED, "hidden and the first product's width (ffn_shard, 2*ffn_shard for SwiGLU) "
+                                        "must be at most 2^22 (32-bit operand offsets)");
+  if (T / 128 * (std::max(d->hidden, mlp_n1(d)) / 128 + 1) >= (int64_t(1) << 30))
+    return fail(DOMINO_ERR_UNSUPPORTED, "too many output tiles for one launch");
+  if (T * (d->hidden / al) > kReduceMaxGroups)
+    return fail(DOMINO_ERR_UNSUPPORTED, "tokens * hidden beyond the reduction's 32-bit range");
   return DOMINO_OK;
 }
 
@@ -340,6 +348,12 @@ domino_status check_attn_desc(const domino_attn_desc* d) {
   if (!(d->scale >= 0.0f)) return fail(DOMINO_ERR_INVALID_ARG, "scale must be >= 0 (0 selects 1/sqrt(head_dim))");
   const int64_t T = d->batch * d->seq;
   if (T > (int64_t(1) << 31) || d->seq > (int64_t(1) << 30)) return fail(DOMINO_ERR_UNSUPPORTED, "too many tokens");
+  if (d->hidden > kMaxLd || 3 * d->heads * d->head_dim > kMaxLd)
+    return fail(DOMINO_ERR_UNSUPPORTED, "hidden and 3*heads*head_dim must be at most 2^22 (32-bit operand offsets)");
+  if (T / 128 * (std::max(d->hidden, 3 * d->heads * d->head_dim) / 128 + 1) >= (int64_t(1) << 30))
+    return fail(DOMINO_ERR_UNSUPPORTED, "too many output tiles for one launch");
+  if (T * (d->hidden / 8) > kReduceMaxGroups)
+    return fail(DOMINO_ERR_UNSUPPORTED, "tokens * hidden beyond the reduction's 32-bit range");
   return DOMINO_OK;
 }
 
@@ -354,7 +368,6 @@ GemmArgs gemm_base(int64_t M, int64_t N, int64_t K, bool bf16) {
   g.bf16 = bf16;
   return g;
 }
-int64_t mlp_n1(const domino_mlp_desc* d) { return d->act == DOMINO_ACT_SWIGLU ? 2 * d->ffn_shard : d->ffn_shard; }
 const char* at(const void* p, int64_t elems, size_t es) { return p ? static_cast<const char*>(p) + elems * es : nullptr; }
 char* at(void* p, int64_t elems, size_t es) { return p ? static_cast<char*>(p) + elems * es : nullptr; }
 
@@ -563,7 +576,8 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
   if (cols % al || ld_in % al || ld_out % al)
     return fail(DOMINO_ERR_ALIGN, "cols and leading dimensions must be multiples of 8 (bf16) / 4 (fp32)");
   if (ld_in < cols || ld_out < cols) return fail(DOMINO_ERR_SHAPE, "leading dimension smaller than cols");
-  if (rows * (cols / al) > int64_t(0xffffffffu)) return fail(DOMINO_ERR_UNSUPPORTED, "region too large");
+  if (rows > kReduceMaxGroups || rows * (cols / al) > kReduceMaxGroups)
+    return fail(DOMINO_ERR_UNSUPPORTED, "region too large: rows * cols / (8 bf16, 4 fp32) must be at most 2^32 - 2^21");
   domino_status st = check_ptr(out, "out", true);
   if (st != DOMINO_OK) return st;
   for (int p = 0; p < n_partials; ++p) {

@@ -18,6 +18,19 @@ LaunchEvents& launch_events();
 
 constexpr int kMaxPartials = 16;
 
+// Size limits of the kernels' 32-bit index arithmetic, which the C ABI checks.
+//  * GEMM operands are copied by buffer loads whose per-lane byte offset from the tile's
+//    first row is an int32: row·ld·2 + k-chunk with row < 256, so every leading dimension
+//    of a product operand must stay at or below 2^22 elements (255·2^22·2 + 112 < 2^31).
+//    The attention kernels' copy offsets (64 rows of the QKV leading dimension) fit
+//    within the same bound.
+//  * shard_reduce walks its 16-byte groups with a uint32 grid stride (at most 2048
+//    workgroups × 256 threads, two groups per thread per pass), so a region may hold at
+//    most 2^32 − 2^21 groups: the index then never wraps past the end.
+constexpr int64_t kMaxLd = int64_t(1) << 22;
+constexpr int64_t kReduceMaxGroups = (int64_t(1) << 32) - (int64_t(1) << 21);
+constexpr int kReduceMaxBlocks = 2048;
+
 // Records the kernel (symbol and template arguments) a launcher is about to launch on the
 // calling thread; the timing facility attaches it to the launch it brackets.
 void note_kernel(const char* name);

@@ -88,7 +88,8 @@ static hipError_t launch_reduce_p(const ReduceArgs& a, hipStream_t s) {
   const uint32_t total = uint32_t(a.rows) * groups_per_row;
   // Enough waves to cover HBM latency: up to 8 workgroups of 256 threads per CU.
   const uint32_t want = (total + 2 * 256 - 1) / (2 * 256);
-  const uint32_t blocks = want < 256u * 8u ? (want ? want : 1u) : 256u * 8u;
+  static_assert(int64_t(kReduceMaxBlocks) * 256 * 2 <= (int64_t(1) << 21), "grid stride within the group limit");
+  const uint32_t blocks = want < uint32_t(kReduceMaxBlocks) ? (want ? want : 1u) : uint32_t(kReduceMaxBlocks);
   char name[64];
   snprintf(name, sizeof name, "shard_reduce_kernel<%s, %d>", sizeof(T) == 2 ? "bf16" : "f32", P);
   note_kernel(name);

@@ -131,6 +131,55 @@ def test_shard_reduce_rejects(lib):
         D.shard_reduce(FAKE, 8, [FAKE], 8, 4, 8, 5)
 
 
+# Sizes just past the kernels' 32-bit index arithmetic (operand byte offsets of 256-row
+# tiles, the reduction's uint32 grid stride) are rejected before anything is enqueued; the
+# largest accepted sizes pass validation (the calls then fail only on the NULL pointer
+# planted to stop them before any launch).
+@pytest.mark.parametrize("kw,ok", [
+    (dict(hidden=1 << 22, ffn_shard=8, batch=1, seq=8), True),
+    (dict(hidden=(1 << 22) + 8, ffn_shard=8, batch=1, seq=8), False),
+    (dict(hidden=64, ffn_shard=1 << 22, act=0, batch=1, seq=8), True),
+    (dict(hidden=64, ffn_shard=1 << 21, act=1, batch=1, seq=8), True),
+    (dict(hidden=64, ffn_shard=(1 << 21) + 8, act=1, batch=1, seq=8), False),
+    (dict(hidden=8192, ffn_shard=8, batch=1, seq=(1 << 22) - 2048), True),  # T·h/8 = 2^32 − 2^21
+    (dict(hidden=8192, ffn_shard=8, batch=1, seq=1 << 22), False),          # T·h/8 = 2^32
+])
+def test_block_size_limits(lib, kw, ok):
+    if ok:
+        with pytest.raises(D.DominoError, match="X is NULL"):
+            D.domino_block_fwd(mlp_desc(**kw), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    else:
+        with pytest.raises(D.DominoError, match="UNSUPPORTED"):
+            D.domino_block_fwd(mlp_desc(**kw), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
+def test_shard_reduce_size_limit(lib):
+    limit = (1 << 32) - (1 << 21)       # 16-byte groups the reduction's uint32 stride can walk
+    with pytest.raises(D.DominoError, match="partials\\[0\\] is NULL"):   # at the limit: accepted
+        D.shard_reduce(FAKE, 8, [None], 8, limit, 8, 1)
+    with pytest.raises(D.DominoError, match="region too large"):
+        D.shard_reduce(FAKE, 8, [None], 8, limit + 1, 8, 1)
+    with pytest.raises(D.DominoError, match="region too large"):
+        D.shard_reduce(FAKE, 16, [None], 16, limit // 2 + 1, 16, 1)
+    with pytest.raises(D.DominoError, match="region too large"):     # fp32: 4 elements per group
+        D.shard_reduce(FAKE, 8, [None], 8, limit // 2 + 1, 8, 0)
+
+
+def test_attn_size_limits(lib):
+    def ad(**kw):
+        base = dict(batch=1, seq=16, hidden=64, heads=2, head_dim=128, scale=0.0, dtype=1, row_chunks=1,
+                    n_partials=1, no_join=0)
+        base.update(kw)
+        return L.AttnDesc(**base)
+
+    with pytest.raises(D.DominoError, match="X is NULL"):
+        D.domino_attn_block_fwd(ad(heads=(1 << 22) // 384), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    with pytest.raises(D.DominoError, match="UNSUPPORTED"):
+        D.domino_attn_block_fwd(ad(heads=(1 << 22) // 384 + 1), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    with pytest.raises(D.DominoError, match="UNSUPPORTED"):
+        D.domino_attn_block_fwd(ad(hidden=(1 << 22) + 8), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
 def test_attn_rejects(lib):
     def ad(**kw):
         base = dict(batch=2, seq=16, hidden=64, heads=2, head_dim=128, scale=0.0, dtype=1, row_chunks=1,

@@ -34,11 +34,17 @@ def test_attention_small(batch, seq, row_chunks):
     check("QKV", f64(g.QKV[0]), QKV_ref, BF16_TOL)
     check("O", f64(g.O[0]), O_ref, BF16_TOL)
     check("Y_own", f64(g.Y_own[0]), Y0_ref, BF16_TOL)
-    # The per-row log-sum-exp the backward uses (fp32 output; absolute error, as it is a log).
-    lse_ref = oracle.attn_lse(QKV_ref, batch, seq, hs, 128)
+    # The per-row log-sum-exp the backward uses (fp32 output; absolute error, as it is a
+    # log), against the oracle evaluated on the GPU's own bf16 QKV, so bf16 rounding of Q
+    # and K is out of the comparison and only fp32 arithmetic remains: scores are 128-term
+    # fp32 dot products of bf16 values, |scale·q·k| here at most ~10, so the rounding of
+    # one score is below 128·2⁻²⁴·10 ≈ 8e-5, and exp2/log2 add about one ulp each. 1e-3
+    # bounds that with a wide margin (the earlier bar, against the unrounded QKV, had to
+    # absorb the bf16 rounding of Q and K: 0.05).
+    lse_ref = oracle.attn_lse(f64(g.QKV[0]), batch, seq, hs, 128)
     err = float(np.max(np.abs(f64(g.lse[0]) - lse_ref)))
-    print(f"  lse: max abs err {err:.3e}", flush=True)
-    assert err < 0.05, err
+    print(f"  lse: max abs err {err:.3e} (against the GPU's bf16 QKV)", flush=True)
+    assert err < 1e-3, err
 
 
 def test_attention_first_row_is_v0_and_chunks_bitwise():

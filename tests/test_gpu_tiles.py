@@ -1,5 +1,5 @@
 """Products that run the 256×160 tile (four waves stacked along M, one workgroup per CU),
-against the fp64 oracle on every output element. Two shapes make it the tile of different
+against the fp64 oracle, whole-tensor and row by row (normwise). Two shapes make it the tile of different
 products: a wide FFN shard (forward GEMM1 and the activation-gradient product dY·B_sᵀ)
 and a wide hidden size (GEMM2 per row chunk and dHpre·A_sᵀ). Both leave ragged tiles in
 m (2000 rows), n (3904 columns: 24 tiles of 160 and one of 64) and k (200, or 400 for

@@ -428,6 +428,40 @@ def test_attention_lse():
     assert np.max(np.abs(O - oattn.causal_attention(Q, K, V, scale))) < 1e-13
 
 
+def test_multi_head_lse_matches_logsumexp_and_sdpa():
+    """attn_lse over a multi-head QKV: per (sequence, head), against scipy's logsumexp of
+    the scores of the Q and K heads that torch's own head reshape picks out, and the
+    softmax it implies against torch's causal scaled-dot-product attention (so the Q and
+    K column blocks and every head offset are pinned by a route other than the oracle's
+    slicing)."""
+    from scipy.special import logsumexp
+    batch, seq, heads, d = 3, 6, 3, 4
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(77)
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    # Distinct scales per block so a block mix-up moves the scores a lot.
+    QKV[:, heads * d:2 * heads * d] *= 2.0
+    QKV[:, 2 * heads * d:] *= 0.3
+    L = oattn.attn_lse(QKV, batch, seq, heads, d)
+    assert L.shape == (batch * seq, heads)
+    q, k, v = (torch.from_numpy(QKV).view(batch, seq, 3, heads, d)[:, :, i].transpose(1, 2) for i in range(3))
+    q, k, v = q.numpy(), k.numpy(), v.numpy()  # [batch, heads, seq, d]
+    for b in range(batch):
+        for j in range(heads):
+            ref = np.array([logsumexp(scale * (k[b, j, : i + 1] @ q[b, j, i])) for i in range(seq)])
+            assert np.max(np.abs(L[b * seq:(b + 1) * seq, j] - ref)) < 1e-12, (b, j)
+    # exp(S − LSE) is the attention row: over the visible keys it sums to one and, applied
+    # to V, gives torch's causal attention output.
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
+    O = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy()
+    for b in range(batch):
+        for j in range(heads):
+            S = scale * (q[b, j] @ k[b, j].T)
+            Pm = np.where(np.tril(np.ones((seq, seq), dtype=bool)), np.exp(S - L[b * seq:(b + 1) * seq, j][:, None]), 0)
+            assert np.max(np.abs(Pm.sum(axis=1) - 1.0)) < 1e-12
+            assert np.max(np.abs(Pm @ v[b, j] - O[b, j])) < 1e-12
+
+
 @pytest.mark.parametrize("row_chunks", [1, 2, 4])
 def test_domino_attn_backward_chunks_equal_unsplit(row_chunks):
     batch, seq, heads, d, h, P = 4, 5, 4, 3, 7, 2
@@ -460,6 +494,7 @@ def _pins():
         lambda: test_attention_backward_matches_torch_autograd(),
         lambda: test_attention_backward_closed_forms(),
         lambda: test_attention_lse(),
+        lambda: test_multi_head_lse_matches_logsumexp_and_sdpa(),
     ]
 
 
@@ -537,4 +572,36 @@ def _mut_attn_bwd(Q, K, V, dO, scale, row_term=True, transpose_dk=True, use_scal
 @pytest.mark.parametrize("name", sorted(ATTN_BWD_MUTATIONS))
 def test_planted_attention_backward_mistakes_are_caught(name, monkeypatch):
     monkeypatch.setattr(oattn, "causal_attention_backward", ATTN_BWD_MUTATIONS[name])
+    assert _any_pin_fails(), name
+
+
+def _mut_attn_lse(QKV, batch, seq, heads, head_dim, scale=None, k_block=1, head_shift=0):
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
+    Hd = heads * head_dim
+    L = np.zeros((batch * seq, heads))
+    for b in range(batch):
+        r = slice(b * seq, (b + 1) * seq)
+        for j in range(heads):
+            jq = j
+            jk = (j + head_shift) % heads
+            Q = QKV[r, jq * head_dim:(jq + 1) * head_dim]
+            K = QKV[r, k_block * Hd + jk * head_dim:k_block * Hd + (jk + 1) * head_dim]
+            L[r, j] = oattn.causal_attention_lse(Q, K, scale)
+    return L
+
+
+LSE_MUTATIONS = {
+    # K read from the V block
+    "k_from_v_block": lambda *a, **kw: _mut_attn_lse(*a, k_block=2, **kw),
+    # K of the neighbouring head (head offset off by one)
+    "head_offset_off_by_one": lambda *a, **kw: _mut_attn_lse(*a, head_shift=1, **kw),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LSE_MUTATIONS))
+def test_planted_lse_mistakes_are_caught(name, monkeypatch):
+    # The unmutated copy passes the pin; each mutation must fail it.
+    monkeypatch.setattr(oattn, "attn_lse", lambda *a, **kw: _mut_attn_lse(*a, **kw))
+    assert not _any_pin_fails()
+    monkeypatch.setattr(oattn, "attn_lse", LSE_MUTATIONS[name])
     assert _any_pin_fails(), name
