@@ -1,16 +1,30 @@
-"""Throughput of one tensor-parallel rank's Domino MLP block (forward + backward) on one MI355X.
+"""Throughput of one tensor-parallel rank's Domino block on one MI355X.
 
-A step is one pass of the whole hot path over one batch of the workload: the forward
-(GEMM1 with the activation epilogue, GEMM2 per chunk, each chunk's reduction of the 8
-shard partials on a second stream) and the backward (activation-gradient GEMM and
-input-gradient GEMM per chunk, each chunk's reduction of dX, then the two weight-gradient
-GEMMs). Peer ranks' partials are produced once before timing (they are other GPUs' work
-in a real tensor-parallel group). Inputs are resident in HBM when timing starts.
+Default line: the Llama-2-13B-shaped SwiGLU MLP shard at TP 8 with the 2D split (rows ×2,
+columns ×2), forward + backward — the largest workload that fits one GPU. A step is one
+pass of the whole hot path over one batch: GEMM1 with the SwiGLU epilogue once over all
+rows; GEMM2 per 2D chunk (r0c0, r0c1, r1c0, r1c1), each chunk's reduction of the 8 shard
+partials on a second stream; the activation-gradient GEMM; the input-gradient GEMM per
+row chunk, each chunk's reduction of dX on the second stream; the two weight-gradient
+GEMMs behind the last reduction. Peer ranks' partials are produced once before timing
+(other GPUs' work in a real tensor-parallel group). Inputs are resident in HBM when
+timing starts.
 
-Prints one JSON line: value = rank's fwd+bwd GEMM-chain TFLOP/s (algorithmic FLOPs:
-3 × 2·T·h·(n1 + f_s)), plus a roofline object for the dominant kernel (its average launch
-time measured with HIP events recorded on its own stream by the library) and the CPU
-oracle's throughput on this host.
+Timing policy: before every timed step a 1 GiB scratch buffer is read and written on the
+compute stream (outside the step's event pair), so no step starts with the previous
+step's operands in the 256 MB last-level cache or the L2s; each step is bracketed by HIP
+events on the compute stream (its reductions join that stream at the end), and
+ms_per_step is their mean. The same steps back to back without the flush are reported
+beside it (`t_domino_backtoback_ms`).
+
+Prints one JSON line: value = the rank's fwd+bwd GEMM-chain TFLOP/s (algorithmic FLOPs:
+3 × 2·T·h·(n1 + f_s)); a roofline object for the dominant kernel (its launches timed by
+events the launches' own dispatches record); T_unsplit (one chunk, no reduction: tensor-
+parallel communication disabled), T_serial (one chunk, reductions on the same stream),
+T_domino and the standalone reduction time, with hidden_fraction = 1 − (T_domino −
+T_unsplit) / T_reduce; the CPU oracle's throughput on this host; and, as extra keys, the
+same step figures for the Llama-2-7B column-split and GPT-3-2.7B row-split MLP workloads
+and the GPT-3-6.7B attention block's forward alone (with its last reduction exposed).
 
 `--workload gpt3_6p7b_attn_tp8_row` measures the attention block of one rank instead (QKV
 product, causal attention over the rank's heads, out-projection per chunk and its
@@ -21,6 +35,12 @@ attention's 4·d·S(S+1)/2 per (sequence, head).
 `--workload gpt3_6p7b_layer_tp8_row` measures a stack of whole layers (LayerNorm, attention,
 dropout + residual, LayerNorm, MLP, dropout + residual) in the μ-batch schedule, forward +
 backward, with the FLOPs of the attention block and of the MLP per layer.
+
+`--traffic-summary FETCH.csv WRITE.csv KERNEL COPY_MIB WORKLOAD OUT.txt` writes the HBM
+traffic summary of one kernel from two rocprofv3 counter runs of this bench (one
+FETCH_SIZE, one WRITE_SIZE), calibrated against the plain device copy that
+`--calibration-copy-mib` runs first; bench reports that traffic while the kernel source
+is unchanged.
 """
 from __future__ import annotations
 
@@ -38,34 +58,52 @@ import synth  # noqa: E402  (seeded input generators; no arithmetic of the metho
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 METRIC = "TP-shard block fwd+bwd TFLOP/s (bf16) + % MFMA peak; shard_reduce GB/s"
+DEFAULT_WORKLOAD = "llama2_13b_swiglu_tp8_2d"
+DEFAULT_ALSO = "llama2_7b_swiglu_tp8_col,gpt3_2p7b_mlp_tp8_row,gpt3_6p7b_attn_tp8_row"
+FLUSH_BYTES = 1 << 30
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt3_2p7b_mlp_tp8_row")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads whose step figures are added as extra keys "
+                         f"(default with the default workload: {DEFAULT_ALSO}; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=7)
+    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--no-flush", action="store_true", help="time steps back to back without the cache flush")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "COPY_MIB",
+                                                           "WORKLOAD", "OUT"))
     return ap.parse_args()
 
 
-TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "traffic_*_gpt3_2p7b_mlp.txt")
-GEMM_SOURCE = os.path.join(ROOT, "tensor_transformer_block_domino_amd", "csrc", "gemm_bf16.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "tensor_transformer_block_domino_amd", "csrc", f)
+                  for f in ("gemm_bf16.hip", "common.hpp")]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, calibrated against a plain copy), or None if the summary covers another
-    kernel or the kernel source changed since the counters were taken."""
-    import glob
+def kernel_source_sha():
     import hashlib
 
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in `workload` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None if no summary
+    covers that kernel and workload or the GEMM source changed since the counters were
+    taken."""
+    import glob
+
+    src = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"traffic_*_{workload}.txt"))):
         try:
             kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
             if kv.get("kernel_source_sha256", "").strip() == src and kv.get("kernel", "").strip() == kernel:
@@ -75,44 +113,108 @@ def measured_traffic(kernel):
     return None
 
 
+def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path):
+    """Writes the traffic summary bench reads (measured_traffic) from two counter runs."""
+    import csv
+
+    def values(path, counter):
+        out = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return out
+
+    def norm(name):
+        # rocprofv3 prints the demangled symbol with "void", the namespaces and the
+        # parameter list; the library names the template instantiation alone.
+        n = name.replace(" ", "").replace("domino::(anonymousnamespace)::", "")
+        return n[4:] if n.startswith("void") else n
+
+    def match(vals):
+        want = norm(kernel)
+        return [v for name, vs in vals.items() if norm(name).startswith(want + "(") for v in vs]
+
+    copy_kib = float(copy_mib) * 1024
+    fetch, write = values(fetch_csv, "FETCH_SIZE"), values(write_csv, "WRITE_SIZE")
+    f_copy = sum(fetch["__amd_rocclr_copyBuffer"]) / len(fetch["__amd_rocclr_copyBuffer"])
+    w_copy = sum(write["__amd_rocclr_copyBuffer"]) / len(write["__amd_rocclr_copyBuffer"])
+    fs, ws = copy_kib / f_copy, copy_kib / w_copy
+    fk, wk = match(fetch), match(write)
+    if not fk or not wk:
+        raise SystemExit(f"kernel {kernel} not found in the counter files")
+    f_avg, w_avg = sum(fk) / len(fk), sum(wk) / len(wk)
+    lines = [
+        f"kernel: {kernel}",
+        f"workload: {workload}",
+        f"kernel_source_sha256: {kernel_source_sha()}",
+        f"fetch_kib_per_launch: {f_avg:.1f}",
+        f"write_kib_per_launch: {w_avg:.1f}",
+        f"fetch_scale: {fs:.4f}",
+        f"write_scale: {ws:.4f}",
+        f"calibrated_bytes_per_launch: {int(round((f_avg * fs + w_avg * ws) * 1024))}",
+        f"# {len(fk)} dispatches averaged; the {copy_mib} MiB copy read FETCH_SIZE {f_copy:.0f} KiB and "
+        f"WRITE_SIZE {w_copy:.0f} KiB for {copy_kib:.0f} KiB moved each way.",
+    ]
+    cmd = f"python3 bench.py --workload {workload} --also none --no-cpu-baseline --steps 3 --warmup 1 " \
+          f"--calibration-copy-mib {copy_mib}"
+    header = [
+        f"# HBM traffic of {kernel} in the {workload} bench step.",
+        "# Two rocprofv3 counter runs of the bench command, one counter each, then this summary:",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- {cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- {cmd}",
+        f"#   python3 bench.py --traffic-summary <dir>/fetch_counter_collection.csv "
+        f"<dir>/write_counter_collection.csv '{kernel}' {copy_mib} {workload} <this file>",
+    ]
+    tail = [l.rstrip("\n") for l in open(out_path) if l.startswith("algorithmic") or l.startswith("# ")
+            and not l.startswith("# HBM") and not l.startswith("#   ") and not l.startswith("# Two")
+            and "dispatches averaged" not in l] if os.path.exists(out_path) else []
+    with open(out_path, "w") as f:
+        f.write("\n".join(header + lines + tail) + "\n")
+    print("\n".join(lines))
+
+
+def mlp_role_flops(w):
+    """Algorithmic FLOPs per step of each GEMM role of the MLP block's schedule (the shapes
+    the library launches: GEMM1 and the activation-gradient product once over all rows,
+    GEMM2 per chunk, the input-gradient product per dX chunk, both weight gradients)."""
+    T, h, f, n1 = w.tokens, w.hidden, w.ffn_shard, w.n1
+    return {
+        "fwd_gemm1": 2.0 * T * h * n1,
+        "fwd_gemm2": 2.0 * T * f * h,
+        "dgrad_b": 2.0 * T * h * f,
+        "dgrad_a": 2.0 * T * n1 * h,
+        "wgrad_b": 2.0 * T * f * h,
+        "wgrad_a": 2.0 * T * h * n1,
+    }
+
+
 def mlp_flops(w):
     fwd = 2.0 * w.tokens * w.hidden * w.n1 + 2.0 * w.tokens * w.ffn_shard * w.hidden
     return fwd, 3.0 * fwd
 
 
-def kernel_flops(w, kind):
-    """Algorithmic FLOPs of one launch of each GEMM kind in the workload's schedule."""
-    T, h, f, n1 = w.tokens, w.hidden, w.ffn_shard, w.n1
-    Tc = T // w.row_chunks
-    hc_f = h // w.col_chunks
-    bwd_rows = w.row_chunks
-    bwd_cols = 1 if w.row_chunks > 1 else w.col_chunks
-    return {
-        "fwd_gemm1": 2.0 * Tc * h * n1,
-        "fwd_gemm2": 2.0 * Tc * f * hc_f,
-        "dgrad_b": 2.0 * (T // bwd_rows) * h * f,
-        "dgrad_a": 2.0 * (T // bwd_rows) * n1 * (h // bwd_cols),
-        "wgrad_b": 2.0 * T * f * h,
-        "wgrad_a": 2.0 * T * h * n1,
-    }[kind]
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, inp, reps):
-    """The oracle (numpy fp64) on this host: one rank's forward + backward of the workload."""
+def cpu_baseline(w, inp, reps, max_tokens=8192):
+    """The oracle (numpy fp64) on this host: one rank's forward + backward over the first
+    `max_tokens` tokens of the workload (the whole workload when smaller)."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    rows = min(w.tokens, max_tokens)
     X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
     A0, B0 = oracle.mlp_shard_weights(A, B, w.act, w.n_partials, 0)
     A0, B0 = np.ascontiguousarray(A0), np.ascontiguousarray(B0)
-    _, total = mlp_flops(w)
+    X, dY = np.ascontiguousarray(X[:rows]), np.ascontiguousarray(dY[:rows])
+    total = 3.0 * (2.0 * rows * w.hidden * w.n1 + 2.0 * rows * w.ffn_shard * w.hidden)
     best, done, start = None, 0, time.perf_counter()
     while done < max(1, reps):
         t0 = time.perf_counter()
@@ -123,9 +225,187 @@ def cpu_baseline(w, inp, reps):
         done += 1
         if time.perf_counter() - start > 25:  # bound the whole baseline to ~25 s of CPU work
             break
-    return {"value": total / best / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one rank's full forward+backward of {w.name} (T={w.tokens}, fp64 numpy), best of "
-                      f"{done} reps, {best:.2f} s each"}
+    return {"value": total / best / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"one rank's full forward+backward of {w.name} over its first {rows} of {w.tokens} tokens "
+                      f"(fp64 numpy), best of {done} reps, {best:.2f} s each"}
+
+
+class StepTimer:
+    """Times steps on `stream`: each step between two events, and (unless disabled) a
+    read+write of a 1 GiB scratch buffer on the stream before it, outside the events."""
+
+    def __init__(self, stream, flush=True):
+        import torch
+
+        self.stream = stream
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0") if flush else None
+
+    def flush(self):
+        import torch
+
+        if self.buf is not None:
+            with torch.cuda.stream(self.stream):
+                self.buf.add_(1.0)
+
+    def run(self, fn, steps, warmup):
+        """Mean ms per step over `steps` event-timed steps after `warmup` untimed ones."""
+        import torch
+
+        for _ in range(warmup):
+            self.flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            self.flush()
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def backtoback(fn, steps, warmup):
+    """ms per step of `steps` steps issued back to back (wall clock between synchronisations)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def reduce_standalone_us(D, out, parts, rows, cols, ld, dtype, stream, reps):
+    """shard_reduce of a [rows, cols] region alone on an idle GPU: µs per launch over
+    back-to-back launches between one pair of events on their stream."""
+    import torch
+
+    for _ in range(3):
+        D.shard_reduce(out, ld, parts, ld, rows, cols, dtype, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        D.shard_reduce(out, ld, parts, ld, rows, cols, dtype, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def dominant(per, kernel_of, role_flops, steps):
+    """The GEMM kernel (one template instantiation, as the profiler names it) with the most
+    time per step over every schedule role that launched it, and its rate."""
+    by_kernel = {}
+    for r, fl in role_flops.items():
+        if fl > 0 and per[r][0] > 0:
+            by_kernel.setdefault(kernel_of[r], []).append(r)
+    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
+    n_dom = sum(per[r][0] for r in by_kernel[dom])
+    tot_ms = sum(per[r][1] for r in by_kernel[dom])
+    flops = sum(role_flops[r] for r in by_kernel[dom]) * steps
+    achieved = flops / (tot_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "avg_launch_us": round(tot_ms / max(1, n_dom) * 1e3, 2), "launches": n_dom,
+            "flops_per_launch": flops / max(1, n_dom)}
+
+
+def measure_mlp(w, args, timer, detail):
+    """The MLP block's step figures for workload `w` (bf16)."""
+    import torch
+
+    import tensor_transformer_block_domino_amd as D
+    from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
+
+    print(f"[bench] {w.name}: inputs and peer partials", file=sys.stderr, flush=True)
+    inp = synth.mlp_inputs(w)
+    g = MlpGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn_shard=w.ffn_shard, act=w.act, dtype=w.dtype,
+                 row_chunks=w.row_chunks, col_chunks=w.col_chunks, n_partials=w.n_partials, X=inp["X"], A=inp["A"],
+                 B=inp["B"], dY=inp["dY"], device=torch.device("cuda:0"))
+    g.peer_forward()
+    g.forward()
+    g.peer_backward()
+    torch.cuda.synchronize()
+    compute = timer.stream
+    comm = torch.cuda.Stream()
+
+    def step_domino():
+        g.forward(compute, comm, no_join=1)
+        g.backward(compute, comm)
+
+    def step_serial():
+        g.forward(compute, None, row_chunks=1, col_chunks=1)
+        g.backward(compute, None, row_chunks=1, col_chunks=1)
+
+    def step_unsplit():
+        d_f = g.desc(rank_alone=True, row_chunks=1, col_chunks=1)
+        D.domino_block_fwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, g.ws, g.ws_bytes,
+                           compute, None)
+        D.domino_block_bwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.dY, g.dHpre[0], g.dX_own[0], None,
+                           None, g.dA, g.dB, 0, g.ws, g.ws_bytes, compute, None)
+
+    ms = timer.run(step_domino, args.steps, args.warmup)
+    print(f"[bench] {w.name}: domino step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms_serial = timer.run(step_serial, args.steps, 2)
+    ms_unsplit = timer.run(step_unsplit, args.steps, 2)
+    print(f"[bench] {w.name}: serial {ms_serial:.3f} ms, unsplit without reduce {ms_unsplit:.3f} ms",
+          file=sys.stderr, flush=True)
+    parts = [g.Y_own[r] for r in g.ranks]
+    red_us = reduce_standalone_us(D, g.Y, parts, w.tokens, w.hidden, w.hidden, D.DOMINO_BF16, compute,
+                                  max(args.steps, 10))
+    red_gbps = (w.n_partials + 1) * w.tokens * w.hidden * 2 / (red_us * 1e-6) / 1e9
+    t_reduce_ms = 2 * red_us * 1e-3     # Y and dX, each [T, hidden], per step
+    _, total_flops = mlp_flops(w)
+    value = total_flops / (ms * 1e-3) / 1e12
+    out = {
+        "value": round(value, 2), "ms_per_step": round(ms, 4),
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "ffn_shard": w.ffn_shard, "act": w.act, "tp_partials": w.n_partials,
+                   "split": f"rows x{w.row_chunks}, cols x{w.col_chunks}", "pass": "fwd+bwd"},
+        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "t_domino_ms": round(ms, 4), "t_serial_ms": round(ms_serial, 4),
+        "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
+        "t_reduce_standalone_ms": round(t_reduce_ms, 4),
+        "hidden_fraction": round(1.0 - (ms - ms_unsplit) / t_reduce_ms, 3),
+        "domino_over_serial": round(ms / ms_serial, 4),
+        "domino_over_unsplit": round(ms / ms_unsplit, 4),
+        "shard_reduce_GBps": round(red_gbps, 1),
+        "shard_reduce_hbm_frac": round(red_gbps / HBM_PEAK_GBPS, 4),
+        "shard_reduce_avg_us": round(red_us, 2),
+    }
+    if not detail:
+        del g
+        torch.cuda.empty_cache()
+        return out, None
+    out["t_domino_backtoback_ms"] = round(backtoback(step_domino, args.steps, 2), 4)
+    out["t_graph_ms"] = round(graph_steps(step_domino, timer, args.steps), 4)
+    # Per-kernel durations: the same Domino steps with the library's event timing on.
+    D.domino_timing_enable(True)
+    for _ in range(args.steps):
+        timer.flush()
+        step_domino()
+    torch.cuda.synchronize()
+    roles = ["reduce", "fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a", "aux"]
+    per = {r: D.domino_timing_read(r) for r in roles}
+    kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
+    D.domino_timing_enable(False)
+    rf = mlp_role_flops(w)
+    gemm_ms_step = sum(per[k][1] for k in rf) / args.steps
+    roof = dominant(per, kernel_of, rf, args.steps)
+    roof["traffic"] = measured_traffic(roof["kernel"], w.name)
+    out.update({
+        "gemm_chain_tflops": round(total_flops / (gemm_ms_step * 1e-3) / 1e12, 2),
+        "shard_reduce_in_step_GBps": round(2 * (w.n_partials + 1) * w.tokens * w.hidden * 2 /
+                                           (per["reduce"][1] / args.steps * 1e-3) / 1e9, 1),
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
+        "kernel_tflops": {r: round(rf[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1) for r in rf if per[r][1] > 0},
+        "kernel_of_role": kernel_of,
+        "roofline": roof,
+    })
+    return out, (g, inp)
 
 
 def attn_flops(w):
@@ -178,23 +458,61 @@ def cpu_baseline_attn(w, inp, reps, n_seq=2):
                       f"(fp64 numpy), best of {done} reps, {best:.2f} s each"}
 
 
-def main_attn(args, w):
+def measure_attn(w, args, timer, detail):
+    """The attention block's figures for workload `w`: its forward alone (Domino row chunks,
+    each chunk's out-projection reduced on the second stream; the last reduction has no
+    later work of the block to hide behind, so it is reported as exposed) and, with
+    `detail`, the forward + backward step with per-kernel times and the roofline."""
     import torch
 
     import tensor_transformer_block_domino_amd as D
     from tensor_transformer_block_domino_amd.tp_sim import AttnGroup
 
-    dev = torch.device("cuda:0")
+    print(f"[bench] {w.name}: inputs and peer partials", file=sys.stderr, flush=True)
     inp = synth.attn_inputs(w)
     g = AttnGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
                   row_chunks=w.row_chunks, n_partials=w.n_partials, X=inp["X"], Aqkv=inp["Aqkv"], Bo=inp["Bo"],
-                  dY=inp["dY"], device=dev)
+                  dY=inp["dY"] if detail else None, device=torch.device("cuda:0"))
     g.peer_forward()
     g.forward()
-    g.peer_backward()
+    if detail:
+        g.peer_backward()
     torch.cuda.synchronize()
-    compute = torch.cuda.Stream()
+    compute = timer.stream
     comm = torch.cuda.Stream()
+
+    # Forward alone.
+    fl = attn_flops(w)
+    fwd_flops = fl["qkv"] + fl["attn"] + fl["outproj"]
+    ms_f = timer.run(lambda: g.forward(compute, comm), args.steps, args.warmup)
+    ms_f_serial = timer.run(lambda: g.forward(compute, None, row_chunks=1), args.steps, 2)
+    ms_f_unsplit = timer.run(lambda: g.forward(compute, None, rank_alone=True, row_chunks=1), args.steps, 2)
+    ms_f_chunks = timer.run(lambda: g.forward(compute, None, rank_alone=True), args.steps, 2)
+    print(f"[bench] {w.name}: forward domino {ms_f:.3f} ms, serial {ms_f_serial:.3f}, unsplit {ms_f_unsplit:.3f}",
+          file=sys.stderr, flush=True)
+    parts = [g.Y_own[r] for r in range(w.n_partials)]
+    red_us = reduce_standalone_us(D, g.Y, parts, w.tokens, w.hidden, w.hidden, D.DOMINO_BF16, compute,
+                                  max(args.steps, 10))
+    out = {
+        "forward": {
+            "value": round(fwd_flops / (ms_f * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "t_domino_ms": round(ms_f, 4), "t_serial_ms": round(ms_f_serial, 4),
+            "t_unsplit_no_reduce_ms": round(ms_f_unsplit, 4), "t_chunks_no_reduce_ms": round(ms_f_chunks, 4),
+            "t_reduce_standalone_ms": round(red_us * 1e-3, 4),
+            # The last chunk's reduction: what the Domino forward adds over its chunks alone.
+            "exposed_last_reduce_ms": round(ms_f - ms_f_chunks, 4),
+            "hidden_fraction": round(1.0 - (ms_f - ms_f_unsplit) / (red_us * 1e-3), 3),
+            "domino_over_serial": round(ms_f / ms_f_serial, 4),
+            "domino_over_unsplit": round(ms_f / ms_f_unsplit, 4),
+            "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "heads_shard": w.heads_shard,
+                       "head_dim": w.head_dim, "tp_partials": w.n_partials, "split": f"rows x{w.row_chunks}",
+                       "pass": "fwd", "attention": "causal"},
+        }
+    }
+    if not detail:
+        del g
+        torch.cuda.empty_cache()
+        return out, None
 
     def step_domino():
         g.forward(compute, comm, no_join=1)
@@ -204,60 +522,43 @@ def main_attn(args, w):
         g.forward(compute, None, rank_alone=True, row_chunks=1)
         g.backward(compute, None, rank_alone=True, row_chunks=1)
 
-    ms = timed_steps(step_domino, args.steps, args.warmup)
-    print(f"[bench] attention domino step {ms:.3f} ms", file=sys.stderr, flush=True)
-    ms_unsplit = timed_steps(step_unsplit, args.steps, 2)
-
+    ms = timer.run(step_domino, args.steps, args.warmup)
+    print(f"[bench] {w.name}: domino fwd+bwd step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms_unsplit = timer.run(step_unsplit, args.steps, 2)
     D.domino_timing_enable(True)
     for _ in range(args.steps):
+        timer.flush()
         step_domino()
     torch.cuda.synchronize()
-    fl = attn_flops(w)
     roles = list(fl) + ["reduce", "aux"]
     per = {r: D.domino_timing_read(r) for r in roles}
     kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
     D.domino_timing_enable(False)
     total_flops = sum(fl.values())
     value = total_flops / (ms * 1e-3) / 1e12
-    by_kernel = {}
-    for r in fl:
-        if fl[r] > 0:
-            by_kernel.setdefault(kernel_of[r], []).append(r)
-    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
-    n_dom = sum(per[r][0] for r in by_kernel[dom])
-    tot_dom = sum(per[r][1] for r in by_kernel[dom])
-    flops_dom = sum(fl[r] for r in by_kernel[dom]) * args.steps
-    achieved = flops_dom / (tot_dom * 1e-3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    t_reduce_ms = 2 * red_us * 1e-3
+    out.update({
+        "value": round(value, 2), "ms_per_step": round(ms, 4),
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
                    "heads_shard": w.heads_shard, "head_dim": w.head_dim, "tp_partials": w.n_partials,
                    "split": f"rows x{w.row_chunks}", "pass": "fwd+bwd", "attention": "causal"},
         "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "t_domino_ms": round(ms, 4),
         "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
-        "t_reduce_ms": round(per["reduce"][1] / args.steps, 4),
+        "t_reduce_standalone_ms": round(t_reduce_ms, 4),
+        "hidden_fraction": round(1.0 - (ms - ms_unsplit) / t_reduce_ms, 3),
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
         "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
                           for r in fl if fl[r] > 0 and per[r][1] > 0},
         "kernel_of_role": kernel_of,
-        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "avg_launch_us": round(tot_dom / max(1, n_dom) * 1e3, 2), "launches": n_dom,
-                     "flops_per_launch": flops_dom / max(1, n_dom)},
-    }
+        "roofline": dominant(per, kernel_of, fl, args.steps),
+    })
+    return out, (g, inp)
+
+
+def main_attn(args, w, timer):
+    res, (g, inp) = measure_attn(w, args, timer, detail=True)
+    out = headline(args, res)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_attn(w, inp, args.cpu_reps)
@@ -308,7 +609,7 @@ def cpu_baseline_layer(w, inp, n_seq=1):
                       f"{dt:.1f} s"}
 
 
-def main_layer(args, w):
+def main_layer(args, w, timer):
     import torch
 
     import tensor_transformer_block_domino_amd as D
@@ -324,7 +625,7 @@ def main_layer(args, w):
     g.peer_forward()
     g.peer_backward()
     torch.cuda.synchronize()
-    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    compute, comm = timer.stream, torch.cuda.Stream()
 
     def step_domino():
         g.forward(compute, comm)
@@ -338,13 +639,14 @@ def main_layer(args, w):
         g.forward(compute, comm, row_chunks=1)
         g.backward(compute, comm, row_chunks=1)
 
-    ms = timed_steps(step_domino, args.steps, args.warmup)
+    ms = timer.run(step_domino, args.steps, args.warmup)
     print(f"[bench] layer stack domino step {ms:.3f} ms", file=sys.stderr, flush=True)
-    ms_serial = timed_steps(step_serial, args.steps, 2)
-    ms_unsplit = timed_steps(step_unsplit, args.steps, 2)
-    ms_graph = graph_steps(step_domino, compute, args.steps)
+    ms_serial = timer.run(step_serial, args.steps, 2)
+    ms_unsplit = timer.run(step_unsplit, args.steps, 2)
+    ms_graph = graph_steps(step_domino, timer, args.steps)
     D.domino_timing_enable(True)
     for _ in range(args.steps):
+        timer.flush()
         step_domino()
     torch.cuda.synchronize()
     fl = layer_flops(w)
@@ -354,28 +656,8 @@ def main_layer(args, w):
     D.domino_timing_enable(False)
     total_flops = sum(fl.values())
     value = total_flops / (ms * 1e-3) / 1e12
-    by_kernel = {}
-    for r in fl:
-        if fl[r] > 0 and per[r][0] > 0:
-            by_kernel.setdefault(kernel_of[r], []).append(r)
-    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
-    n_dom = sum(per[r][0] for r in by_kernel[dom])
-    tot_dom = sum(per[r][1] for r in by_kernel[dom])
-    flops_dom = sum(fl[r] for r in by_kernel[dom]) * args.steps
-    achieved = flops_dom / (tot_dom * 1e-3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    res = {
+        "value": round(value, 2), "ms_per_step": round(ms, 4),
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
                    "heads_shard": w.heads_shard, "head_dim": w.head_dim, "ffn_shard": w.ffn_shard, "act": w.act,
                    "layers": w.layers, "p_drop": w.p_drop, "tp_partials": w.n_partials,
@@ -385,51 +667,57 @@ def main_layer(args, w):
         "t_serial_ms": round(ms_serial, 4),
         "t_unsplit_ms": round(ms_unsplit, 4),
         "t_graph_ms": round(ms_graph, 4),
-        "t_reduce_ms": round(per["reduce"][1] / args.steps, 4),
+        "t_reduce_in_step_ms": round(per["reduce"][1] / args.steps, 4),
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
         "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
                           for r in fl if fl[r] > 0 and per[r][1] > 0},
         "kernel_of_role": kernel_of,
-        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "avg_launch_us": round(tot_dom / max(1, n_dom) * 1e3, 2), "launches": n_dom,
-                     "flops_per_launch": flops_dom / max(1, n_dom)},
+        "roofline": dominant(per, kernel_of, fl, args.steps),
     }
+    out = headline(args, res)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_layer(w, inp)
     print(json.dumps(out), flush=True)
 
 
-def graph_steps(fn, stream, steps):
-    """The step captured once into a HIP graph on `stream` and replayed: ms per replay."""
+def graph_steps(fn, timer, steps):
+    """The step captured once into a HIP graph on the timer's stream and replayed: ms per
+    replay (timed like the eager steps)."""
     import torch
 
     fn()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
+    with torch.cuda.graph(graph, stream=timer.stream):
         fn()
     torch.cuda.synchronize()
-    return timed_steps(graph.replay, steps, 2)
+
+    def replay():
+        with torch.cuda.stream(timer.stream):   # replay() launches on the current stream
+            graph.replay()
+
+    return timer.run(replay, steps, 2)
 
 
-def timed_steps(fn, steps, warmup):
-    import torch
-
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+def headline(args, res):
+    """The JSON line's fixed keys, then the workload's figures."""
+    out = {
+        "metric": METRIC, "value": res.pop("value"), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": res.pop("config"),
+        "timing": ("mean of per-step HIP-event times on the compute stream; a 1 GiB scratch read+write before "
+                   "each step, outside the events" if not args.no_flush else
+                   "mean of per-step HIP-event times on the compute stream, steps back to back"),
+    }
+    out.update(res)
+    return out
 
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported: the library sums the "
               f"tensor-parallel partials on one GPU, with no collective between GPUs", file=sys.stderr)
@@ -437,7 +725,6 @@ def main():
     import torch
 
     import tensor_transformer_block_domino_amd as D
-    from tensor_transformer_block_domino_amd.tp_sim import MlpGroup
 
     D.load()
     if args.calibration_copy_mib:
@@ -447,153 +734,30 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    timer = StepTimer(torch.cuda.Stream(), flush=not args.no_flush)
     w = synth.WORKLOADS[args.workload]
     if isinstance(w, synth.AttnWorkload):
-        return main_attn(args, w)
+        return main_attn(args, w, timer)
     if isinstance(w, synth.LayerWorkload):
-        return main_layer(args, w)
+        return main_layer(args, w, timer)
     assert isinstance(w, synth.MlpWorkload) and w.dtype == "bf16"
-    dev = torch.device("cuda:0")
-    inp = synth.mlp_inputs(w)
-    g = MlpGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn_shard=w.ffn_shard, act=w.act, dtype=w.dtype,
-                 row_chunks=w.row_chunks, col_chunks=w.col_chunks, n_partials=w.n_partials, X=inp["X"], A=inp["A"],
-                 B=inp["B"], dY=inp["dY"], device=dev)
-    g.peer_forward()
-    g.forward()
-    g.peer_backward()
-    torch.cuda.synchronize()
-    compute = torch.cuda.Stream()
-    comm = torch.cuda.Stream()
-
-    def step_domino():
-        g.forward(compute, comm, no_join=1)
-        g.backward(compute, comm)
-
-    def step_serial():
-        g.forward(compute, None, row_chunks=1, col_chunks=1)
-        g.backward(compute, None, row_chunks=1, col_chunks=1)
-
-    def step_unsplit():
-        d_f = g.desc(rank_alone=True, row_chunks=1, col_chunks=1)
-        D.domino_block_fwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.Y_own[0], None, None, g.ws, g.ws_bytes,
-                           compute, None)
-        D.domino_block_bwd(d_f, g.X, g.A_s[0], g.B_s[0], g.Hpre[0], g.H[0], g.dY, g.dHpre[0], g.dX_own[0], None,
-                           None, g.dA, g.dB, 0, g.ws, g.ws_bytes, compute, None)
-
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
-
-    # The timed region: Domino chunks, reductions on the second stream.
-    ms = timed(step_domino, args.steps, args.warmup)
-    print(f"[bench] domino step {ms:.3f} ms", file=sys.stderr, flush=True)
-    ms_serial = timed(step_serial, args.steps, 2)
-    ms_unsplit = timed(step_unsplit, args.steps, 2)
-    ms_graph = graph_steps(step_domino, compute, args.steps)
-    print(f"[bench] serial {ms_serial:.3f} ms, unsplit without reduce {ms_unsplit:.3f} ms", file=sys.stderr,
-          flush=True)
-
-    # Per-kernel durations: the same Domino steps with the library's event timing on.
-    D.domino_timing_enable(True)
-    for _ in range(args.steps):
-        step_domino()
-    torch.cuda.synchronize()
-    per, kernel_of = {}, {}
-    for kind in ("reduce", "fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a", "aux"):
-        n, tot = D.domino_timing_read(kind)
-        per[kind] = (n, tot)
-        kernel_of[kind] = D.domino_timing_kernel(kind)
-    # shard_reduce alone: the whole [T, h] output, the 8 partials, on an idle GPU. The rate is
-    # taken over back-to-back launches between one pair of events on their stream (the gaps
-    # between launches included); the library's per-launch events, which also span each
-    # launch's dispatch and completion signal, are reported beside it.
-    D.domino_timing_enable(True)
-    parts = [g.Y_own[r] for r in g.ranks]
-    for _ in range(args.steps):
-        D.shard_reduce(g.Y, w.hidden, parts, w.hidden, w.tokens, w.hidden, D.DOMINO_BF16, compute)
-    torch.cuda.synchronize()
-    n_sa, tot_sa = D.domino_timing_read("reduce")
-    D.domino_timing_enable(False)
-    red_ev_us = tot_sa / max(1, n_sa) * 1e3
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(args.steps, 20)
-    e0.record(compute)
-    for _ in range(reps):
-        D.shard_reduce(g.Y, w.hidden, parts, w.hidden, w.tokens, w.hidden, D.DOMINO_BF16, compute)
-    e1.record(compute)
-    torch.cuda.synchronize()
-    red_sa_us = e0.elapsed_time(e1) / reps * 1e3
-    red_sa_gbps = (w.n_partials + 1) * w.tokens * w.hidden * 2 / (red_sa_us * 1e-6) / 1e9
-
-    fwd_flops, total_flops = mlp_flops(w)
-    value = total_flops / (ms * 1e-3) / 1e12
-    gemm_kinds = ["fwd_gemm1", "fwd_gemm2", "dgrad_b", "dgrad_a", "wgrad_b", "wgrad_a"]
-    # Dominant kernel: the GEMM kernel (one template instantiation, as the profiler names
-    # it) with the most time per step, over every schedule role that launched it.
-    by_kernel = {}
-    for r in gemm_kinds:
-        by_kernel.setdefault(kernel_of[r], []).append(r)
-    dom = max(by_kernel, key=lambda k: sum(per[r][1] for r in by_kernel[k]))
-    n_dom = sum(per[r][0] for r in by_kernel[dom])
-    tot_dom = sum(per[r][1] for r in by_kernel[dom])
-    flops_dom = sum(per[r][0] * kernel_flops(w, r) for r in by_kernel[dom])
-    avg_ms = tot_dom / max(1, n_dom)
-    achieved = flops_dom / (tot_dom * 1e-3) / 1e12
-    n_red, tot_red = per["reduce"]
-    # Reduced bytes per step: Y and dX, each (P+1)·T·h·2 bytes.
-    red_bytes_step = 2 * (w.n_partials + 1) * w.tokens * w.hidden * 2
-    red_ms_step = tot_red / args.steps
-    red_gbps = red_bytes_step / (red_ms_step * 1e-3) / 1e9
-    gemm_ms_step = sum(per[k][1] for k in gemm_kinds) / args.steps
-    hidden_frac = 1.0 - (ms - ms_unsplit) / red_ms_step if red_ms_step > 0 else None
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
-                   "ffn_shard": w.ffn_shard, "act": w.act, "tp_partials": w.n_partials,
-                   "split": f"rows x{w.row_chunks}, cols x{w.col_chunks}", "pass": "fwd+bwd"},
-        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-        "gemm_chain_tflops": round(total_flops / (gemm_ms_step * 1e-3) / 1e12, 2),
-        "shard_reduce_GBps": round(red_sa_gbps, 1),
-        "shard_reduce_hbm_frac": round(red_sa_gbps / HBM_PEAK_GBPS, 4),
-        "shard_reduce_avg_us": round(red_sa_us, 2),
-        "shard_reduce_event_us": round(red_ev_us, 2),
-        "shard_reduce_in_step_GBps": round(red_gbps, 1),
-        "t_domino_ms": round(ms, 4),
-        "t_serial_ms": round(ms_serial, 4),
-        "t_unsplit_no_reduce_ms": round(ms_unsplit, 4),
-        "t_graph_ms": round(ms_graph, 4),
-        "t_reduce_ms": round(red_ms_step, 4),
-        "hidden_fraction": None if hidden_frac is None else round(hidden_frac, 3),
-        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
-        "kernel_of_role": kernel_of,
-        "roofline": {"bound": "mfma", "kernel": dom, "roles": by_kernel[dom], "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(dom) if args.workload == "gpt3_2p7b_mlp_tp8_row" else None,
-                     "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n_dom,
-                     "flops_per_launch": flops_dom / max(1, n_dom)},
-    }
+    res, (g, inp) = measure_mlp(w, args, timer, detail=True)
+    out = headline(args, res)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_reps)
+    del g
+    torch.cuda.empty_cache()
+    also = args.also if args.also is not None else (DEFAULT_ALSO if args.workload == DEFAULT_WORKLOAD else "none")
+    others = {}
+    for name in [n for n in also.split(",") if n and n != "none"]:
+        ow = synth.WORKLOADS[name]
+        if isinstance(ow, synth.MlpWorkload):
+            others[name] = measure_mlp(ow, args, timer, detail=False)[0]
+        elif isinstance(ow, synth.AttnWorkload):
+            others[name] = measure_attn(ow, args, timer, detail=False)[0]["forward"]
+    if others:
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 

@@ -191,9 +191,13 @@ class AttnGroup:
                                     stream, None, lse=self.lse[r])
 
     def forward(self, compute=None, comm=None, **desc_kw):
-        peers = [self.Y_own[r] for r in range(1, self.P)] if self.P > 1 else None
+        """Rank 0's forward. With rank_alone=True the call reduces nothing: Y_own is the
+        output (tensor-parallel communication disabled)."""
+        alone = desc_kw.get("rank_alone", False)
+        peers = [self.Y_own[r] for r in range(1, self.P)] if self.P > 1 and not alone else None
         L.domino_attn_block_fwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
-                                self.Y_own[0], peers, self.Y, self.ws, self.ws_bytes, compute, comm, lse=self.lse[0])
+                                self.Y_own[0], peers, None if alone else self.Y, self.ws, self.ws_bytes, compute,
+                                comm, lse=self.lse[0])
 
     def peer_backward(self, stream=None):
         dA, dB = torch.empty_like(self.dA), torch.empty_like(self.dB)
@@ -203,10 +207,13 @@ class AttnGroup:
                                     self.dX_own[r], None, None, dA, dB, 0, self.ws, self.ws_bytes, stream, None)
 
     def backward(self, compute=None, comm=None, accumulate=0, **desc_kw):
-        peers = [self.dX_own[r] for r in range(1, self.P)] if self.P > 1 else None
+        """Rank 0's backward; rank_alone=True reduces nothing (dX_own is the output)."""
+        alone = desc_kw.get("rank_alone", False)
+        peers = [self.dX_own[r] for r in range(1, self.P)] if self.P > 1 and not alone else None
         L.domino_attn_block_bwd(self.desc(**desc_kw), self.X, self.A_s[0], self.B_s[0], self.QKV[0], self.O[0],
-                                self.lse[0], self.dY, self.dO[0], self.dQKV[0], self.dX_own[0], peers, self.dX,
-                                self.dA, self.dB, accumulate, self.ws, self.ws_bytes, compute, comm)
+                                self.lse[0], self.dY, self.dO[0], self.dQKV[0], self.dX_own[0], peers,
+                                None if alone else self.dX, self.dA, self.dB, accumulate, self.ws, self.ws_bytes,
+                                compute, comm)
 
 
 _ACTS = {"gelu_tanh": L.DOMINO_ACT_GELU_TANH, "swiglu": L.DOMINO_ACT_SWIGLU}
