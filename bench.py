@@ -79,6 +79,9 @@ def parse():
                     help="run one plain device copy of this size first (for HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "COPY_MIB",
                                                            "WORKLOAD", "OUT"))
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "OUT"),
+                    help="per-kernel, per-launch-shape statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--trace-command", default="", help="the command that made the trace (recorded in the summary)")
     return ap.parse_args()
 
 
@@ -170,6 +173,41 @@ def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path):
             and "dispatches averaged" not in l] if os.path.exists(out_path) else []
     with open(out_path, "w") as f:
         f.write("\n".join(header + lines + tail) + "\n")
+    print("\n".join(lines))
+
+
+def trace_summary(trace_csv, out_path, command=""):
+    """Writes per-kernel statistics of a rocprofv3 kernel trace, one line per kernel and
+    launch shape (grid size): a kernel launched on chunks and on whole tensors gets one
+    line for each, so the average of the launches a bench figure covers can be read off."""
+    import csv
+
+    rows = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"].replace("domino::(anonymous namespace)::", "").replace("void ", "")
+        name = name[:name.rfind(">(") + 1] if ">(" in name else name.split("(")[0]
+        key = (name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])), int(r["Workgroup_Size_X"]))
+        d = rows.setdefault(key, {"n": 0, "tot": 0.0, "min": 1e30, "max": 0.0, "vgpr": r["VGPR_Count"],
+                                  "agpr": r["Accum_VGPR_Count"], "lds": r["LDS_Block_Size"]})
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        d["n"] += 1
+        d["tot"] += us
+        d["min"] = min(d["min"], us)
+        d["max"] = max(d["max"], us)
+    total = sum(d["tot"] for d in rows.values())
+    lines = [f"# Kernel statistics per launch shape: `{os.path.basename(trace_csv)}`", ""]
+    if command:
+        lines += ["Made by:", "", "```", command,
+                  f"python3 bench.py --trace-summary {trace_csv} {out_path} --trace-command '<the line above>'",
+                  "```", ""]
+    lines += ["| kernel | workgroups | threads | calls | avg µs | min µs | max µs | total ms | % | VGPR | AGPR | LDS B |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, wgs, thr), d in sorted(rows.items(), key=lambda kv: -kv[1]["tot"]):
+        lines.append(f"| `{name}` | {wgs} | {thr} | {d['n']} | {d['tot'] / d['n']:.1f} | {d['min']:.1f} | "
+                     f"{d['max']:.1f} | {d['tot'] * 1e-3:.3f} | {100 * d['tot'] / total:.1f} | {d['vgpr']} | "
+                     f"{d['agpr']} | {d['lds']} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -718,6 +756,8 @@ def main():
     args = parse()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.trace_summary:
+        return trace_summary(*args.trace_summary, args.trace_command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported: the library sums the "
               f"tensor-parallel partials on one GPU, with no collective between GPUs", file=sys.stderr)

@@ -7,6 +7,13 @@ import tensor_transformer_block_domino_amd as D
 
 BF16_TOL = 1e-2   # normwise relative error bar for bf16 storage with fp32 accumulation
 F32_TOL = 1e-5    # the same bar for the fp32 layer
+# Per-row bar of the gradients that pass through the attention's softmax backward (dQ, dK,
+# and what is computed from them: dQKV, dA_qkv_s, the attention's dX). There each score
+# gradient is P·(dP − Δ), and Δ, a row's Σ P·dP, is formed from the bf16 O and dO; in rows
+# with few visible keys dP − Δ is small next to its terms, so its rounding error, relative
+# to that row's result, exceeds the tensor's normwise error (up to 1.5e-2 measured against
+# ~4e-3 normwise). 3e-2 still fails a row with one wrong element among its 256 or more.
+ATTN_BWD_ROW_TOL = 3e-2
 
 
 def dev():
@@ -45,18 +52,24 @@ def row_relerr(got, ref) -> tuple:
     return float(e[worst]), worst
 
 
-def check(name, got, ref, tol, rows=True):
-    """Normwise relative error of the whole tensor within tol, and (rows=True) of every row
-    within tol as well (row_relerr)."""
+def check(name, got, ref, tol, row_tol=None):
+    """Normwise relative error of the whole tensor within tol and, for a matrix, that of
+    every row within row_tol (default tol; row_relerr). A vector (bias, LayerNorm and
+    per-row statistics) gets the normwise bound alone: its elements are sums whose own
+    relative error is not bounded by it, while one wrong element among a few thousand
+    already moves the normwise error past the bar."""
+    got, ref = np.asarray(got), np.asarray(ref)
     e = relerr(got, ref)
+    rows = got.ndim >= 2
+    row_tol = tol if row_tol is None else row_tol
     msg = f"  {name}: normwise rel err {e:.3e}"
     if rows:
         er, worst = row_relerr(got, ref)
-        msg += f", worst row {er:.3e} (row {worst})"
+        msg += f", worst row {er:.3e} (row {worst}, tol {row_tol:g})"
     print(msg + f" (tol {tol:g})", flush=True)
     assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
     if rows:
-        assert er <= tol, f"{name}: row {worst} has normwise rel err {er:.3e} > {tol:g}"
+        assert er <= row_tol, f"{name}: row {worst} has normwise rel err {er:.3e} > {row_tol:g}"
     return e
 
 
@@ -70,4 +83,4 @@ def sync():
     torch.cuda.synchronize()
 
 
-__all__ = ["oracle", "D", "np", "torch", "dev", "f64", "relerr", "row_relerr", "check", "poison", "sync", "BF16_TOL", "F32_TOL"]
+__all__ = ["oracle", "D", "np", "torch", "dev", "f64", "relerr", "row_relerr", "check", "poison", "sync", "BF16_TOL", "F32_TOL", "ATTN_BWD_ROW_TOL"]

@@ -5,7 +5,7 @@ rank, one and two row chunks; determinism and accumulation."""
 import pytest
 
 import synth
-from gpu_util import D, np, torch, dev, f64, check, poison, sync, oracle, BF16_TOL
+from gpu_util import D, np, torch, dev, f64, check, poison, sync, oracle, BF16_TOL, ATTN_BWD_ROW_TOL
 from tensor_transformer_block_domino_amd.tp_sim import AttnGroup
 
 pytestmark = pytest.mark.gpu
@@ -55,10 +55,10 @@ def test_attention_backward_small(batch, seq, hs, row_chunks):
             print(f"  {name}: max abs {np.max(np.abs(blk)):.3e} (exact 0, bound {bound:.3e})", flush=True)
             assert np.max(np.abs(blk)) <= bound, name
     else:
-        check("dQ", got[:, :hd], dQKV[:, :hd], BF16_TOL)
-        check("dK", got[:, hd:2 * hd], dQKV[:, hd:2 * hd], BF16_TOL)
-    check("dX", f64(g.dX), dX, BF16_TOL)
-    check("dA_qkv_s", f64(g.dA), dA, BF16_TOL)
+        check("dQ", got[:, :hd], dQKV[:, :hd], BF16_TOL, ATTN_BWD_ROW_TOL)
+        check("dK", got[:, hd:2 * hd], dQKV[:, hd:2 * hd], BF16_TOL, ATTN_BWD_ROW_TOL)
+    check("dX", f64(g.dX), dX, BF16_TOL, ATTN_BWD_ROW_TOL)
+    check("dA_qkv_s", f64(g.dA), dA, BF16_TOL, ATTN_BWD_ROW_TOL)
     check("dB_o_s", f64(g.dB), dB, BF16_TOL)
 
 

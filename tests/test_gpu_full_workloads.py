@@ -5,7 +5,7 @@ exact functions of the same rows / columns of the inputs)."""
 import pytest
 
 import synth
-from gpu_util import D, np, torch, dev, f64, check, sync, oracle, BF16_TOL
+from gpu_util import D, np, torch, dev, f64, check, sync, oracle, BF16_TOL, ATTN_BWD_ROW_TOL
 from tensor_transformer_block_domino_amd.tp_sim import AttnGroup, MlpGroup
 
 pytestmark = pytest.mark.gpu
@@ -102,15 +102,15 @@ def test_full_attention_backward_workload():
     A0, B0 = oracle.attn_shard_weights(Aqkv, Bo, w.heads_full, w.head_dim, w.n_partials, 0)
     dO, dQKV, _, dA, dB = oracle.attn_shard_backward(X, A0, B0, dY, w.batch, w.seq, w.heads_shard, w.head_dim)
     check("dO", f64(g.dO[0]), dO, BF16_TOL)
-    check("dQKV", f64(g.dQKV[0]), dQKV, BF16_TOL)
-    check("dA_qkv_s", f64(g.dA), dA, BF16_TOL)
+    check("dQKV", f64(g.dQKV[0]), dQKV, BF16_TOL, ATTN_BWD_ROW_TOL)
+    check("dA_qkv_s", f64(g.dA), dA, BF16_TOL, ATTN_BWD_ROW_TOL)
     check("dB_o_s", f64(g.dB), dB, BF16_TOL)
     dX = f64(g.dX)
     for b in (0, w.batch // w.row_chunks):
         print(f"  oracle: reduced dX of sequence {b} (all {w.heads_full} heads)", flush=True)
         r = slice(b * w.seq, (b + 1) * w.seq)
         ref = oracle.attn_backward_unsharded(X[r], Aqkv, Bo, dY[r], 1, w.seq, w.heads_full, w.head_dim)
-        check(f"dX seq {b}", dX[r], ref, BF16_TOL)
+        check(f"dX seq {b}", dX[r], ref, BF16_TOL, ATTN_BWD_ROW_TOL)
 
 
 def test_full_layer_stack_workload():
@@ -146,4 +146,4 @@ def test_full_layer_stack_workload():
     out, _ = oracle.stack_forward(X, layers, keeps, w.p_drop, 1, w.seq, w.heads_full, w.head_dim, w.act)
     check(f"out (sequence {b})", f64(g.out[rows]), out, BF16_TOL)
     dx, _ = oracle.stack_backward(X, layers, keeps, w.p_drop, dY, 1, w.seq, w.heads_full, w.head_dim, w.act)
-    check(f"dX (sequence {b})", f64(g.dX[rows]), dx, BF16_TOL)
+    check(f"dX (sequence {b})", f64(g.dX[rows]), dx, BF16_TOL, ATTN_BWD_ROW_TOL)
