@@ -179,6 +179,28 @@ domino_status domino_block_bwd(const domino_mlp_desc* desc, const void* X, const
                                hipStream_t compute, hipStream_t comm);
 
 /*
+ * domino_block_bwd_noalloc — domino_block_bwd without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The arguments and results are those of
+ * domino_block_bwd; the k-split workspace is a static device array of
+ * DOMINO_NOALLOC_SCRATCH_BYTES bytes that each GPU holds until the process ends.
+ *   - Shapes whose domino_block_bwd_workspace_size exceeds that size are rejected with
+ *     DOMINO_ERR_UNSUPPORTED before anything is enqueued (domino_last_error says why).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (different streams, or host threads) race on it and
+ *     must be ordered by the caller.
+ *   - No hipMalloc, hipFree or other allocating routine is called. The first call on a
+ *     device looks up the array's device address; the library's events are created once
+ *     per device and host thread, on its first call there (as for every entry point).
+ */
+#define DOMINO_NOALLOC_SCRATCH_BYTES (64u << 20)
+domino_status domino_block_bwd_noalloc(const domino_mlp_desc* desc, const void* X, const void* A_s,
+                                       const void* B_s, const void* Hpre, const void* H, const void* dY,
+                                       void* dHpre, void* dX_own, const void* const* peer_dX, void* dX,
+                                       float* dA_s, float* dB_s, float* d_b1_s, int32_t accumulate,
+                                       hipStream_t compute, hipStream_t comm);
+
+/*
  * domino_attn_block_fwd — attention shard forward by row chunks (whole sequences)
  * ("TP 的数据依赖…": A = multi-head attention on the rank's heads, B = output projection;
  * "前向：多个计算片段轮转重叠 AllReduce": AllReduce(attn0) overlaps μ-batch 1's attention).

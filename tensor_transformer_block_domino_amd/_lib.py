@@ -26,6 +26,7 @@ KERNEL_KINDS = {"reduce": 0, "fwd_gemm1": 1, "fwd_gemm2": 2, "dgrad_b": 3, "dgra
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTED = ("shard_reduce", "domino_block_fwd", "domino_block_fwd_workspace_size", "domino_block_bwd",
+            "domino_block_bwd_noalloc",
             "domino_block_bwd_workspace_size", "domino_attn_block_fwd", "domino_attn_block_fwd_workspace_size",
             "domino_attn_block_bwd", "domino_attn_block_bwd_workspace_size",
             "domino_resid_ln_fwd", "domino_resid_ln_bwd", "domino_resid_ln_bwd_workspace_size", "domino_stack_fwd",
@@ -117,6 +118,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.domino_block_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp,
                                      i32, vp, ctypes.c_size_t, vp, vp]
     lib.domino_block_bwd.restype = i32
+    lib.domino_block_bwd_noalloc.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp,
+                                             vp, i32, vp, vp]
+    lib.domino_block_bwd_noalloc.restype = i32
     lib.domino_attn_block_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp,
                                           ctypes.c_size_t, vp, vp]
     lib.domino_attn_block_fwd.restype = i32
@@ -204,6 +208,17 @@ def domino_block_fwd_workspace_size(desc: MlpDesc) -> int:
 
 def domino_block_bwd_workspace_size(desc: MlpDesc) -> int:
     return int(load().domino_block_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def domino_block_bwd_noalloc(desc: MlpDesc, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, peer_dX, dX, dA_s, dB_s,
+                             accumulate: int = 0, compute=None, comm=None, d_b1_s=None):
+    _check(load().domino_block_bwd_noalloc(ctypes.byref(desc), _ptr(X), _ptr(A_s), _ptr(B_s), _ptr(Hpre), _ptr(H),
+                                           _ptr(dY), _ptr(dHpre), _ptr(dX_own), _ptr_array(peer_dX), _ptr(dX),
+                                           _ptr(dA_s), _ptr(dB_s), _ptr(d_b1_s), int(accumulate), _stream(compute),
+                                           _stream(comm)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DOMINO_NOALLOC_SCRATCH_BYTES
 
 
 def domino_attn_block_fwd_workspace_size(desc: AttnDesc) -> int:

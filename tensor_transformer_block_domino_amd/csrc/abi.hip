@@ -1216,6 +1216,70 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
   return DOMINO_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// The allocation-free variant of domino_block_bwd, for callers that cannot allocate device
+// memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+// hipMalloc): the workspace of the backward's k-split products is a file-scope device
+// array instead of a caller buffer. Each GPU the library runs on holds its own copy of
+// `scratch` until the process ends. Its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) on the first call there, and only that
+// address is handed to kernels: in host code the array's name is a host-side stand-in,
+// not a device pointer. Every call on a GPU shares that GPU's array; nothing in it needs
+// to start at zero (the split products write every slot they read), and calls that
+// overlap on one GPU race on it.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(DOMINO_NOALLOC_SCRATCH_BYTES);
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array (looked up on first use).
+domino_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DOMINO_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DOMINO_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DOMINO_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DOMINO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+domino_status domino_block_bwd_noalloc(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
+                                       const void* Hpre, const void* H, const void* dY, void* dHpre, void* dX_own,
+                                       const void* const* peer_dX, void* dX, float* dA_s, float* dB_s,
+                                       float* d_b1_s, int32_t accumulate, hipStream_t compute, hipStream_t comm) {
+  t_last_error.clear();
+  domino_status st = check_mlp_desc(d);
+  if (st != DOMINO_OK) return st;
+  const size_t need = domino_block_bwd_workspace_size(d);
+  if (need > kScratchBytes)
+    return fail(DOMINO_ERR_UNSUPPORTED, "this shape's backward needs " + std::to_string(need) +
+                                            " bytes of workspace; the static scratch holds " +
+                                            std::to_string(kScratchBytes) +
+                                            " (domino_block_bwd takes a caller workspace of any size)");
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != DOMINO_OK) return st;
+  return domino_block_bwd(d, X, A_s, B_s, Hpre, H, dY, dHpre, dX_own, peer_dX, dX, dA_s, dB_s, d_b1_s, accumulate, ws,
+                          kScratchBytes, compute, comm);
+}
+
 domino_status domino_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   for (auto& r : g_timing_recs) {
