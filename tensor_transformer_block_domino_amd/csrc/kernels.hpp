@@ -24,12 +24,15 @@ constexpr int kMaxPartials = 16;
 //    of a product operand must stay at or below 2^22 elements (255·2^22·2 + 112 < 2^31).
 //    The attention kernels' copy offsets (64 rows of the QKV leading dimension) fit
 //    within the same bound.
-//  * shard_reduce walks its 16-byte groups with a uint32 grid stride (at most 2048
-//    workgroups × 256 threads, two groups per thread per pass), so a region may hold at
-//    most 2^32 − 2^21 groups: the index then never wraps past the end.
+//  * shard_reduce walks its 16-byte groups with a uint32 grid stride (at most
+//    kReduceMaxBlocks workgroups × 256 threads, two groups per thread per pass), so a
+//    region may hold at most 2^32 − 2^21 groups: the index then never wraps past the end.
 constexpr int64_t kMaxLd = int64_t(1) << 22;
 constexpr int64_t kReduceMaxGroups = (int64_t(1) << 32) - (int64_t(1) << 21);
-constexpr int kReduceMaxBlocks = 2048;
+// One workgroup per CU: on the Llama-2-13B reductions (8 partials of 16384 × 2560) 256
+// workgroups stream 5.7 TB/s alone against 4.9 TB/s for 2048, and leave more of each CU's
+// memory pipeline to the products running beside them (Domino step 5.81 vs 5.97 ms).
+constexpr int kReduceMaxBlocks = 256;
 
 // Records the kernel (symbol and template arguments) a launcher is about to launch on the
 // calling thread; the timing facility attaches it to the launch it brackets.
@@ -81,6 +84,10 @@ struct GemmSplit {
   int tile = 0, tiles_m = 0, tiles_n = 0, dp_tiles = 0, splits = 1;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, GemmSplit* split);
+// The eight-wave 256×256 kernel on whole tiles (gemm8.hip); launch_gemm picks it for the
+// products it supports and that are large enough.
+bool gemm8_supports(const GemmArgs& g);
+hipError_t launch_gemm8(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_fixup(const GemmArgs& g, const GemmSplit& split, hipStream_t s);
 // Floats of workspace the product's k-split tiles use (0: it splits none); shapes, layouts
 // and epilogue of g are read, its pointers are not.

@@ -86,7 +86,7 @@ static hipError_t launch_reduce_p(const ReduceArgs& a, hipStream_t s) {
   for (int p = 0; p < P; ++p) parts.p[p] = a.partials[p];
   const uint32_t groups_per_row = uint32_t(a.cols / kElems);
   const uint32_t total = uint32_t(a.rows) * groups_per_row;
-  // Enough waves to cover HBM latency: up to 8 workgroups of 256 threads per CU.
+  // One workgroup of 256 threads per CU at most (kReduceMaxBlocks).
   const uint32_t want = (total + 2 * 256 - 1) / (2 * 256);
   static_assert(int64_t(kReduceMaxBlocks) * 256 * 2 <= (int64_t(1) << 21), "grid stride within the group limit");
   const uint32_t blocks = want < uint32_t(kReduceMaxBlocks) ? (want ? want : 1u) : uint32_t(kReduceMaxBlocks);

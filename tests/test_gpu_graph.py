@@ -18,8 +18,17 @@ def replay_and_compare(graph, outputs, ref, replays=3):
         sync()
         graph.replay()
         sync()
+        diffs = []
         for name, t, r in zip(range(len(outputs)), outputs, ref):
-            assert torch.equal(t, r), f"replay {i}: output {name} differs from the eager run"
+            if not torch.equal(t, r):
+                bad = (t != r) & ~(torch.isnan(t) & torch.isnan(r))
+                rows = torch.nonzero(bad.reshape(bad.shape[0], -1).any(1)).flatten().tolist()
+                d = (t.float() - r.float()).abs().nan_to_num(float("inf"))
+                diffs.append(f"output {name}: {int(bad.sum())} elements differ (max |diff| {d.max().item():.3e}, "
+                             f"nan {int(torch.isnan(t).sum())}) in rows {rows[:8]}{'...' if len(rows) > 8 else ''}")
+        for msg in diffs:
+            print(f"  replay {i}: {msg}", flush=True)
+        assert not diffs, f"replay {i} differs from the eager run: {diffs}"
 
 
 def test_mlp_block_step_as_graph():

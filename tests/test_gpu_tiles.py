@@ -60,3 +60,49 @@ def test_256x160_tile_matches_oracle(shape, act):
     check("dX", f64(g.dX), dX, BF16_TOL)
     check("dA_s", f64(g.dA), dA, BF16_TOL)
     check("dB_s", f64(g.dB), dB, BF16_TOL)
+
+
+# Products on the eight-wave 256×256 kernel (gemm8_kernel: two ping-pong wave groups, one
+# workgroup per CU). Sizes leave ragged tiles in m (8200 rows: 32 tiles and 8 rows), n
+# (4104 hidden columns, 2056 FFN columns) and k, with at least one full round of tiles.
+# With the column split, the first chunk's reduction runs on the second stream while the
+# second chunk's input gradient runs on the eight-wave kernel: its memory traffic slows the
+# kernel's copies, which is when a copy landing late in LDS would show (it did, before the
+# kernel drained every wave's copies ahead of its epilogue).
+@pytest.mark.parametrize("act,col_chunks", [("gelu_tanh", 1), ("swiglu", 1), ("swiglu", 2)])
+def test_8wave_tile_matches_oracle(act, col_chunks):
+    h, f = 4104 if col_chunks == 1 else 4112, 2056
+    w = synth.MlpWorkload("tile8w", batch=2, seq=4100, hidden=h, ffn_shard=f, act=act, dtype="bf16",
+                          row_chunks=1, col_chunks=col_chunks, n_partials=2, backward=True, seed=57)
+    print(f"8-wave tile: act={act} T={w.tokens} h={h} f_s={f} col_chunks={col_chunks}", flush=True)
+    inp = synth.mlp_inputs(w)
+    g = MlpGroup(batch=w.batch, seq=w.seq, hidden=h, ffn_shard=f, act=act, dtype="bf16", row_chunks=1,
+                 col_chunks=col_chunks, n_partials=2, X=inp["X"], A=inp["A"], B=inp["B"], dY=inp["dY"],
+                 device=dev())
+    poison(g.Y, *g.Hpre.values(), *g.H.values(), *g.Y_own.values(), g.dX, *g.dHpre.values(),
+           *g.dX_own.values(), g.dA, g.dB)
+    g.peer_forward()
+    g.peer_backward()
+    D.domino_timing_enable(True)
+    g.forward(comm=torch.cuda.Stream())
+    g.backward(comm=torch.cuda.Stream())
+    sync()
+    kernels = {r: D.domino_timing_kernel(r) for r in ("fwd_gemm1", "dgrad_b", "dgrad_a")}
+    D.domino_timing_enable(False)
+    for role, k in kernels.items():
+        assert k.startswith("gemm8_kernel<"), (role, k)
+
+    X, A, B, dY = (oracle.to_f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    A0, B0 = oracle.mlp_shard_weights(A, B, act, 2, 0)
+    Hpre, H, Y0 = oracle.mlp_shard_forward(X, A0, B0, act)
+    check("Hpre", f64(g.Hpre[0]), Hpre, BF16_TOL)
+    check("H", f64(g.H[0]), H, BF16_TOL)
+    check("Y_own", f64(g.Y_own[0]), Y0, BF16_TOL)
+    check("Y", f64(g.Y), oracle.mlp_forward_unsharded(X, A, B, act), BF16_TOL)
+    dHpre, dX0, dA, dB = oracle.mlp_shard_backward(X, A0, B0, dY, act)
+    check("dHpre", f64(g.dHpre[0]), dHpre, BF16_TOL)
+    check("dX_own", f64(g.dX_own[0]), dX0, BF16_TOL)
+    check("dA_s", f64(g.dA), dA, BF16_TOL)
+    check("dB_s", f64(g.dB), dB, BF16_TOL)
+    check("dX", f64(g.dX), oracle.mlp_backward_unsharded(X, A, B, dY, act), BF16_TOL)
+    check("Y (chunks)", f64(g.Y), oracle.domino_mlp_forward(X, A, B, act, 2, w.batch, w.seq, 1, col_chunks), BF16_TOL)
