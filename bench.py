@@ -79,14 +79,20 @@ def parse():
                     help="run one plain device copy of this size first (for HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "COPY_MIB",
                                                            "WORKLOAD", "OUT"))
+    ap.add_argument("--traffic-workgroups", type=int, default=0,
+                    help="with --traffic-summary: only the kernel's dispatches of this many workgroups")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "OUT"),
                     help="per-kernel, per-launch-shape statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--timeline-summary", nargs=3, metavar=("TRACE_CSV", "OUT", "TITLE"),
+                    help="write one Domino step of a rocprofv3 kernel trace of this bench as a timeline")
+    ap.add_argument("--counter-summary", nargs="+", metavar="OUT TITLE CSV",
+                    help="write per-kernel averages of rocprofv3 counter runs: OUT TITLE CSV [CSV ...]")
     ap.add_argument("--trace-command", default="", help="the command that made the trace (recorded in the summary)")
     return ap.parse_args()
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_transformer_block_domino_amd", "csrc", f)
-                  for f in ("gemm_bf16.hip", "common.hpp")]
+                  for f in ("gemm_bf16.hip", "gemm8.hip", "gemm_common.hpp", "common.hpp")]
 
 
 def kernel_source_sha():
@@ -116,14 +122,17 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path):
-    """Writes the traffic summary bench reads (measured_traffic) from two counter runs."""
+def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path, workgroups=0):
+    """Writes the traffic summary bench reads (measured_traffic) from two counter runs,
+    over the kernel's dispatches of `workgroups` workgroups (all of them when 0)."""
     import csv
 
     def values(path, counter):
         out = {}
         for row in csv.DictReader(open(path)):
-            if row["Counter_Name"] == counter:
+            wgs = int(row["Grid_Size"]) // max(1, int(row["Workgroup_Size"]))
+            if row["Counter_Name"] == counter and (not workgroups or wgs == workgroups
+                                                   or "copyBuffer" in row["Kernel_Name"]):
                 out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
         return out
 
@@ -149,6 +158,7 @@ def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path):
     lines = [
         f"kernel: {kernel}",
         f"workload: {workload}",
+        f"workgroups: {workgroups or 'all launch shapes'}",
         f"kernel_source_sha256: {kernel_source_sha()}",
         f"fetch_kib_per_launch: {f_avg:.1f}",
         f"write_kib_per_launch: {w_avg:.1f}",
@@ -166,7 +176,8 @@ def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path):
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- {cmd}",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- {cmd}",
         f"#   python3 bench.py --traffic-summary <dir>/fetch_counter_collection.csv "
-        f"<dir>/write_counter_collection.csv '{kernel}' {copy_mib} {workload} <this file>",
+        f"<dir>/write_counter_collection.csv '{kernel}' {copy_mib} {workload} <this file>"
+        + (f" --traffic-workgroups {workgroups}" if workgroups else ""),
     ]
     tail = [l.rstrip("\n") for l in open(out_path) if l.startswith("algorithmic") or l.startswith("# ")
             and not l.startswith("# HBM") and not l.startswith("#   ") and not l.startswith("# Two")
@@ -206,6 +217,143 @@ def trace_summary(trace_csv, out_path, command=""):
         lines.append(f"| `{name}` | {wgs} | {thr} | {d['n']} | {d['tot'] / d['n']:.1f} | {d['min']:.1f} | "
                      f"{d['max']:.1f} | {d['tot'] * 1e-3:.3f} | {100 * d['tot'] / total:.1f} | {d['vgpr']} | "
                      f"{d['agpr']} | {d['lds']} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def timeline_summary(trace_csv, out_path, title, command=""):
+    """Writes one Domino step of a rocprofv3 kernel trace of this bench as a timeline: the
+    timed Domino steps come first in the trace, each after the cache flush (an elementwise
+    torch kernel); the step shown is the one of median length among those whose kernels ran
+    on two queues (the compute stream and the reductions' stream)."""
+    import csv
+
+    rows = []
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"].replace("domino::(anonymous namespace)::", "").replace("void ", "")
+        name = name[:name.rfind(">(") + 1] if ">(" in name else name.split("(")[0]
+        rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r.get("Queue_Id", "?"), name,
+                     int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))))
+    rows.sort()
+    flush = [i for i, r in enumerate(rows) if "elementwise" in r[3]]
+    steps = []
+    for a, b in zip(flush, flush[1:]):
+        win = rows[a + 1:b]
+        if win and len({r[2] for r in win}) > 1 and any("shard_reduce" in r[3] for r in win):
+            steps.append(win)
+        elif steps:
+            break       # the Domino phase is over
+    if not steps:
+        raise SystemExit("no Domino step found in the trace")
+    dur = lambda win: max(r[1] for r in win) - win[0][0]
+    order = sorted(range(len(steps)), key=lambda i: dur(steps[i]))
+    pick = order[len(order) // 2]
+    win = steps[pick]
+    t0 = win[0][0]
+    queues = sorted({r[2] for r in win}, key=lambda q: -sum(r[1] - r[0] for r in win if r[2] == q))
+    main_q = queues[0]
+
+    def busy(q):
+        iv = sorted((r[0], r[1]) for r in win if r[2] == q)
+        out, cur = [], None
+        for a, b in iv:
+            if cur and a <= cur[1]:
+                cur[1] = max(cur[1], b)
+            else:
+                cur = [a, b]
+                out.append(cur)
+        return out
+
+    def overlap(x, y):
+        tot = 0
+        for a, b in x:
+            for c, d in y:
+                tot += max(0, min(b, d) - max(a, c))
+        return tot
+
+    bq = {q: busy(q) for q in queues}
+    span = dur(win)
+    lines = [f"# One Domino step on the timeline ({title})", ""]
+    if command:
+        lines += ["Made by:", "", "```", command,
+                  f"python3 bench.py --timeline-summary {os.path.basename(trace_csv)} <this file> '<title>' "
+                  "--trace-command '<the line above>'", "```", ""]
+    lines += [
+        f"Step {pick + 1} of the {len(steps)} flushed Domino steps in the trace (the median length; "
+        f"lengths {dur(steps[order[0]]) / 1e3:.1f}-{dur(steps[order[-1]]) / 1e3:.1f} µs). Queue {main_q} is the "
+        "compute stream; the reductions run on the other queue.", "",
+        f"- step, first kernel start to last kernel end: {span / 1e3:.1f} µs",
+    ]
+    for q in queues:
+        b = sum(e - s for s, e in bq[q])
+        lines.append(f"- queue {q} busy: {b / 1e3:.1f} µs ({100 * b / span:.0f}% of the step)")
+    if len(queues) > 1:
+        ov = overlap(bq[queues[0]], bq[queues[1]])
+        comm = sum(e - s for s, e in bq[queues[1]])
+        lines.append(f"- reductions' queue busy while the compute queue is busy: {ov / 1e3:.1f} µs "
+                     f"({100 * ov / max(1, comm):.0f}% of its busy time)")
+    lines += ["", "| start µs | end µs | dur µs | queue | workgroups | kernel |", "|---:|---:|---:|---:|---:|---|"]
+    for s0, e0, q, name, wgs in win:
+        lines.append(f"| {(s0 - t0) / 1e3:.1f} | {(e0 - t0) / 1e3:.1f} | {(e0 - s0) / 1e3:.1f} | {q} | {wgs} | `{name}` |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:14]))
+
+
+def counter_summary(out_path, title, command, *csv_paths):
+    """Writes per-kernel averages of rocprofv3 counter runs of this bench (one line per kernel
+    and launch shape), with the clock each kernel ran at: GRBM_GUI_ACTIVE counts GPU cycles
+    summed over the 8 XCDs, so cycles / 8 / the dispatch's duration is its clock."""
+    import csv
+    import collections
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("domino::(anonymous namespace)::", "").replace("domino::", "")
+            name = name.replace("void ", "")
+            name = name[:name.rfind(">(") + 1] if ">(" in name else name.split("(")[0]
+            key = (name, int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            agg[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[key][(path, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    names = sorted({c for v in agg.values() for c in v})
+    cols = [c for c in ("MfmaUtil", "LdsUtil", "LdsBankConflict", "LdsLatency") if c in names]
+    extra = [c for c in names if c not in cols and c not in ("GRBM_GUI_ACTIVE", "TA_BUSY_avr", "TD_TD_BUSY_sum")]
+    unit = "TA_BUSY_avr" in names and "TD_TD_BUSY_sum" in names and "GRBM_GUI_ACTIVE" in names
+    lines = [f"# Hardware counters per kernel ({title})", "", "Made by:", "", "```"] + list(command.split("\n")) + [
+        f"python3 bench.py --counter-summary <this file> '<title>' <dir>/*_counter_collection.csv "
+        "--trace-command '<the lines above>'", "```", "",
+        "Averages over every dispatch of a kernel and launch shape in the command (warmup, timed, serial and "
+        "unsplit steps alike). `MfmaUtil` = MFMA-busy cycles / (active cycles × SIMDs); `LdsUtil` = LDS-busy "
+        "fraction; `LdsBankConflict` = bank-conflict cycles per LDS access cycle. The clock is GRBM_GUI_ACTIVE "
+        "/ 8 / the dispatch's duration (meaningful for dispatches of more than ~50 µs)."]
+    if unit:
+        lines += ["TA busy = TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8); TD busy = TD_TD_BUSY_sum / 256 CUs / "
+                  "(GRBM_GUI_ACTIVE / 8). TA addresses vector-memory requests (copies to LDS included), TD "
+                  "returns their data."]
+    hdr = ["kernel", "workgroups", "dispatches", "avg µs"] + (["clock GHz"] if "GRBM_GUI_ACTIVE" in names else []) \
+        + cols + (["TA busy %", "TD busy %"] if unit else []) + extra
+    lines += ["", "| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
+    order = sorted(agg, key=lambda k: -sum(dur[k].values()))
+    for key in order:
+        v = {c: sum(x) / len(x) for c, x in agg[key].items()}
+        d = list(dur[key].values())
+        us = sum(d) / len(d) / 1e3
+        n = len(d) // len(csv_paths)
+        row = [f"`{key[0]}`", str(key[1]), str(n), f"{us:.1f}"]
+        if "GRBM_GUI_ACTIVE" in names:
+            row.append(f"{v['GRBM_GUI_ACTIVE'] / 8 / (us * 1e3):.2f}" if "GRBM_GUI_ACTIVE" in v and us > 0 else "")
+        for c in cols:
+            row.append(f"{v[c]:.3f}" if c == "LdsBankConflict" else f"{v[c]:.1f}" if c in v else "")
+        if unit:
+            cyc = v.get("GRBM_GUI_ACTIVE", 0) / 8
+            row.append(f"{100 * v['TA_BUSY_avr'] / cyc:.0f}" if cyc else "")
+            row.append(f"{100 * v['TD_TD_BUSY_sum'] / 256 / cyc:.0f}" if cyc else "")
+        for c in extra:
+            row.append(f"{v[c]:.3g}" if c in v else "")
+        lines.append("| " + " | ".join(row) + " |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -755,9 +903,14 @@ def headline(args, res):
 def main():
     args = parse()
     if args.traffic_summary:
-        return traffic_summary(*args.traffic_summary)
+        return traffic_summary(*args.traffic_summary, workgroups=args.traffic_workgroups)
     if args.trace_summary:
         return trace_summary(*args.trace_summary, args.trace_command)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary[0], args.counter_summary[1], args.trace_command,
+                               *args.counter_summary[2:])
+    if args.timeline_summary:
+        return timeline_summary(*args.timeline_summary, args.trace_command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported: the library sums the "
               f"tensor-parallel partials on one GPU, with no collective between GPUs", file=sys.stderr)
