@@ -7,23 +7,41 @@
 // block with a running maximum and running sum (online softmax), so the seq×seq score
 // matrix never leaves registers.
 //
-// Design (gfx950): one workgroup = 4 waves = 128 query rows of one (sequence, head); each
-// wave owns 32 query rows. Keys advance 64 at a time; K and V blocks reach LDS through
-// buffer loads that write LDS directly, two stages deep, one barrier per block.
+// Design (gfx950): one workgroup = 8 waves = 128 query rows of one (sequence, head),
+// computed twice over: wave group 0 (waves 0-3) takes the even 64-key blocks, group 1
+// (waves 4-7) the odd ones, and each wave of a group owns 32 query rows. The two partial
+// results (O, running max, running sum) are merged at the end, through LDS. Splitting
+// the keys rather than the queries gives both groups the same number of blocks, so they
+// stay paired to the end.
+//  * Ping-pong: time step t is key block t. The group that owns block t runs its MFMAs
+//    (S_t = Q·K_tᵀ, and O += P·V of its previous block t − 2) while the other group runs
+//    the online softmax of its block t − 1 (VALU and transcendental work) and issues the
+//    copies of later blocks; a workgroup barrier ends each step. Waves w and w + 4 share a
+//    SIMD, so each SIMD always pairs one wave's MFMAs with the other wave's softmax.
+//  * K blocks sit in a ring of 4 stages and V blocks in a ring of 5 (144 KB): at the start
+//    of step t the softmax group copies K_{t+3} and V_{t+2} over K_{t−1} and V_{t−3} (which
+//    it read in its previous step) and waits for them at the end of its next softmax step,
+//    three steps ahead of their first reads. Copies issued between the MFMAs measured
+//    slower: they stall the MFMA group more than the softmax group.
 //  * S = Q·Kᵀ on 32×32×16 MFMAs with the operands swapped, so lane l holds the scores of
 //    query l%32 for keys 8j + 4·(l/32) + r (j, r = 0..3) of each 32-key block: a query's
 //    row lives in two lanes (l, l^32), and its running max and sum need one cross-lane
-//    exchange each.
+//    exchange each (v_permlane32_swap).
 //  * The exponentiated scores of a 16-key step are then already the A operand of O += P·V
 //    (keys 4·(l/32) + r and 8 + 4·(l/32) + r of the step, in that k order); the V operand
-//    reads the same keys, transposed out of LDS with ds_read_b64_tr_b16, so P never leaves
-//    registers.
+//    reads the same keys, transposed out of LDS with ds_read_b64_tr_b16, so P never goes
+//    through LDS.
 //  * Q stays in registers (read once). K is staged [key][d] with a 16-byte-chunk XOR
 //    swizzle (a fragment read, 16 keys × one chunk, hits distinct banks); V is staged
 //    [key][d] with a 32-byte-chunk swizzle for the transposed reads.
-//  * Causal balance: the first half of the grid takes query blocks longest first, the
-//    second half shortest first, so the two workgroups a CU holds at once carry the same
-//    total work.
+//  * Causal balance: query blocks are launched longest first. One workgroup fills a CU,
+//    so the second half of the grid (also longest first) lands on the CUs that finished
+//    first, and each CU's two blocks add up to about the same work.
+//  * The running maximum moves only when a block's exceeds it by more than 2^8, so O and
+//    l are rescaled rarely; fragment addresses are one XOR of a per-lane base with the
+//    fragment's index, the rest instruction immediates.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,6 +51,9 @@ namespace {
 constexpr int kD = 128;   // head_dim
 constexpr int kQB = 128;  // query rows per workgroup
 constexpr int kKB = 64;   // keys per block
+constexpr int kTile = kKB * kD;          // elements of one K or V block (16 KB)
+constexpr int kKRing = 4, kVRing = 5;    // stages of the K and V rings
+
 
 // K tile [64 keys][128 d]: 16-byte chunk c of key k at c ^ (k & 15).
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * kD + ((chunk ^ (key & 15)) << 3); }
@@ -48,21 +69,32 @@ struct AttnParams {
   float scale_log2;    // scale · log2(e)
 };
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kKB * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kKB * kD];
+// The value of lane l ^ 32 combined with lane l's: both halves of the wave get op(x[l], x[l ^ 32]).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(kKRing + kVRing) * kTile];
+  uint16_t* const sK = smem;
+  uint16_t* const sV = smem + kKRing * kTile;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, w = wave & 3;
   const int h = lane >> 5, l32 = lane & 31;
 
-  // Grid order: positions 0 .. G/2−1 longest query block first, the rest shortest first.
-  const int hb = p.heads * p.batch, G = p.nqb * hb, half = (G + 1) / 2;
+  // Longest query blocks first; (sequence, head) inner.
+  const int hb = p.heads * p.batch;
   const int lin = blockIdx.x;
-  const int srt = lin < half ? lin : G - 1 - (lin - half);
-  const int qb = p.nqb - 1 - srt / hb;
-  const int head = (srt % hb) % p.heads;
-  const int b = (srt % hb) / p.heads;
+  const int qb = p.nqb - 1 - lin / hb;
+  const int head = (lin % hb) % p.heads;
+  const int b = (lin % hb) / p.heads;
 
   const int64_t row0 = int64_t(b) * p.seq;  // first token of this sequence
   const uint16_t* Qg = p.qkv + head * kD;
@@ -73,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const int qw = q0 + w * 32;     // this wave's first query
   const int q = qw + l32;         // this lane's query
 
-  // Q fragments (A operand of S): d = 16s + 8h .. +7 of query q.
+  // Q fragments (B operand of S): d = 16s + 8h .. +7 of query q.
   u32x4_t qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -87,12 +119,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float mrun = -1e30f, lrun = 0.f;
 
-  const int q_hi = min(q0 + kQB, p.seq);   // exclusive
-  const int nkb = (q_hi + kKB - 1) / kKB;  // key blocks this workgroup needs
+  const int q_hi = min(q0 + kQB, p.seq);    // exclusive
+  const int nkb = (q_hi + kKB - 1) / kKB;   // key blocks of this query block
+  // The last key block holding a key this wave's queries see (key blocks start at multiples
+  // of 64 and waves at multiples of 32, so every query of the wave sees the first key of
+  // each block up to this one).
+  const int wlast = qw < p.seq ? min(qw + 31, p.seq - 1) / kKB : -1;
 
-  // Copies of one key block: wave w fills 1 KB pieces w, w+4, w+8, w+12 of each tile.
-  // Piece byte offset 16·(64·piece + lane) holds key (64·piece + lane)/16 and, for K,
-  // 16-byte chunk (lane & 15) ^ (key & 15); for V, 32-byte chunk ((lane & 15) >> 1) ^ 2·(key & 3).
+  // Copies of one key block by the four waves of a group: wave w fills 1 KB pieces w, w+4,
+  // w+8, w+12 of each tile. Piece byte offset 16·(64·piece + lane) holds key
+  // (64·piece + lane)/16 and, for K, 16-byte chunk (lane & 15) ^ (key & 15); for V, 32-byte
+  // chunk ((lane & 15) >> 1) ^ 2·(key & 3).
   int32_t koff[4], voff[4];
   int kkey[4];
 #pragma unroll
@@ -103,155 +140,266 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     const int c32 = (c16 >> 1) ^ ((key & 3) << 1);
     voff[i] = int32_t((int64_t(key) * p.ld_qkv + (c32 << 4) + ((c16 & 1) << 3)) * 2);
   }
-  auto issue = [&](int kb, int st) {
-    const int key0 = kb * kKB;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (row0 + key0) * p.ld_qkv);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (row0 + key0) * p.ld_qkv);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = key0 + kkey[i] < p.seq;
-      dma16(rk, &sK[st][(w + 4 * i) * 512], in ? koff[i] : kOOB);
-      dma16(rv, &sV[st][(w + 4 * i) * 512], in ? voff[i] : kOOB);
-    }
+  // Copy i (1 KB) of K or V block kb; a block past this query block's range (kb ≥ nkb)
+  // loads zeros without touching memory, so every step issues the same number of copies.
+  struct Copy {
+    __amdgpu_buffer_rsrc_t rs;
+    uint16_t* dst;
+    bool in;
+  };
+  auto copy_k = [&](int kb) {
+    return Copy{make_rsrc(Kg + (row0 + int64_t(kb) * kKB) * p.ld_qkv), sK + (kb % kKRing) * kTile, kb < nkb};
+  };
+  auto copy_v = [&](int kb) {
+    return Copy{make_rsrc(Vg + (row0 + int64_t(kb) * kKB) * p.ld_qkv), sV + (kb % kVRing) * kTile, kb < nkb};
+  };
+  auto issue_k = [&](const Copy& cp, int kb, int i) {
+    dma16(cp.rs, cp.dst + (w + 4 * i) * 512, cp.in && kb * kKB + kkey[i] < p.seq ? koff[i] : kOOB);
+  };
+  auto issue_v = [&](const Copy& cp, int kb, int i) {
+    dma16(cp.rs, cp.dst + (w + 4 * i) * 512, cp.in && kb * kKB + kkey[i] < p.seq ? voff[i] : kOOB);
   };
 
-  issue(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int st = kb & 1;
-    // Block kb has landed (the only copies in flight) and every wave is done with kb−1,
-    // whose stage the next copies overwrite.
-    wait_vm_barrier<0>();
-    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+  // LDS byte addresses of the fragment reads. A K fragment (key nb·32 + l, 16-byte chunk
+  // 2s + h) sits at key·256 + 16·((2s + h) ^ (key & 15)) = kbase ^ 32s, plus 8192·nb: kbase
+  // holds the lane's key row and, in bits 5-7 and 4, the swizzle's lane part. A V
+  // fragment (key 16u + 8·hi + 4h + k3 with k3 = (l & 15) >> 2, 32-byte chunk
+  // 2·(db ^ k3) + ((l >> 4) & 1), column 4·(l & 3) of it) sits at vbase ^ 64db, plus
+  // 4096u + 2048·hi. The per-block offsets are instruction immediates.
+  const int x15 = l32 & 15, k3 = x15 >> 2;
+  const uint32_t kbase = lds_addr(sK) + l32 * 256 + ((x15 >> 1) << 5) + (((h ^ x15) & 1) << 4);
+  const uint32_t vbase = lds_addr(sV) + (4 * h + k3) * 256 + (k3 << 6) + (((l32 >> 4) & 1) << 5) + ((x15 & 3) << 3);
 
-    const int key0 = kb * kKB;
-    if (key0 > qw + 31 || qw >= p.seq) continue;  // every key of this block is in this wave's future
+  f32x16_t sacc[2];   // S of this group's current block
+  u32x4_t pf[4];      // P of this group's previous block, bf16: four 16-key steps
+  bool p_live = false;
+  const float c = p.scale_log2;
 
-    // S = Q·Kᵀ for 32 queries × 64 keys (two 32-key blocks).
-    f32x16_t sacc[2];
+  // Prologue: K_0 .. K_2 and V_0, V_1 before the first step.
+  {
+    const int k0 = g == 0 ? 0 : 1;
+    const Copy a = copy_k(k0), bk = copy_k(2), v = copy_v(k0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
-    // LDS reads are inline assembly with explicit waits: through the builtins the
-    // compiler makes them wait for every global→LDS copy in flight (it cannot tell which
-    // LDS they write), which would serialise the next block's copies with this block.
-    // All K fragments are read before the first MFMA; the MFMAs of sub-step s wait only
-    // for the reads of fragments s (LDS reads complete in order).
-    u32x4_t kf[8][2];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) lds_read_b128(kf[s][nb], &sK[st][k_off(nb * 32 + l32, 2 * s + h)]);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      lgkm_wait_tied(14 - 2 * s, kf[s][0], kf[s][1]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s][nb]),
-                                                          __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb], 0, 0, 0);
-    }
-
-    // The V fragments do not depend on the softmax: read them now, behind it. Lane keys
-    // of step t: 16t + 4h + (0..3) and 16t + 8 + 4h + (0..3); the transposed read gives
-    // lane i of each 16-lane group column n0 + i of 4 rows.
-    u32x4_t vf[4][4];
-    {
-      const int g = lane >> 4, i16 = lane & 15;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int krow = 16 * t + 4 * h + (i16 >> 2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-          u32x2_t lo, hi;
-          lds_read_tr16_b64(lo, &sV[st][v_off(krow, d)]);
-          lds_read_tr16_b64(hi, &sV[st][v_off(krow + 8, d)]);
-          vf[t][db] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        }
-      }
-    }
-
-    // Online softmax over this block in the log2 domain, with scores scaled inside the
-    // exponent (c = scale·log2 e > 0, so max(c·s) = c·max(s)). Key key0 + 4h + off
-    // (off = 32·nb + 8j + r) is visible iff off ≤ lim; only blocks that reach the wave's
-    // diagonal (or the sequence end) are masked.
-    float mx = -1e30f;
-    if (key0 + kKB - 1 > qw || key0 + kKB > p.seq) {  // wave-uniform
-      const int lim = min(q, p.seq - 1) - key0 - 4 * h;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = nb * 32 + 8 * (e >> 2) + (e & 3);
-          sacc[nb][e] = off <= lim ? sacc[nb][e] : -INFINITY;
-        }
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[nb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float c = p.scale_log2;
-    const float mnew = fmaxf(mrun, mx * c);
-    float rs = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[nb][e], c, -mnew));
-        sacc[nb][e] = pe;
-        rs += pe;
-      }
-    rs += __shfl_xor(rs, 32);
-    // Rescale O and l only when some row's maximum grew (after the first blocks it
-    // rarely does).
-    if (__ballot(mnew > mrun)) {
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-    }
-    lrun += rs;
-    mrun = mnew;
-
-    // O += P·V over the block's 64 keys: four 16-key steps; step t = 2·nb + tt uses the
-    // scores j = 2tt, 2tt+1 of 32-key block nb. The V reads have landed behind the softmax.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(vf[t][db]));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int nb = t >> 1, tt = t & 1;
-      const u32x4_t pf = {pack_bf16x2(sacc[nb][8 * tt + 0], sacc[nb][8 * tt + 1]),
-                          pack_bf16x2(sacc[nb][8 * tt + 2], sacc[nb][8 * tt + 3]),
-                          pack_bf16x2(sacc[nb][8 * tt + 4], sacc[nb][8 * tt + 5]),
-                          pack_bf16x2(sacc[nb][8 * tt + 6], sacc[nb][8 * tt + 7])};
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[t][db]),
-                                                          __builtin_bit_cast(bf16x8_t, pf), oacc[db], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      issue_k(a, k0, i);
+      issue_v(v, k0, i);
+      if (g == 0) issue_k(bk, 2, i);
     }
   }
-  // No LDS write may land after the workgroup ends.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // O[q][d .. d+3] = O / l; lane holds d = 32·db + 8j + 4h + (0..3).
-  if (q < p.seq) {
-    // ln Σ_k exp(scale·s_k) = (m + log2 l)·ln 2 with m, l the running max and sum (log2 units).
-    if (p.lse && h == 0) p.lse[(row0 + q) * p.ld_lse + head] = (mrun + log2f(lrun)) * 0.69314718055994531f;
-    const float inv = 1.0f / lrun;
-    uint16_t* dst = p.o + (row0 + q) * p.ld_o + head * kD;
+  // Step t: the group owning block t runs mma_step(t), the other softmax_step(t). Each
+  // group's steps alternate, so each group's loop is written with its two kinds of step in
+  // order (the compiler then sees that S and P are never live at once), and every wave
+  // passes the same barriers.
+  auto mma_step = [&](int t) {
+    // MFMA step of block t (this group's): O += P·V of block t − 2 (P dies before S_t
+    // is born, so the two never hold registers at once), then S_t.
+    if (p_live) {
+      const uint32_t vb = vbase + uint32_t(((t - 2) % kVRing) * kTile * 2);
+      uint32_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[db] = vb ^ uint32_t(db << 6);
+      // V fragments two 16-key steps ahead (eight reads per step).
+      u32x4_t vf[4][4];
+      auto read_v = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          u32x2_t lo, hi;
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(va[db]), "n"(4096 * u));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(va[db]), "n"(4096 * u + 2048));
+          vf[u][db] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+      };
+      read_v(std::integral_constant<int, 0>{});
+      read_v(std::integral_constant<int, 1>{});
+      auto pv = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u < 3) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(vf[u][db]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[u][db]),
+                                                            __builtin_bit_cast(bf16x8_t, pf[u]), oacc[db], 0, 0, 0);
+        if constexpr (u < 2) read_v(std::integral_constant<int, u + 2>{});
+      };
+      pv(std::integral_constant<int, 0>{});
+      pv(std::integral_constant<int, 1>{});
+      pv(std::integral_constant<int, 2>{});
+      pv(std::integral_constant<int, 3>{});
+    }
+    if (t < nkb && t <= wlast) {
+      const uint32_t kb0 = kbase + uint32_t((t % kKRing) * kTile * 2);
+      // K fragments four sub-steps ahead: sub-step s + 4 is read once the MFMAs of s are
+      // issued, so at most four sub-steps' registers are live.
+      u32x4_t kf[8][2];
+      auto read_k = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        const uint32_t a = kb0 ^ uint32_t(s << 5);
+        u32x4_t r0, r1;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(r0) : "v"(a));
+        asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(r1) : "v"(a));
+        kf[s][0] = r0;
+        kf[s][1] = r1;
+      };
+      read_k(std::integral_constant<int, 0>{});
+      read_k(std::integral_constant<int, 1>{});
+      read_k(std::integral_constant<int, 2>{});
+      read_k(std::integral_constant<int, 3>{});
+      auto qk = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        lgkm_wait_tied(s < 4 ? 6 : 14 - 2 * s, kf[s][0], kf[s][1]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          sacc[nb] = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s][nb]),
+                                                                     __builtin_bit_cast(bf16x8_t, qf[s]),
+                                                                     f32x16_t{}, 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s][nb]),
+                                                                     __builtin_bit_cast(bf16x8_t, qf[s]), sacc[nb],
+                                                                     0, 0, 0);
+        if constexpr (s < 4) read_k(std::integral_constant<int, s + 4>{});
+      };
+      qk(std::integral_constant<int, 0>{});
+      qk(std::integral_constant<int, 1>{});
+      qk(std::integral_constant<int, 2>{});
+      qk(std::integral_constant<int, 3>{});
+      qk(std::integral_constant<int, 4>{});
+      qk(std::integral_constant<int, 5>{});
+      qk(std::integral_constant<int, 6>{});
+      qk(std::integral_constant<int, 7>{});
+    }
+  };
+  auto softmax_step = [&](int t) {
+    // Softmax step of block j = t − 1 (this group's). First the copies of K_{t+3} and
+    // V_{t+2} (over K_{t−1} and V_{t−3}, which this group read in its previous step); this
+    // group waits for them at the end of its next softmax step, before K_{t+3} is read.
+    {
+      const Copy ck = copy_k(t + 3), cv = copy_v(t + 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        issue_k(ck, t + 3, i);
+        issue_v(cv, t + 2, i);
+      }
+    }
+    const int j = t - 1;
+    p_live = j >= 0 && j < nkb && j <= wlast;
+    if (p_live) {
+      // Online softmax in the log2 domain, scores scaled inside the exponent (c > 0, so
+      // max(c·s) = c·max(s)). Key key0 + 4h + off (off = 32·nb + 8e' + r) is visible iff
+      // off ≤ lim; only blocks that reach the wave's diagonal (or the sequence end) are
+      // masked.
+      const int key0 = j * kKB;
+      if (key0 + kKB - 1 > qw || key0 + kKB > p.seq) {  // wave-uniform
+        const int lim = min(q, p.seq - 1) - key0 - 4 * h;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int off = nb * 32 + 8 * (e >> 2) + (e & 3);
+            sacc[nb][e] = off <= lim ? sacc[nb][e] : -INFINITY;
+          }
+      }
+      float mx0 = -1e30f, mx1 = -1e30f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        mx0 = fmaxf(mx0, sacc[0][e]);
+        mx1 = fmaxf(mx1, sacc[1][e]);
+      }
+      const float bmax = xor32_max(fmaxf(mx0, mx1)) * c;
+      // The running maximum moves only when the block's exceeds it by more than 2^8 (the
+      // exponentials stay ≤ 256, exact in fp32 and as precise in bf16); O and l are
+      // rescaled only then. The group's first block sets it.
+      const bool first = j == g;
+      const float mnew = first || bmax > mrun + 8.0f ? fmaxf(mrun, bmax) : mrun;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int nb = qq >> 1;
+#pragma unroll
+        for (int e = 8 * (qq & 1); e < 8 * (qq & 1) + 8; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[nb][e], c, -mnew));
+          sacc[nb][e] = pe;
+          rs[e & 3] += pe;
+        }
+      }
+      const float bsum = xor32_sum((rs[0] + rs[1]) + (rs[2] + rs[3]));
+      if (!first && __ballot(mnew != mrun)) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        lrun *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
+      lrun += bsum;
+      mrun = mnew;
+      // 16-key step u = 2·nb + uu uses the scores e = 8uu .. 8uu + 7 of 32-key block nb.
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int nb = u >> 1, uu = u & 1;
+        pf[u] = u32x4_t{pack_bf16x2(sacc[nb][8 * uu + 0], sacc[nb][8 * uu + 1]),
+                        pack_bf16x2(sacc[nb][8 * uu + 2], sacc[nb][8 * uu + 3]),
+                        pack_bf16x2(sacc[nb][8 * uu + 4], sacc[nb][8 * uu + 5]),
+                        pack_bf16x2(sacc[nb][8 * uu + 6], sacc[nb][8 * uu + 7])};
+      }
+    }
+    // The copies of step t − 2 have landed (this step's eight are the only ones newer).
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  };
+  const int pairs = (nkb + 3) / 2;   // steps 0 .. nkb + 1, two per iteration
+  if (g == 0) {
+    for (int i = 0; i < pairs; ++i) {
+      mma_step(2 * i);
+      asm volatile("s_barrier" ::: "memory");
+      softmax_step(2 * i + 1);
+      asm volatile("s_barrier" ::: "memory");
+    }
+  } else {
+    for (int i = 0; i < pairs; ++i) {
+      softmax_step(2 * i);
+      asm volatile("s_barrier" ::: "memory");
+      mma_step(2 * i + 1);
+      asm volatile("s_barrier" ::: "memory");
+    }
+  }
+  // The last copies (zeros past the range) land before the rings are reused below.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Merge the two groups' partial results (every copy has landed and every LDS read of
+  // the rings is done). Group 1 stages O (fp32, lane-major 16-byte pieces), m and l.
+  float* const stO = reinterpret_cast<float*>(smem) + w * (64 * 64);
+  float* const stM = reinterpret_cast<float*>(smem) + 4 * 64 * 64 + w * 128;
+  if (g == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t v = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
-                           oacc[db][4 * j + 3] * inv};
-        *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * j + 4 * h) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4_t*>(stO + ((db * 4 + jj) * 64 + lane) * 4) =
+            f32x4_t{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+    stM[lane] = mrun;
+    stM[64 + lane] = lrun;
   }
+  __syncthreads();
+  if (g == 1 || q >= p.seq) return;
+  const float m1 = stM[lane], l1 = stM[64 + lane];
+  const float m = fmaxf(mrun, m1);
+  const float a0 = __builtin_amdgcn_exp2f(mrun - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+  const float l = a0 * lrun + a1 * l1;
+  // ln Σ_k exp(scale·s_k) = (m + log2 l)·ln 2 with m, l the merged max and sum (log2 units).
+  if (p.lse && h == 0) p.lse[(row0 + q) * p.ld_lse + head] = (m + log2f(l)) * 0.69314718055994531f;
+  const float inv = 1.0f / l, b0 = a0 * inv, b1 = a1 * inv;
+  // O[q][d .. d+3]; lane holds d = 32·db + 8·jj + 4h + (0..3).
+  uint16_t* dst = p.o + (row0 + q) * p.ld_o + head * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(stO + ((db * 4 + jj) * 64 + lane) * 4);
+      const float v0 = oacc[db][4 * jj] * b0 + o1.x * b1, v1 = oacc[db][4 * jj + 1] * b0 + o1.y * b1;
+      const float v2 = oacc[db][4 * jj + 2] * b0 + o1.z * b1, v3 = oacc[db][4 * jj + 3] * b0 + o1.w * b1;
+      *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * jj + 4 * h) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+    }
 }
 
 }  // namespace
@@ -273,7 +421,7 @@ hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   const int blocks = p.nqb * p.heads * p.batch;
   note_kernel("attn_fwd_kernel");
-  DOMINO_LAUNCH(attn_fwd_kernel, dim3(blocks), dim3(256), 0, s, p);
+  DOMINO_LAUNCH(attn_fwd_kernel, dim3(blocks), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
