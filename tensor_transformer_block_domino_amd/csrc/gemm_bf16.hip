@@ -522,12 +522,17 @@ bool one_round_256x160(const GemmArgs& g, bool sw) {
 // gradient, when their 256×256 tiles fill at least one round of the CUs. Measured on the
 // Llama-2-13B shard (products alone): GEMM1 1040–1080 vs 1029 TFLOP/s, activation
 // gradient 890–905 vs ~710, input gradient 1180–1200 vs ~1100 for the four-wave kernels.
-// The second product (its B operand n-major, k = the FFN width) runs 5–10% faster on the
-// four-wave 128×256 tiles, and the weight gradients (both operands m/n-major, read
-// transposed) 20–50% faster on the four-wave kernels' k-split.
+// Products with a plain store and an n-major B (the second MLP product, the attention's
+// output projection) take it when at least 2048 wide: alone they run 5–10% faster on the
+// four-wave 128×256 tiles, but those leave no room on a CU for a reduction wave beside
+// them (2·224 of 512 VGPRs), and in the step they run beside reductions (Llama-2-13B GEMM2
+// chunks 0.86 vs 0.89 ms per step, the attention's output projection 137 vs 191 µs);
+// the 1536-wide QKV product runs alone and stays on the four-wave tiles (5% faster). The
+// weight gradients (both operands m/n-major, read transposed) run 20–50% faster on the
+// four-wave kernels' k-split.
 bool use_gemm8(const GemmArgs& g) {
   if (g.epi == Epi::kF32 || !gemm8_supports(g)) return false;
-  if (g.epi == Epi::kStore && !g.b_kcontig) return false;
+  if (g.epi == Epi::kStore && !g.b_kcontig && g.N < 2048) return false;
   const int64_t bn = g.epi == Epi::kSwiglu ? 128 : 256;
   const int64_t tiles = ((g.M + 255) / 256) * ((g.N + bn - 1) / bn);
   return tiles >= kCUs;

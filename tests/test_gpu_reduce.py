@@ -66,3 +66,29 @@ def test_shard_reduce_empty_is_noop():
     D.shard_reduce(x, 8, [x, x], 8, 4, 0, D.DOMINO_BF16)
     sync()
     assert (f64(x) == 3.0).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shard_reduce_large_matches_small_launches(dtype):
+    # At least 2^25 elements: the launch takes the buffer-load kernel (one 32-bit offset per
+    # group shared by the partials); a slab of the same rows reduced on its own (below that
+    # size) takes the 64-bit kernel. Both sum in the same order: bit-identical. Sampled rows
+    # are also checked against the oracle. Ragged rows, padded leading dimensions.
+    d = dev()
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    P, rows, cols, ld_in, ld_out = 8, 8195, 4096, 4104, 4112
+    print(f"shard_reduce large P={P} dtype={dtype} rows={rows} cols={cols}", flush=True)
+    parts = [synth.randn((rows, ld_in), seed=700 + p, dtype=dtype).to(d) for p in range(P)]
+    out = torch.full((rows, ld_out), float("nan"), dtype=td, device=d)
+    code = D.DOMINO_BF16 if dtype == "bf16" else D.DOMINO_F32
+    D.shard_reduce(out, ld_out, parts, ld_in, rows, cols, code)
+    r0, n = 4001, 1000
+    slab = torch.full((n, ld_out), float("nan"), dtype=td, device=d)
+    D.shard_reduce(slab, ld_out, [p[r0:] for p in parts], ld_in, n, cols, code)
+    sync()
+    assert torch.equal(out[r0:r0 + n, :cols].view(torch.int16 if dtype == "bf16" else torch.int32),
+                       slab[:, :cols].view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.isnan(out[:, cols:]).all()
+    sample = [0, 1, 4095, 8194]
+    ref = oracle.shard_sum([f64(p[sample])[:, :cols] for p in parts])
+    check("large (sampled rows)", f64(out[sample])[:, :cols], ref, BF16_TOL if dtype == "bf16" else F32_TOL)
