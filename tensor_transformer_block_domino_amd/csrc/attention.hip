@@ -175,18 +175,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
   bool p_live = false;
   const float c = p.scale_log2;
 
-  // Prologue: K_0 .. K_2 and V_0, V_1 before the first step.
+  // Prologue: K_0 .. K_2 and V_0, V_1, each group first the K block it reads first.
+  // Group 0 reads K_0 in step 0: its copies land once at most the eight later ones are in
+  // flight. Everything else lands by the end of the issuing group's first softmax step
+  // (all but that step's own eight copies), before anything reads it.
   {
     const int k0 = g == 0 ? 0 : 1;
     const Copy a = copy_k(k0), bk = copy_k(2), v = copy_v(k0);
 #pragma unroll
+    for (int i = 0; i < 4; ++i) issue_k(a, k0, i);
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      issue_k(a, k0, i);
       issue_v(v, k0, i);
       if (g == 0) issue_k(bk, 2, i);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (g == 0) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
 
   // Step t: the group owning block t runs mma_step(t), the other softmax_step(t). Each
   // group's steps alternate, so each group's loop is written with its two kinds of step in
