@@ -34,9 +34,9 @@
 //  * Q stays in registers (read once). K is staged [key][d] with a 16-byte-chunk XOR
 //    swizzle (a fragment read, 16 keys × one chunk, hits distinct banks); V is staged
 //    [key][d] with a 32-byte-chunk swizzle for the transposed reads.
-//  * Causal balance: query blocks are launched longest first. One workgroup fills a CU,
-//    so the second half of the grid (also longest first) lands on the CUs that finished
-//    first, and each CU's two blocks add up to about the same work.
+//  * Causal balance: a workgroup (one per CU) takes the k-th longest and then the k-th
+//    shortest query block of one (sequence, head), so all carry about the same work and
+//    no CU waits between two workgroups.
 //  * The running maximum moves only when a block's exceeds it by more than 2^8, so O and
 //    l are rescaled rarely; fragment addresses are one XOR of a per-lane base with the
 //    fragment's index, the rest instruction immediates.
@@ -89,10 +89,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
   const int g = wave >> 2, w = wave & 3;
   const int h = lane >> 5, l32 = lane & 31;
 
-  // Longest query blocks first; (sequence, head) inner.
+  // Two query blocks of one (sequence, head) per workgroup in turn, the k-th longest and
+  // the k-th shortest (only the middle one when they meet), so every workgroup carries
+  // about the same work and no CU waits for a second workgroup to be dispatched.
   const int hb = p.heads * p.batch;
   const int lin = blockIdx.x;
-  const int qb = p.nqb - 1 - lin / hb;
+  const int kpair = lin / hb;
   const int head = (lin % hb) % p.heads;
   const int b = (lin % hb) / p.heads;
 
@@ -101,6 +103,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
   const uint16_t* Kg = p.qkv + p.hd + head * kD;
   const uint16_t* Vg = p.qkv + 2 * p.hd + head * kD;
 
+  // One query block, start to finish (inlined once per block of the pair).
+  auto run_block = [&](const int qb) {
   const int q0 = qb * kQB;
   const int qw = q0 + w * 32;     // this wave's first query
   const int q = qw + l32;         // this lane's query
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
     stM[64 + lane] = lrun;
   }
   __syncthreads();
-  if (g == 1 || q >= p.seq) return;
+  if (g == 0 && q < p.seq) {
   const float m1 = stM[lane], l1 = stM[64 + lane];
   const float m = fmaxf(mrun, m1);
   const float a0 = __builtin_amdgcn_exp2f(mrun - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
@@ -405,6 +409,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnParams p) {
       const float v2 = oacc[db][4 * jj + 2] * b0 + o1.z * b1, v3 = oacc[db][4 * jj + 3] * b0 + o1.w * b1;
       *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * jj + 4 * h) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
     }
+  }
+  };
+  run_block(p.nqb - 1 - kpair);
+  if (p.nqb - 1 - kpair != kpair) {
+    // The staged partials are read before the next block's copies overwrite them.
+    __syncthreads();
+    run_block(kpair);
+  }
 }
 
 }  // namespace
@@ -424,7 +436,7 @@ hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.nqb = int((a.seq + kQB - 1) / kQB);
   p.hd = a.heads * a.head_dim;
   p.scale_log2 = a.scale * 1.4426950408889634f;
-  const int blocks = p.nqb * p.heads * p.batch;
+  const int blocks = (p.nqb + 1) / 2 * p.heads * p.batch;
   note_kernel("attn_fwd_kernel");
   DOMINO_LAUNCH(attn_fwd_kernel, dim3(blocks), dim3(512), 0, s, p);
   return hipGetLastError();
