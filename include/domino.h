@@ -140,7 +140,13 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
  *   peer_Y  HOST array of n_partials-1 device pointers [T, hidden]      (inputs; NULL if P==1)
  *   Y [T, hidden]                      reduced output; NULL or Y_own reduces in place into
  *                                      Y_own (with P == 1 that means no reduction runs)
- *   workspace, workspace_bytes         optional device scratch (see Workspace above)
+ *   workspace, workspace_bytes         optional device scratch (see Workspace above). In bf16,
+ *                                      when the first product runs on the large-tile kernel
+ *                                      and the workspace holds domino_block_fwd_workspace_size
+ *                                      bytes, its front first receives transposed copies of A_s
+ *                                      and B_s, which both products then read contiguous along
+ *                                      k (the same values in the same order: the outputs equal
+ *                                      those without a workspace bit for bit).
  */
 domino_status domino_block_fwd(const domino_mlp_desc* desc, const void* X, const void* A_s, const void* B_s,
                                const void* b1_s, void* Hpre, void* H, void* Y_own, const void* const* peer_Y, void* Y,
@@ -449,7 +455,8 @@ typedef enum {
   DOMINO_K_QKV = 7,
   DOMINO_K_ATTN = 8,
   DOMINO_K_OUTPROJ = 9,
-  DOMINO_K_AUX = 10,        /* k-split tiles' fixed-order slice sums with their epilogues */
+  DOMINO_K_AUX = 10,        /* k-split tiles' fixed-order slice sums with their epilogues; the
+                               MLP forward's transposed weight copies */
   DOMINO_K_ATTN_BWD = 11,   /* attention backward: the dK/dV kernel */
   DOMINO_K_OUTPROJ_DGRAD = 12,  /* dY·B_o_sᵀ */
   DOMINO_K_QKV_DGRAD = 13,  /* dQKV·A_qkv_sᵀ */

@@ -383,6 +383,27 @@ GemmArgs mlp_gemm1(const domino_mlp_desc* d, const void* X, const void* A_s, voi
   g.epi = d->act == DOMINO_ACT_SWIGLU ? Epi::kSwiglu : Epi::kGelu;
   return g;
 }
+// The same two products reading transposed weight copies (A_sT [n1, h], B_sT [h, f_s]),
+// contiguous along k.
+GemmArgs mlp_gemm1_t(const domino_mlp_desc* d, const void* X, const void* A_sT, void* Hpre, void* H) {
+  GemmArgs g = mlp_gemm1(d, X, A_sT, Hpre, H);
+  g.ldb = d->hidden; g.b_kcontig = true;
+  return g;
+}
+GemmArgs mlp_gemm2_t(const domino_mlp_desc* d, const void* H, const void* B_sT, void* Y_own, int i, int j) {
+  const int64_t h = d->hidden, f = d->ffn_shard, Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
+  GemmArgs g = gemm_base(Tc, hc, f, true);
+  g.A = at(H, i * Tc * f, 2); g.lda = f; g.a_kcontig = true;
+  g.B = at(B_sT, j * hc * f, 2); g.ldb = f; g.b_kcontig = true;
+  g.C = at(Y_own, i * Tc * h + j * hc, 2); g.ldc = h;
+  g.epi = Epi::kStore;
+  return g;
+}
+// Bytes of the transposed weight copies at the front of the forward's workspace.
+size_t mlp_wt_bytes(const domino_mlp_desc* d) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  return up(size_t(mlp_n1(d)) * d->hidden * 2) + up(size_t(d->ffn_shard) * d->hidden * 2);
+}
 // Y_own chunk (i, j) = H[rows_i]·B_s[:, cols_j].
 GemmArgs mlp_gemm2(const domino_mlp_desc* d, const void* H, const void* B_s, void* Y_own, int i, int j) {
   const int64_t h = d->hidden, f = d->ffn_shard, Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
@@ -603,9 +624,24 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
   return DOMINO_OK;
 }
 
+// Whether the forward transposes the weights (bf16, and the first product then runs on
+// the eight-wave kernel, which takes the activations' k-contiguous weight operand).
+bool mlp_fwd_transposed(const domino_mlp_desc* d) {
+  return d->dtype == DOMINO_BF16 && d->ffn_shard > 0 && d->batch * d->seq > 0 &&
+         use_gemm8(mlp_gemm1_t(d, nullptr, nullptr, nullptr, nullptr));
+}
+size_t mlp_fwd_ws_plain(const domino_mlp_desc* d) {
+  return ws_bytes_of({mlp_gemm1(d, nullptr, nullptr, nullptr, nullptr), mlp_gemm2(d, nullptr, nullptr, nullptr, 0, 0)});
+}
+size_t mlp_fwd_ws_transposed(const domino_mlp_desc* d) {
+  return mlp_wt_bytes(d) + ws_bytes_of({mlp_gemm1_t(d, nullptr, nullptr, nullptr, nullptr),
+                                        mlp_gemm2_t(d, nullptr, nullptr, nullptr, 0, 0)});
+}
+
 size_t domino_block_fwd_workspace_size(const domino_mlp_desc* d) {
   if (check_mlp_desc(d) != DOMINO_OK) return 0;
-  return ws_bytes_of({mlp_gemm1(d, nullptr, nullptr, nullptr, nullptr), mlp_gemm2(d, nullptr, nullptr, nullptr, 0, 0)});
+  const size_t plain = mlp_fwd_ws_plain(d);
+  return mlp_fwd_transposed(d) ? std::max(plain, mlp_fwd_ws_transposed(d)) : plain;
 }
 
 domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const void* A_s, const void* B_s,
@@ -628,18 +664,32 @@ domino_status domino_block_fwd(const domino_mlp_desc* d, const void* X, const vo
   if ((st = make_sched(compute, comm, &sc)) != DOMINO_OK) return st;
 
   const int64_t Tc = (d->batch / d->row_chunks) * d->seq, hc = h / d->col_chunks;
-  GemmArgs g1 = mlp_gemm1(d, X, A_s, Hpre, H);
-  g1.bias = b1_s;
   std::string msg;
+  // With room in the workspace (bf16), the weights are first copied transposed to its
+  // front, so both products read them contiguous along k; the rest of the workspace serves
+  // the products' k-split slices.
+  const bool tw = workspace && mlp_fwd_transposed(d) && workspace_bytes >= mlp_fwd_ws_transposed(d);
+  const size_t wt = tw ? mlp_wt_bytes(d) : 0;
+  void* const A_sT = workspace;
+  void* const B_sT = tw ? at(workspace, int64_t((size_t(mlp_n1(d)) * h * 2 + 255) / 256 * 256), 1) : nullptr;
+  void* const ws = tw ? at(workspace, int64_t(wt), 1) : workspace;
+  const size_t ws_bytes = workspace_bytes - wt;
+  if (tw && hip_ok(timed(DOMINO_K_AUX, sc.cs, [&] {
+                     hipError_t e = launch_transpose_bf16(A_s, mlp_n1(d), A_sT, h, h, mlp_n1(d), sc.cs);
+                     return e == hipSuccess ? launch_transpose_bf16(B_s, h, B_sT, f, f, h, sc.cs) : e;
+                   }), &msg, "weight transposes"))
+    return fail(DOMINO_ERR_HIP, msg);
+  GemmArgs g1 = tw ? mlp_gemm1_t(d, X, A_sT, Hpre, H) : mlp_gemm1(d, X, A_s, Hpre, H);
+  g1.bias = b1_s;
   // The first product (column-parallel, activation fused) feeds no reduction, so it runs
   // once over all rows: chunking it would only narrow the GEMM. The second product is
   // launched per Domino chunk, and each chunk's reduction starts as soon as it ends.
-  if (f > 0 && hip_ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, workspace, workspace_bytes, sc.cs), &msg, "GEMM1"))
+  if (f > 0 && hip_ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, ws, ws_bytes, sc.cs), &msg, "GEMM1"))
     return fail(DOMINO_ERR_HIP, msg);
   for (int i = 0; i < d->row_chunks; ++i) {
     for (int j = 0; j < d->col_chunks; ++j) {
-      if (hip_ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(d, H, B_s, Y_own, i, j), workspace, workspace_bytes, sc.cs),
-                 &msg, "GEMM2"))
+      const GemmArgs g2 = tw ? mlp_gemm2_t(d, H, B_sT, Y_own, i, j) : mlp_gemm2(d, H, B_s, Y_own, i, j);
+      if (hip_ok(run_gemm(DOMINO_K_FWD_GEMM2, g2, ws, ws_bytes, sc.cs), &msg, "GEMM2"))
         return fail(DOMINO_ERR_HIP, msg);
       if (red && hip_ok(sc.reduce(Y ? Y : Y_own, Y_own, peer_Y, d->n_partials, h, i * Tc * h + j * hc, Tc, hc, d->dtype),
                         &msg, "reduce Y"))

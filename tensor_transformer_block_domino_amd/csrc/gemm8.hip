@@ -48,7 +48,7 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
   constexpr int TM = 2, TN = 4;  // 32×32 blocks per wave
   constexpr bool kSw = kEpi == Epi::kSwiglu;
   using OA = typename std::conditional<kAK, OpK<BM, BK>, OpMN<BM, BK, false>>::type;
-  using OB = typename std::conditional<kBKc, OpK<BN, BK>, OpMN<BN, BK, kSw>>::type;
+  using OB = typename std::conditional<kBKc, OpK<BN, BK, kSw>, OpMN<BN, BK, kSw>>::type;
   static_assert(OA::kLoads == 4 && OB::kLoads == 4, "four 1 KB copies per wave per step");
   constexpr int kLoads = 4;
   constexpr int kStage = (BM + BN) * BK;  // bf16 elements per stage (32 KB)
@@ -258,7 +258,7 @@ bool gemm8_supports(const GemmArgs& g) {
   switch (g.epi) {
     case Epi::kStore: return ak;
     case Epi::kGelu:
-    case Epi::kSwiglu: return ak && !bk;
+    case Epi::kSwiglu: return ak;
     case Epi::kDGelu:
     case Epi::kDSwiglu: return ak && bk;
     case Epi::kF32: return !ak && !bk;
@@ -293,9 +293,11 @@ hipError_t launch_gemm8(const GemmArgs& g, hipStream_t s) {
       break;
     case Epi::kGelu:
       if (ak && !bk) return launch8<true, false, Epi::kGelu>(kp, blocks, s);
+      if (ak && bk) return launch8<true, true, Epi::kGelu>(kp, blocks, s);
       break;
     case Epi::kSwiglu:
       if (ak && !bk) return launch8<true, false, Epi::kSwiglu>(kp, blocks, s);
+      if (ak && bk) return launch8<true, true, Epi::kSwiglu>(kp, blocks, s);
       break;
     case Epi::kDGelu:
       if (ak && bk) return launch8<true, true, Epi::kDGelu>(kp, blocks, s);

@@ -530,7 +530,7 @@ bool one_round_256x160(const GemmArgs& g, bool sw) {
 // the 1536-wide QKV product runs alone and stays on the four-wave tiles (5% faster). The
 // weight gradients (both operands m/n-major, read transposed) run 20–50% faster on the
 // four-wave kernels' k-split.
-bool use_gemm8(const GemmArgs& g) {
+bool pick_gemm8(const GemmArgs& g) {
   if (g.epi == Epi::kF32 || !gemm8_supports(g)) return false;
   if (g.epi == Epi::kStore && !g.b_kcontig && g.N < 2048) return false;
   const int64_t bn = g.epi == Epi::kSwiglu ? 128 : 256;
@@ -630,11 +630,13 @@ Plan plan_for(const GemmArgs& g) {
 
 }  // namespace
 
+bool use_gemm8(const GemmArgs& g) { return pick_gemm8(g); }
+
 int64_t gemm_bf16_ws_elems(const GemmArgs& g) { return use_gemm8(g) ? 0 : make_plan(g).ws_elems; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, GemmSplit* split) {
   if (split) *split = GemmSplit{};
-  if (use_gemm8(g)) return launch_gemm8(g, s);
+  if (pick_gemm8(g)) return launch_gemm8(g, s);
   const Plan pl = plan_for(g);
   const KParams kp = make_params(g, pl);
   const int tiles = pl.tiles_m * pl.tiles_n;

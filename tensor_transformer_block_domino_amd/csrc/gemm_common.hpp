@@ -45,7 +45,7 @@ __device__ __forceinline__ int64_t map_row(const RowMap& m, int r) {
 // [R rows][BK k]: CPR 16-byte chunks per row, chunk c of row r stored at c ^ f(r), which
 // keeps a fragment read (16 consecutive rows, same chunk) on distinct banks of the
 // 64-bank LDS (and of a 32-bank one, 8 rows at a time).
-template <int R, int BK>
+template <int R, int BK, bool kSw = false>
 struct OpK {
   static constexpr int CPR = BK / 8;
   static constexpr int kLoads = R * BK / 2048;  // 1 KB instructions per wave per stage
@@ -63,7 +63,13 @@ struct OpK {
     for (int q = 0; q < kLoads; ++q) {
       const int idx = (wave + 4 * q) * 64 + lane, row = idx / CPR, c = (idx % CPR) ^ f(row);
       kc[q] = c * 8;
-      voff[q] = map_row<false, R>(rm, row) >= 0 ? int32_t((row * ld + c * 8) * 2) : kOOB;
+      if constexpr (kSw) {
+        // Tile row r holds the gate or up row of output column pair map_row<true>(r).
+        const int64_t g = map_row<true, R>(rm, row);
+        voff[q] = g >= 0 ? int32_t(((g - rm.base) * ld + c * 8) * 2) : kOOB;
+      } else {
+        voff[q] = map_row<false, R>(rm, row) >= 0 ? int32_t((row * ld + c * 8) * 2) : kOOB;
+      }
     }
   }
   // The copies of one stage: a buffer resource at k0 and the k left, then kLoads 1 KB

@@ -87,6 +87,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, GemmSplit* split);
 // The eight-wave 256×256 kernel on whole tiles (gemm8.hip); launch_gemm picks it for the
 // products it supports and that are large enough.
 bool gemm8_supports(const GemmArgs& g);
+// Whether launch_gemm_bf16 runs this product on the eight-wave kernel.
+bool use_gemm8(const GemmArgs& g);
+// dst[c][r] = src[r][c] for a bf16 [rows, cols] matrix (rows, cols multiples of 8).
+hipError_t launch_transpose_bf16(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t rows,
+                                 int64_t cols, hipStream_t s);
 hipError_t launch_gemm8(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_fixup(const GemmArgs& g, const GemmSplit& split, hipStream_t s);
 // Floats of workspace the product's k-split tiles use (0: it splits none); shapes, layouts

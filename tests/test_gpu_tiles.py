@@ -106,3 +106,13 @@ def test_8wave_tile_matches_oracle(act, col_chunks):
     check("dB_s", f64(g.dB), dB, BF16_TOL)
     check("dX", f64(g.dX), oracle.mlp_backward_unsharded(X, A, B, dY, act), BF16_TOL)
     check("Y (chunks)", f64(g.Y), oracle.domino_mlp_forward(X, A, B, act, 2, w.batch, w.seq, 1, col_chunks), BF16_TOL)
+    # With its workspace the forward read the weights through transposed copies (contiguous
+    # along k); without one it reads them as given. Same values in the same order: the
+    # outputs agree bit for bit.
+    Hp, Hh, Yo = (torch.empty_like(t) for t in (g.Hpre[0], g.H[0], g.Y_own[0]))
+    d = g.desc(rank_alone=True)
+    assert D.domino_block_fwd_workspace_size(d) <= g.ws_bytes
+    D.domino_block_fwd(d, g.X, g.A_s[0], g.B_s[0], Hp, Hh, Yo, None, None)
+    sync()
+    for name, a, b in (("Hpre", Hp, g.Hpre[0]), ("H", Hh, g.H[0]), ("Y_own", Yo, g.Y_own[0])):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
