@@ -314,16 +314,19 @@ size_t domino_resid_ln_bwd_workspace_size(const domino_group_desc* desc);
  *   y_mlp = Σ_ranks MLP_s(m);  x_next = h + dropout(y_mlp + b_2)
  * (Attn_s: QKV product, causal attention over the rank's heads, out-projection; MLP_s: GEMM
  * with the activation epilogue, GEMM; Σ_ranks: the own partial plus the P-1 peer partials,
- * the AllReduce's sum). The rows are split into row_chunks μ-batches of whole sequences and
- * issued on `compute` in the order
- *   for each μ: the closing group of the previous layer fused with LN1 (it waits for that
- *               layer's MLP reduction of μ), the attention of μ, then its reduction on `comm`;
- *   for each μ: wait for the attention reduction of μ; dropout + residual + LN2 of μ; the MLP
- *               of μ, then its reduction on `comm`;
- * so the reduction of one μ-batch's attention hides behind the next μ-batch's attention and
- * the small kernels, an MLP reduction behind the next μ-batch's MLP, and a layer's last MLP
- * reduction behind the next layer's first attention. After the last layer the closing group
- * writes `out` per μ. comm NULL (or == compute): everything in order on `compute`.
+ * the AllReduce's sum). The rows are split into row_chunks μ-batches of whole sequences. Per
+ * layer the work forms blocks: the attention block of each μ, then the MLP block of each μ;
+ * a block is its group kernel (the closing group of the previous layer fused with LN1, which
+ * waits for that layer's MLP reduction of μ; or dropout + residual + LN2, which waits for the
+ * attention reduction of μ), its products (QKV product, attention, out-projection; or GEMM1,
+ * GEMM2) and the reduction its last product starts on `comm`. So the reduction of one
+ * μ-batch's attention hides behind the next μ-batch's attention, an MLP reduction behind the
+ * next μ-batch's MLP, and a layer's last MLP reduction behind the next layer's first
+ * attention. With row_chunks >= 2 each block's group kernel is issued on `compute` before the
+ * previous block's last product (the reduction it waits for was started one block earlier),
+ * so the HBM-bound group does not run beside the reduction that product starts; with one
+ * μ-batch it follows that product. After the last layer the closing group writes `out` per
+ * μ. comm NULL (or == compute): everything in order on `compute`.
  */
 typedef struct {
   int64_t batch, seq, hidden;
@@ -404,7 +407,8 @@ typedef struct {
  * (deep-dive, "反向：扩展与权重梯度计算的重叠"; overlap page §1: input gradients need the
  * reduction, weight gradients are local). Given d_out, the gradient of `out`:
  *   the last layer's closing group: d_ym = dropout'(d_out);
- *   per layer, top down:
+ *   per layer, top down (in each "for each μ" below, the group kernel of μ+1 is issued
+ *   before the last product of μ, so it does not run beside the reduction that product starts):
  *     for each μ: MLP input gradient (dHpre = act'(Hpre) ⊙ d_ym·B_sᵀ, dx_mlp_own =
  *                 dHpre·A_sᵀ), then its reduction on `comm`;
  *     dB_s (+)= Hᵀ·d_ym, dA_s (+)= ln2ᵀ·dHpre                    (hide the last reduction);

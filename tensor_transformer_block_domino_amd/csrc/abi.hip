@@ -1017,12 +1017,30 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
   auto wait = [&](const void* y, const void* own, int kind, int mu) {
     return sc.overlap && needs_reduce(P, own, y) ? hipStreamWaitEvent(sc.cs, sc.ev->sub[kind][mu], 0) : hipSuccess;
   };
-  for (int l = 0; l < d->layers && e == hipSuccess; ++l) {
+  // The schedule as a sequence of blocks: per layer the attention block of each μ-batch,
+  // then the MLP block of each, and after the last layer each μ-batch's closing group.
+  // A block opens with its group kernel (dropout + residual + LayerNorm), which needs the
+  // reduction of the block rc places earlier, then runs its products; its last product
+  // (out-projection or GEMM2) starts the block's reduction. With two or more μ-batches the
+  // next block's group is issued before that last product: the group is HBM-bound like
+  // the reduction, and issued after it would run beside it, while the products before it
+  // already gave the reduction it waits for a GEMM to hide behind.
+  const int nreal = d->layers * 2 * rc, nblk = nreal + rc;
+  auto open = [&](int i) {
+    const int mu = i % rc;
+    const int64_t r0 = mu * Tc;
+    if (i >= nreal) {  // closing group of the last layer
+      const domino_layer_params& q = prm[d->layers - 1];
+      const domino_layer_acts& b = act[d->layers - 1];
+      ok(wait(b.y_mlp, b.y_mlp_own, 1, mu), "wait for the MLP reduction") &&
+          ok(group(b.h, b.y_mlp, q.b_2, q.keep_mlp, out, nullptr, nullptr, nullptr, nullptr, nullptr, r0),
+             "closing group");
+      return;
+    }
+    const int l = i / (2 * rc);
     const domino_layer_params& p = prm[l];
     const domino_layer_acts& a = act[l];
-    const void* x = l == 0 && !a.x_in ? X : a.x_in;
-    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
-      const int64_t r0 = mu * Tc;
+    if ((i / rc) % 2 == 0) {  // LN1, fused with the previous layer's closing group
       if (l == 0) {
         ok(group(X, nullptr, nullptr, nullptr, a.x_in && a.x_in != X ? a.x_in : nullptr, p.ln1_gamma, p.ln1_beta,
                  a.ln1, a.mean1, a.rstd1, r0), "LN1");
@@ -1033,39 +1051,59 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
             ok(group(b.h, b.y_mlp, q.b_2, q.keep_mlp, a.x_in, p.ln1_gamma, p.ln1_beta, a.ln1, a.mean1, a.rstd1, r0),
                "closing group + LN1");
       }
-      AttnArgs aa{};
-      aa.qkv = at(a.QKV, r0 * 3 * hd, 2); aa.ld_qkv = 3 * hd;
-      aa.o = at(a.O, r0 * hd, 2); aa.ld_o = hd;
-      aa.lse = a.lse ? a.lse + r0 * d->heads : nullptr; aa.ld_lse = d->heads;
-      aa.batch = d->batch / rc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
-      aa.scale = scale;
-      GemmArgs gq = attn_qkv(&ad, at(a.ln1, r0 * h, 2), p.A_qkv_s, at(a.QKV, r0 * 3 * hd, 2));
-      gq.bias = p.b_qkv;
-      ok(run_gemm(DOMINO_K_QKV, gq, workspace, workspace_bytes, sc.cs), "QKV GEMM") &&
-          ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), "attention") &&
-          ok(run_gemm(DOMINO_K_OUTPROJ, attn_out(&ad, at(a.O, r0 * hd, 2), p.B_o_s, at(a.y_attn_own, r0 * h, 2), 0),
-                      workspace, workspace_bytes, sc.cs), "out-projection") &&
-          ok(reduce(a.y_attn, a.y_attn_own, a.peer_y_attn, 0, mu), "reduce attention");
-    }
-    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
-      const int64_t r0 = mu * Tc;
-      GemmArgs g1 = mlp_gemm1(&md, at(a.ln2, r0 * h, 2), p.A_s, at(a.Hpre, r0 * n1, 2), at(a.H, r0 * f, 2));
-      g1.bias = p.b_1;
+    } else {  // dropout + residual + LN2
+      const void* x = l == 0 && !a.x_in ? X : a.x_in;
       ok(wait(a.y_attn, a.y_attn_own, 0, mu), "wait for the attention reduction") &&
           ok(group(x, a.y_attn, p.b_o, p.keep_attn, a.h, p.ln2_gamma, p.ln2_beta, a.ln2, a.mean2, a.rstd2, r0),
-             "middle group") &&
-          ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, workspace, workspace_bytes, sc.cs), "GEMM1") &&
-          ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(&md, at(a.H, r0 * f, 2), p.B_s, at(a.y_mlp_own, r0 * h, 2), 0, 0),
-                      workspace, workspace_bytes, sc.cs), "GEMM2") &&
-          ok(reduce(a.y_mlp, a.y_mlp_own, a.peer_y_mlp, 1, mu), "reduce MLP");
+             "middle group");
     }
+  };
+  // The block's products up to (head) and from (tail) its last one.
+  auto products = [&](int i, bool tail) {
+    if (i >= nreal) return;
+    const int l = i / (2 * rc), mu = i % rc;
+    const int64_t r0 = mu * Tc;
+    const domino_layer_params& p = prm[l];
+    const domino_layer_acts& a = act[l];
+    if ((i / rc) % 2 == 0) {
+      if (!tail) {
+        AttnArgs aa{};
+        aa.qkv = at(a.QKV, r0 * 3 * hd, 2); aa.ld_qkv = 3 * hd;
+        aa.o = at(a.O, r0 * hd, 2); aa.ld_o = hd;
+        aa.lse = a.lse ? a.lse + r0 * d->heads : nullptr; aa.ld_lse = d->heads;
+        aa.batch = d->batch / rc; aa.seq = d->seq; aa.heads = d->heads; aa.head_dim = d->head_dim;
+        aa.scale = scale;
+        GemmArgs gq = attn_qkv(&ad, at(a.ln1, r0 * h, 2), p.A_qkv_s, at(a.QKV, r0 * 3 * hd, 2));
+        gq.bias = p.b_qkv;
+        ok(run_gemm(DOMINO_K_QKV, gq, workspace, workspace_bytes, sc.cs), "QKV GEMM") &&
+            ok(timed(DOMINO_K_ATTN, sc.cs, [&] { return launch_attention_fwd(aa, sc.cs); }), "attention");
+      } else {
+        ok(run_gemm(DOMINO_K_OUTPROJ, attn_out(&ad, at(a.O, r0 * hd, 2), p.B_o_s, at(a.y_attn_own, r0 * h, 2), 0),
+                    workspace, workspace_bytes, sc.cs), "out-projection") &&
+            ok(reduce(a.y_attn, a.y_attn_own, a.peer_y_attn, 0, mu), "reduce attention");
+      }
+    } else {
+      if (!tail) {
+        GemmArgs g1 = mlp_gemm1(&md, at(a.ln2, r0 * h, 2), p.A_s, at(a.Hpre, r0 * n1, 2), at(a.H, r0 * f, 2));
+        g1.bias = p.b_1;
+        ok(run_gemm(DOMINO_K_FWD_GEMM1, g1, workspace, workspace_bytes, sc.cs), "GEMM1");
+      } else {
+        ok(run_gemm(DOMINO_K_FWD_GEMM2, mlp_gemm2(&md, at(a.H, r0 * f, 2), p.B_s, at(a.y_mlp_own, r0 * h, 2), 0, 0),
+                    workspace, workspace_bytes, sc.cs), "GEMM2") &&
+            ok(reduce(a.y_mlp, a.y_mlp_own, a.peer_y_mlp, 1, mu), "reduce MLP");
+      }
+    }
+  };
+  // With one μ-batch a block's group needs the reduction the previous block just started,
+  // so it is issued after that block's tail.
+  const bool early = rc >= 2;
+  open(0);
+  for (int i = 0; i < nblk && e == hipSuccess; ++i) {
+    products(i, false);
+    if (early && i + 1 < nblk) open(i + 1);
+    products(i, true);
+    if (!early && i + 1 < nblk) open(i + 1);
   }
-  const domino_layer_params& q = prm[d->layers - 1];
-  const domino_layer_acts& b = act[d->layers - 1];
-  for (int mu = 0; mu < rc && e == hipSuccess; ++mu)
-    ok(wait(b.y_mlp, b.y_mlp_own, 1, mu), "wait for the MLP reduction") &&
-        ok(group(b.h, b.y_mlp, q.b_2, q.keep_mlp, out, nullptr, nullptr, nullptr, nullptr, nullptr, mu * Tc),
-           "closing group");
   if (e != hipSuccess) return fail(DOMINO_ERR_HIP, msg);
   return DOMINO_OK;
 }
@@ -1189,8 +1227,10 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
     const domino_layer_grads& g = grd[l];
     // Gradient of the layer's output residual: d_out, or what the layer above wrote.
     const void* d_r = l == Lk - 1 ? d_out : grd[l + 1].d_x_in;
-    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
-      const int64_t r0 = mu * Tc;
+    // Each section below issues the group kernel of μ-batch μ+1 before the last product of
+    // μ-batch μ: the group is HBM-bound like the reduction that product starts, and the
+    // reduction it needs was started in the previous section.
+    auto open_mlp = [&](int mu) {
       if (l == Lk - 1) {
         ok(group(nullptr, d_out, nullptr, nullptr, nullptr, nullptr, p.keep_mlp, nullptr, g.d_ym, nullptr, nullptr,
                  g.d_b_2, mu), "closing group backward");
@@ -1203,11 +1243,16 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
             ok(group(u.dx_attn, u.d_h, x_in(l + 1), b.mean1, b.rstd1, q.ln1_gamma, p.keep_mlp, u.d_x_in, g.d_ym,
                      u.d_ln1_gamma, u.d_ln1_beta, g.d_b_2, mu), "LN1 backward + closing group backward");
       }
+    };
+    open_mlp(0);
+    for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
+      const int64_t r0 = mu * Tc;
       ok(run_gemm(DOMINO_K_DGRAD_B, mlp_dgrad_b(&s.md, at(g.d_ym, r0 * h, 2), p.B_s, at(g.dHpre, r0 * n1, 2),
                                                 at(a.Hpre, r0 * n1, 2)), workspace, workspace_bytes, sc.cs),
-         "MLP dgrad-B") &&
-          ok(run_gemm(DOMINO_K_DGRAD_A, mlp_dgrad_a(&s.md, at(g.dHpre, r0 * n1, 2), p.A_s, at(g.dx_mlp_own, r0 * h, 2), 0,
-                                                    0), workspace, workspace_bytes, sc.cs), "MLP dgrad-A") &&
+         "MLP dgrad-B");
+      if (mu + 1 < rc) open_mlp(mu + 1);
+      ok(run_gemm(DOMINO_K_DGRAD_A, mlp_dgrad_a(&s.md, at(g.dHpre, r0 * n1, 2), p.A_s, at(g.dx_mlp_own, r0 * h, 2), 0,
+                                                0), workspace, workspace_bytes, sc.cs), "MLP dgrad-A") &&
           ok(reduce(g.dx_mlp, g.dx_mlp_own, g.peer_dx_mlp, 1, mu), "reduce MLP dX");
     }
     ok(run_gemm(DOMINO_K_WGRAD_B, mlp_wgrad_b(&s.md_all, a.H, g.d_ym, g.dB_s, accumulate), workspace, workspace_bytes,
@@ -1218,6 +1263,12 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
       ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
            return launch_bias_grad(g.dHpre, T, n1, n1, g.d_b_1, accumulate, static_cast<float*>(workspace), sc.cs);
          }), "MLP bias gradient");
+    auto open_attn = [&](int mu) {
+      ok(wait(g.dx_mlp, g.dx_mlp_own, 1, mu), "wait for the MLP reduction") &&
+          ok(group(g.dx_mlp, d_r, a.h, a.mean2, a.rstd2, p.ln2_gamma, p.keep_attn, g.d_h, g.d_ya, g.d_ln2_gamma,
+                   g.d_ln2_beta, g.d_b_o, mu), "middle group backward");
+    };
+    open_attn(0);
     for (int mu = 0; mu < rc && e == hipSuccess; ++mu) {
       const int64_t r0 = mu * Tc;
       AttnBwdArgs ab{};
@@ -1228,20 +1279,18 @@ domino_status domino_stack_bwd(const domino_layer_desc* d, const void* X, const 
       ab.stats = static_cast<float*>(workspace);
       ab.batch = s.ad.batch; ab.seq = d->seq; ab.heads = d->heads; ab.head_dim = d->head_dim;
       ab.scale = s.scale;
-      ok(wait(g.dx_mlp, g.dx_mlp_own, 1, mu), "wait for the MLP reduction") &&
-          ok(group(g.dx_mlp, d_r, a.h, a.mean2, a.rstd2, p.ln2_gamma, p.keep_attn, g.d_h, g.d_ya, g.d_ln2_gamma,
-                   g.d_ln2_beta, g.d_b_o, mu), "middle group backward") &&
-          ok(run_gemm(DOMINO_K_OUTPROJ_DGRAD, attn_dout(&s.ad, at(g.d_ya, r0 * h, 2), p.B_o_s, at(g.dO, r0 * hd, 2)),
-                      workspace, workspace_bytes, sc.cs), "dO GEMM") &&
+      ok(run_gemm(DOMINO_K_OUTPROJ_DGRAD, attn_dout(&s.ad, at(g.d_ya, r0 * h, 2), p.B_o_s, at(g.dO, r0 * hd, 2)),
+                  workspace, workspace_bytes, sc.cs), "dO GEMM") &&
           ok(timed(DOMINO_K_ATTN_BWD_PREP, sc.cs, [&] { return launch_attention_bwd_prep(ab, sc.cs); }),
              "attention backward statistics") &&
           ok(timed(DOMINO_K_ATTN_BWD, sc.cs, [&] { return launch_attention_bwd_dkdv(ab, sc.cs); }),
              "attention backward dK/dV") &&
           ok(timed(DOMINO_K_ATTN_BWD_DQ, sc.cs, [&] { return launch_attention_bwd_dq(ab, sc.cs); }),
-             "attention backward dQ") &&
-          ok(run_gemm(DOMINO_K_QKV_DGRAD, attn_dx(&s.ad, at(g.dQKV, r0 * 3 * hd, 2), p.A_qkv_s,
-                                                  at(g.dx_attn_own, r0 * h, 2), 0), workspace, workspace_bytes, sc.cs),
-             "QKV dgrad") &&
+             "attention backward dQ");
+      if (mu + 1 < rc) open_attn(mu + 1);
+      ok(run_gemm(DOMINO_K_QKV_DGRAD, attn_dx(&s.ad, at(g.dQKV, r0 * 3 * hd, 2), p.A_qkv_s,
+                                              at(g.dx_attn_own, r0 * h, 2), 0), workspace, workspace_bytes, sc.cs),
+         "QKV dgrad") &&
           ok(reduce(g.dx_attn, g.dx_attn_own, g.peer_dx_attn, 0, mu), "reduce attention dX");
     }
     ok(run_gemm(DOMINO_K_OUTPROJ_WGRAD, attn_wgrad_o(&s.ad_all, a.O, g.d_ya, g.dB_o_s, accumulate), workspace,
