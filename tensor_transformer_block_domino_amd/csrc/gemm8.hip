@@ -42,35 +42,31 @@ namespace {
 
 constexpr int k8Threads = 512;
 
-template <bool kAK, bool kBKc, Epi kEpi>
-__global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
-  constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
-  constexpr int TM = 2, TN = 4;  // 32×32 blocks per wave
+constexpr int kBK8 = 32, kNS8 = 4;
+constexpr int kStage8 = (256 + 256) * kBK8;  // bf16 elements per stage (32 KB)
+constexpr int kRS8 = 128 + 4;                // floats per staged epilogue row: rows 4 banks apart
+constexpr int kRegion8 = 32 * kRS8;          // floats staged per wave
+constexpr int kSmem8 = kNS8 * kStage8 > 8 * kRegion8 * 2 ? kNS8 * kStage8 : 8 * kRegion8 * 2;
+
+// One output tile of 128·TM rows × 256 columns at (m0, n0): TM = 2 is the whole 256×256
+// tile, TM = 1 the half tile (each wave then owns 32 rows instead of 64).
+template <bool kAK, bool kBKc, Epi kEpi, int TM>
+__device__ __forceinline__ void gemm8_tile(const KParams& p, uint16_t* smem, int64_t m0, int64_t n0) {
+  constexpr int BM = 128 * TM, BN = 256, BK = kBK8, NS = kNS8;
+  constexpr int TN = 4;  // 32×32 blocks per wave
+  constexpr int WM = 32 * TM;  // rows per wave
   constexpr bool kSw = kEpi == Epi::kSwiglu;
   using OA = typename std::conditional<kAK, OpK<BM, BK>, OpMN<BM, BK, false>>::type;
   using OB = typename std::conditional<kBKc, OpK<BN, BK, kSw>, OpMN<BN, BK, kSw>>::type;
-  static_assert(OA::kLoads == 4 && OB::kLoads == 4, "four 1 KB copies per wave per step");
-  constexpr int kLoads = 4;
-  constexpr int kStage = (BM + BN) * BK;  // bf16 elements per stage (32 KB)
-  constexpr int RS = 128 + 4;             // floats per staged row: rows 4 banks apart
-  constexpr int kRegion = 32 * RS;        // floats staged per wave
-  constexpr int kSmem = NS * kStage > 8 * kRegion * 2 ? NS * kStage : 8 * kRegion * 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmem];
+  constexpr int kLoadsA = OA::kLoads, kLoadsB = OB::kLoads;  // 1 KB copies per wave per step
+  static_assert(kLoadsA == 2 * TM && kLoadsB == 4, "copies per wave per step");
+  constexpr int kStage = kStage8;
+  constexpr int RS = kRS8;
+  constexpr int kRegion = kRegion8;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 2, wi = wave & 3;
-
-  // Tile of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs; the
-  // index is remapped so each XCD gets a contiguous, M-grouped run of tiles.
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int full = (tiles / 8) * 8;
-  const int b = blockIdx.x;
-  const int t = b < full ? (b % 8) * (full / 8) + b / 8 : b;
-  int tm, tn;
-  tile_coords(t, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = int64_t(tm) * BM;
-  const int64_t n0 = kSw ? int64_t(tn) * (BN / 2) : int64_t(tn) * BN;
   const RowMap rmA{m0, p.M, 0};
   const RowMap rmB{n0, kSw ? p.f_s : p.N, p.f_s};
 
@@ -92,11 +88,11 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
     if (g == 0) {
       const typename OA::Src sr = oa.src(int64_t(kt) * BK, p.K);
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) oa.issue_one(sr, st, wi, q);
+      for (int q = 0; q < kLoadsA; ++q) oa.issue_one(sr, st, wi, q);
     } else {
       const typename OB::Src sr = ob.src(int64_t(kt) * BK, p.K);
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) ob.issue_one(sr, st + BM * BK, wi, q);
+      for (int q = 0; q < kLoadsB; ++q) ob.issue_one(sr, st + BM * BK, wi, q);
     }
   };
 
@@ -110,7 +106,7 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < OA::kRd; ++r) OA::read(sa, wi * 64 + i * 32, s, lane, r, fa[s][i]);
+        for (int r = 0; r < OA::kRd; ++r) OA::read(sa, wi * WM + i * 32, s, lane, r, fa[s][i]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -152,7 +148,8 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
   for (int st = 0; st < NS - 1; ++st) issue(st);
   // Step 0 of this group's operand landed (the later two may be in flight), then the
   // barrier publishes it to the other group.
-  wait_vm_barrier<(NS - 2) * kLoads>();
+  if (g == 0) wait_vm_barrier<(NS - 2) * kLoadsA>();
+  else wait_vm_barrier<(NS - 2) * kLoadsB>();
   // Phases are separated by workgroup barriers; group 1 runs one phase behind group 0.
   if (g == 1) asm volatile("s_barrier" ::: "memory");
   for (int kt = 0; kt < kt_total; ++kt) {
@@ -165,14 +162,14 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
     wait_frags();
     // Group 1's copies of step kt + 1 must have landed before group 0 reads that step,
     // which follows this barrier.
-    if (g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
+    if (g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoadsB) : "memory");
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     // Compute phase.
     compute();
     __builtin_amdgcn_sched_barrier(0);
     // Group 0's copies of step kt + 1 must have landed before it reads that step next.
-    if (g == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
+    if (g == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoadsA) : "memory");
     asm volatile("s_barrier" ::: "memory");
   }
   pin_acc();
@@ -202,7 +199,7 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
   static_assert(kPasses % kGrp == 0, "whole groups of passes");
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int band = wi * 64 + i * 32;  // tile-local first row
+    const int band = wi * WM + i * 32;  // tile-local first row
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -239,6 +236,34 @@ __global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
       }
     }
   }
+}
+
+// Workgroups 0 .. dp_tiles−1 compute whole 256×256 tiles; when the tiles do not fill their
+// last round of the CUs, the remaining ones (dp_tiles .. tiles−1) are computed as two
+// 128-row halves each by the workgroups after those, so the partial round takes about half
+// the time. Workgroups are dispatched round-robin over the 8 XCDs; each range is remapped
+// so every XCD gets a contiguous, M-grouped run of tiles (and both halves of a tile).
+template <bool kAK, bool kBKc, Epi kEpi>
+__global__ __launch_bounds__(k8Threads, 1) void gemm8_kernel(KParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmem8];
+  constexpr bool kSw = kEpi == Epi::kSwiglu;
+  const int b = blockIdx.x;
+  int t, half = -1;
+  if (b < p.dp_tiles) {
+    const int full = (p.dp_tiles / 8) * 8;
+    t = b < full ? (b % 8) * (full / 8) + b / 8 : b;
+  } else {
+    const int items = 2 * (p.tiles_m * p.tiles_n - p.dp_tiles), full = (items / 8) * 8;
+    const int hb = b - p.dp_tiles;
+    const int u = hb < full ? (hb % 8) * (full / 8) + hb / 8 : hb;
+    t = p.dp_tiles + u / 2;
+    half = u % 2;
+  }
+  int tm, tn;
+  tile_coords(t, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t n0 = kSw ? int64_t(tn) * 128 : int64_t(tn) * 256;
+  if (half < 0) gemm8_tile<kAK, kBKc, kEpi, 2>(p, smem, int64_t(tm) * 256, n0);
+  else gemm8_tile<kAK, kBKc, kEpi, 1>(p, smem, int64_t(tm) * 256 + half * 128, n0);
 }
 
 template <bool kAK, bool kBKc, Epi kEpi>
@@ -279,11 +304,15 @@ hipError_t launch_gemm8(const GemmArgs& g, hipStream_t s) {
   const int64_t bn = g.epi == Epi::kSwiglu ? 128 : 256;
   kp.tiles_m = int((g.M + 255) / 256);
   kp.tiles_n = int((g.N + bn - 1) / bn);
-  kp.dp_tiles = kp.tiles_m * kp.tiles_n;
+  const int tiles = kp.tiles_m * kp.tiles_n;
+  // A last round filling at most half the CUs runs as half tiles (twice the workgroups).
+  constexpr int kCUs8 = 256;
+  const int rest = tiles % kCUs8;
+  kp.dp_tiles = tiles > kCUs8 && rest > 0 && 2 * rest <= kCUs8 ? tiles - rest : tiles;
   kp.splits = 1;
   kp.kt_per_split = int((g.K + 31) / 32);
   kp.accumulate = g.accumulate;
-  const int blocks = kp.tiles_m * kp.tiles_n;
+  const int blocks = kp.dp_tiles + 2 * (tiles - kp.dp_tiles);
   if (blocks == 0) return hipSuccess;
   const bool ak = g.a_kcontig, bk = g.b_kcontig;
   switch (g.epi) {
