@@ -79,8 +79,9 @@ def parse():
                     help="run one plain device copy of this size first (for HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "COPY_MIB",
                                                            "WORKLOAD", "OUT"))
-    ap.add_argument("--traffic-workgroups", type=int, default=0,
-                    help="with --traffic-summary: only the kernel's dispatches of this many workgroups")
+    ap.add_argument("--traffic-workgroups", default="",
+                    help="with --traffic-summary: only the kernel's dispatches of these workgroup counts "
+                         "(comma-separated)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "OUT"),
                     help="per-kernel, per-launch-shape statistics of a rocprofv3 kernel trace")
     ap.add_argument("--timeline-summary", nargs=3, metavar=("TRACE_CSV", "OUT", "TITLE"),
@@ -122,16 +123,19 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path, workgroups=0):
+def traffic_summary(fetch_csv, write_csv, kernel, copy_mib, workload, out_path, workgroups=""):
     """Writes the traffic summary bench reads (measured_traffic) from two counter runs,
-    over the kernel's dispatches of `workgroups` workgroups (all of them when 0)."""
+    over the kernel's dispatches of the given workgroup counts (comma-separated; all of
+    them when empty)."""
     import csv
+
+    shapes = {int(x) for x in str(workgroups).split(",") if x.strip()}
 
     def values(path, counter):
         out = {}
         for row in csv.DictReader(open(path)):
             wgs = int(row["Grid_Size"]) // max(1, int(row["Workgroup_Size"]))
-            if row["Counter_Name"] == counter and (not workgroups or wgs == workgroups
+            if row["Counter_Name"] == counter and (not shapes or wgs in shapes
                                                    or "copyBuffer" in row["Kernel_Name"]):
                 out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
         return out
