@@ -527,17 +527,18 @@ bool one_round_256x160(const GemmArgs& g, bool sw) {
 // four-wave 128×256 tiles, but those leave no room on a CU for a reduction wave beside
 // them (2·224 of 512 VGPRs), and in the step they run beside reductions (Llama-2-13B GEMM2
 // chunks 0.86 vs 0.89 ms per step, the attention's output projection 137 vs 191 µs).
-// Narrower ones stay on the four-wave tiles (the 1536-wide QKV product over 16384 rows, 384
-// tiles: 5% faster there), except a single round of 256×256 tiles on at least 3/4 of the
-// CUs with a long k loop (the QKV product of one μ-batch of the GPT-3 6.7B layer stack:
-// 192 tiles, k = 4096; layer stack 8.77 -> 8.69 ms). The weight gradients (both operands
-// m/n-major, read transposed) run 20–50% faster on the four-wave kernels' k-split.
+// Narrower ones stay on the four-wave tiles, except with a long k loop (k ≥ 4096) when the
+// 256×256 tiles make one round on at least 3/4 of the CUs, or more rounds whose last one
+// runs as half tiles: the QKV product of the GPT-3 6.7B layer stack per μ-batch (192
+// tiles; stack 8.77 -> 8.69 ms) and of its attention block over 16384 rows (384 tiles;
+// 228 -> 222 µs). The weight gradients (both operands m/n-major, read transposed) run
+// 20–50% faster on the four-wave kernels' k-split.
 bool pick_gemm8(const GemmArgs& g) {
   if (g.epi == Epi::kF32 || !gemm8_supports(g)) return false;
   const int64_t bn = g.epi == Epi::kSwiglu ? 128 : 256;
   const int64_t tiles = ((g.M + 255) / 256) * ((g.N + bn - 1) / bn);
   if (g.epi == Epi::kStore && !g.b_kcontig && g.N < 2048)
-    return g.K >= 4096 && tiles >= kCUs * 3 / 4 && tiles <= kCUs;
+    return g.K >= 4096 && tiles >= kCUs * 3 / 4 && (tiles <= kCUs || 2 * (tiles % kCUs) <= kCUs);
   return tiles >= kCUs;
 }
 
