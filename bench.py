@@ -23,8 +23,9 @@ events the launches' own dispatches record); T_unsplit (one chunk, no reduction:
 parallel communication disabled), T_serial (one chunk, reductions on the same stream),
 T_domino and the standalone reduction time, with hidden_fraction = 1 − (T_domino −
 T_unsplit) / T_reduce; the CPU oracle's throughput on this host; and, as extra keys, the
-same step figures for the Llama-2-7B column-split and GPT-3-2.7B row-split MLP workloads
-and the GPT-3-6.7B attention block's forward alone (with its last reduction exposed).
+same step figures for the Llama-2-7B column-split and GPT-3-2.7B row-split MLP workloads,
+the GPT-3-6.7B attention block's forward alone (with its last reduction exposed) and the
+two-layer GPT-3-6.7B stack (forward + backward, μ-batch schedule).
 
 `--workload gpt3_6p7b_attn_tp8_row` measures the attention block of one rank instead (QKV
 product, causal attention over the rank's heads, out-projection per chunk and its
@@ -59,7 +60,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 METRIC = "TP-shard block fwd+bwd TFLOP/s (bf16) + % MFMA peak; shard_reduce GB/s"
 DEFAULT_WORKLOAD = "llama2_13b_swiglu_tp8_2d"
-DEFAULT_ALSO = "llama2_7b_swiglu_tp8_col,gpt3_2p7b_mlp_tp8_row,gpt3_6p7b_attn_tp8_row"
+DEFAULT_ALSO = "llama2_7b_swiglu_tp8_col,gpt3_2p7b_mlp_tp8_row,gpt3_6p7b_attn_tp8_row,gpt3_6p7b_layer_tp8_row"
 FLUSH_BYTES = 1 << 30
 
 
@@ -799,13 +800,15 @@ def cpu_baseline_layer(w, inp, n_seq=1):
                       f"{dt:.1f} s"}
 
 
-def main_layer(args, w, timer):
+def measure_layer(w, args, timer, detail):
+    """The layer stack's step figures for workload `w`: Domino, serial and one-μ-batch
+    steps, and with `detail` the graph replay, per-kernel times and the roofline."""
     import torch
 
     import tensor_transformer_block_domino_amd as D
     from tensor_transformer_block_domino_amd.tp_sim import LayerGroup
 
-    print("[bench] generating the layer inputs", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: generating the layer inputs", file=sys.stderr, flush=True)
     inp = synth.layer_inputs(w)
     g = LayerGroup(batch=w.batch, seq=w.seq, hidden=w.hidden, heads_shard=w.heads_shard, head_dim=w.head_dim,
                    ffn_shard=w.ffn_shard, act=w.act, row_chunks=w.row_chunks, n_partials=w.n_partials,
@@ -830,20 +833,10 @@ def main_layer(args, w, timer):
         g.backward(compute, comm, row_chunks=1)
 
     ms = timer.run(step_domino, args.steps, args.warmup)
-    print(f"[bench] layer stack domino step {ms:.3f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: domino step {ms:.3f} ms", file=sys.stderr, flush=True)
     ms_serial = timer.run(step_serial, args.steps, 2)
     ms_unsplit = timer.run(step_unsplit, args.steps, 2)
-    ms_graph = graph_steps(step_domino, timer, args.steps)
-    D.domino_timing_enable(True)
-    for _ in range(args.steps):
-        timer.flush()
-        step_domino()
-    torch.cuda.synchronize()
     fl = layer_flops(w)
-    roles = list(fl) + ["reduce", "aux", "group_fwd", "group_bwd"]
-    per = {r: D.domino_timing_read(r) for r in roles}
-    kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
-    D.domino_timing_enable(False)
     total_flops = sum(fl.values())
     value = total_flops / (ms * 1e-3) / 1e12
     res = {
@@ -856,14 +849,32 @@ def main_layer(args, w, timer):
         "t_domino_ms": round(ms, 4),
         "t_serial_ms": round(ms_serial, 4),
         "t_unsplit_ms": round(ms_unsplit, 4),
-        "t_graph_ms": round(ms_graph, 4),
-        "t_reduce_in_step_ms": round(per["reduce"][1] / args.steps, 4),
-        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
-        "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
-                          for r in fl if fl[r] > 0 and per[r][1] > 0},
-        "kernel_of_role": kernel_of,
-        "roofline": dominant(per, kernel_of, fl, args.steps),
+        "domino_over_serial": round(ms / ms_serial, 4),
     }
+    if detail:
+        res["t_graph_ms"] = round(graph_steps(step_domino, timer, args.steps), 4)
+        D.domino_timing_enable(True)
+        for _ in range(args.steps):
+            timer.flush()
+            step_domino()
+        torch.cuda.synchronize()
+        roles = list(fl) + ["reduce", "aux", "group_fwd", "group_bwd"]
+        per = {r: D.domino_timing_read(r) for r in roles}
+        kernel_of = {r: D.domino_timing_kernel(r) for r in roles}
+        D.domino_timing_enable(False)
+        res.update({
+            "t_reduce_in_step_ms": round(per["reduce"][1] / args.steps, 4),
+            "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()},
+            "kernel_tflops": {r: round(fl[r] * args.steps / (per[r][1] * 1e-3) / 1e12, 1)
+                              for r in fl if fl[r] > 0 and per[r][1] > 0},
+            "kernel_of_role": kernel_of,
+            "roofline": dominant(per, kernel_of, fl, args.steps),
+        })
+    return res, (g, inp)
+
+
+def main_layer(args, w, timer):
+    res, (g, inp) = measure_layer(w, args, timer, detail=True)
     out = headline(args, res)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -953,6 +964,9 @@ def main():
             others[name] = measure_mlp(ow, args, timer, detail=False)[0]
         elif isinstance(ow, synth.AttnWorkload):
             others[name] = measure_attn(ow, args, timer, detail=False)[0]["forward"]
+        elif isinstance(ow, synth.LayerWorkload):
+            others[name] = measure_layer(ow, args, timer, detail=False)[0]
+        torch.cuda.empty_cache()
     if others:
         out["other_workloads"] = others
     print(json.dumps(out), flush=True)
