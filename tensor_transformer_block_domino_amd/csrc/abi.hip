@@ -624,6 +624,8 @@ domino_status shard_reduce(void* out, int64_t ld_out, const void* const* partial
   return DOMINO_OK;
 }
 
+}  // extern "C"
+namespace {
 // Whether the forward transposes the weights (bf16, and the first product then runs on
 // the eight-wave kernel, which takes the activations' k-contiguous weight operand).
 bool mlp_fwd_transposed(const domino_mlp_desc* d) {
@@ -637,6 +639,8 @@ size_t mlp_fwd_ws_transposed(const domino_mlp_desc* d) {
   return mlp_wt_bytes(d) + ws_bytes_of({mlp_gemm1_t(d, nullptr, nullptr, nullptr, nullptr),
                                         mlp_gemm2_t(d, nullptr, nullptr, nullptr, 0, 0)});
 }
+}  // namespace
+extern "C" {
 
 size_t domino_block_fwd_workspace_size(const domino_mlp_desc* d) {
   if (check_mlp_desc(d) != DOMINO_OK) return 0;
@@ -1108,6 +1112,8 @@ domino_status domino_stack_fwd(const domino_layer_desc* d, const void* X, const 
   return DOMINO_OK;
 }
 
+}  // extern "C"
+namespace {
 // The sub-problems of the layer schedule: one μ-batch (batch / row_chunks sequences) and
 // all rows (for the weight gradients).
 struct LayerShapes {
@@ -1127,6 +1133,8 @@ LayerShapes layer_shapes(const domino_layer_desc* d) {
   s.md_all.batch = d->batch;
   return s;
 }
+}  // namespace
+extern "C" {
 
 size_t domino_stack_bwd_workspace_size(const domino_layer_desc* d) {
   if (check_layer_desc(d) != DOMINO_OK || d->heads == 0 || d->ffn_shard == 0) return 0;

@@ -44,6 +44,15 @@ def test_library_exports_every_header_symbol(lib):
         assert hasattr(lib, name)
 
 
+def test_library_exports_no_undeclared_c_function():
+    """Every unmangled function the library defines is one the header declares (internal
+    helpers stay in C++ linkage)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], stdout=subprocess.PIPE, text=True, check=True)
+    c_funcs = {parts[-1] for parts in (line.split() for line in out.stdout.splitlines())
+               if len(parts) == 3 and parts[1] == "T" and not parts[2].startswith("_")}
+    assert c_funcs <= set(header_functions()), sorted(c_funcs - set(header_functions()))
+
+
 def test_struct_layouts_match_header():
     # int64 ×4 + int32 ×6 and int64 ×5 + float + int32 ×4 (padded to 8).
     assert ctypes.sizeof(L.MlpDesc) == 56
