@@ -408,14 +408,16 @@ typedef struct {
  * reduction, weight gradients are local). Given d_out, the gradient of `out`:
  *   the last layer's closing group: d_ym = dropout'(d_out);
  *   per layer, top down (in each "for each μ" below, the group kernel of μ+1 is issued
- *   before the last product of μ, so it does not run beside the reduction that product starts):
+ *   before the last product of μ, so it does not run beside the reduction that product starts;
+ *   with two or more μ-batches the first LN2 backward is issued before the MLP's last product):
  *     for each μ: MLP input gradient (dHpre = act'(Hpre) ⊙ d_ym·B_sᵀ, dx_mlp_own =
  *                 dHpre·A_sᵀ), then its reduction on `comm`;
- *     dB_s (+)= Hᵀ·d_ym, dA_s (+)= ln2ᵀ·dHpre                    (hide the last reduction);
  *     for each μ: wait for the MLP reduction of μ; LN2's backward with the residual
  *                 gradient (d_h) and dropout'(d_h) = d_ya; attention input gradient (dO,
- *                 attention backward, dx_attn_own = dQKV·A_qkv_sᵀ), then its reduction;
- *     dB_o_s (+)= Oᵀ·d_ya, dA_qkv_s (+)= ln1ᵀ·dQKV;
+ *                 attention backward, dx_attn_own = dQKV·A_qkv_sᵀ), then its reduction
+ *                 (the MLP's last reduction hides behind the first μ-batch's work here);
+ *     dA_qkv_s (+)= ln1ᵀ·dQKV, dB_o_s (+)= Oᵀ·d_ya, dB_s (+)= Hᵀ·d_ym,
+ *     dA_s (+)= ln2ᵀ·dHpre                          (hide the attention's last reduction);
  *     for each μ: wait for the attention reduction of μ; LN1's backward with the residual
  *                 gradient gives d_x_in, fused with the layer below's closing group
  *                 (d_ym of that layer = dropout'(d_x_in)) — issued at the start of the layer
