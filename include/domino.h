@@ -239,7 +239,7 @@ size_t domino_attn_block_fwd_workspace_size(const domino_attn_desc* desc);
  *   dX_own[chunk] = dQKV·A_qkv_sᵀ            (this rank's partial input gradient)
  *   dX[chunk] = dX_own + Σ peer_dX            (reduction on `comm`)
  * then the independent weight gradients, which hide the last reduction:
- *   dB_o_s (+)= Oᵀ·dY,  dA_qkv_s (+)= Xᵀ·dQKV  (fp32; accumulate != 0 adds to their contents)
+ *   dA_qkv_s (+)= Xᵀ·dQKV,  dB_o_s (+)= Oᵀ·dY  (fp32; accumulate != 0 adds to their contents)
  *   X, A_qkv_s, B_o_s, QKV, O as in the forward; lse from the forward (required);
  *   dY [T, hidden]                                                         (inputs)
  *   dO [T, heads·head_dim], dQKV [T, 3·heads·head_dim]   caller-provided scratch/outputs

@@ -908,10 +908,13 @@ domino_status domino_attn_block_bwd(const domino_attn_desc* d, const void* X, co
       return fail(DOMINO_ERR_HIP, msg);
   }
   // (no tokens: k = 0 and the products write zeros, or add nothing when accumulating)
-  if (heads && (hip_ok(run_gemm(DOMINO_K_OUTPROJ_WGRAD, attn_wgrad_o(d, O, dY, dB_o_s, accumulate), workspace,
-                                workspace_bytes, sc.cs), &msg, "dB_o GEMM") ||
-                hip_ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(d, X, dQKV, dA_qkv_s, accumulate), workspace,
-                                workspace_bytes, sc.cs), &msg, "dA_qkv GEMM")))
+  // The QKV weight gradient first: with the out-projection's first, that product's k-slice
+  // sum ran beside the last reduction, ~90 instead of ~25 µs (GPT-3 6.7B block fwd+bwd 1.55
+  // vs 1.47 ms).
+  if (heads && (hip_ok(run_gemm(DOMINO_K_QKV_WGRAD, attn_wgrad_qkv(d, X, dQKV, dA_qkv_s, accumulate), workspace,
+                                workspace_bytes, sc.cs), &msg, "dA_qkv GEMM") ||
+                hip_ok(run_gemm(DOMINO_K_OUTPROJ_WGRAD, attn_wgrad_o(d, O, dY, dB_o_s, accumulate), workspace,
+                                workspace_bytes, sc.cs), &msg, "dB_o GEMM")))
     return fail(DOMINO_ERR_HIP, msg);
   if (heads && d_b_qkv_s && hip_ok(timed(DOMINO_K_BIAS_GRAD, sc.cs, [&] {
                                      return launch_bias_grad(dQKV, T, 3 * hd, 3 * hd, d_b_qkv_s, accumulate,
