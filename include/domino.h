@@ -41,6 +41,9 @@
  *              valid only in `comm` order. comm == NULL or comm == compute runs the
  *              reductions inline on `compute` (plain, un-overlapped tensor parallelism).
  *              Peer partials must be ready in `compute` order when the call is made.
+ *              The overlap needs the two streams on different hardware queues: HIP
+ *              spreads streams over a few queues (4 by default) in creation order, so a
+ *              process that makes many streams should make these two early and keep them.
  *   Workspace  The block calls take an optional device workspace (`workspace`,
  *              `workspace_bytes`; its size from the matching *_workspace_size query).
  *              With it, a product whose last round of tiles would leave most of the GPU
