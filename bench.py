@@ -458,7 +458,9 @@ class StepTimer:
             fn()
             b.record(self.stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / steps
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        self.last = {"median": t[len(t) // 2], "min": t[0], "max": t[-1]}
+        return sum(t) / steps
 
 
 def backtoback(fn, steps, warmup):
@@ -544,6 +546,7 @@ def measure_mlp(w, args, timer, detail):
                            None, g.dA, g.dB, 0, g.ws, g.ws_bytes, compute, None)
 
     ms = timer.run(step_domino, args.steps, args.warmup)
+    spread = {k: round(v, 4) for k, v in timer.last.items()}
     print(f"[bench] {w.name}: domino step {ms:.3f} ms", file=sys.stderr, flush=True)
     ms_serial = timer.run(step_serial, args.steps, 2)
     ms_unsplit = timer.run(step_unsplit, args.steps, 2)
@@ -557,7 +560,7 @@ def measure_mlp(w, args, timer, detail):
     _, total_flops = mlp_flops(w)
     value = total_flops / (ms * 1e-3) / 1e12
     out = {
-        "value": round(value, 2), "ms_per_step": round(ms, 4),
+        "value": round(value, 2), "ms_per_step": round(ms, 4), "ms_per_step_spread": spread,
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
                    "ffn_shard": w.ffn_shard, "act": w.act, "tp_partials": w.n_partials,
                    "split": f"rows x{w.row_chunks}, cols x{w.col_chunks}", "pass": "fwd+bwd"},
